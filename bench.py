@@ -1,0 +1,163 @@
+"""Benchmark of the chunked gated delta rule prefill on one MI355X.
+
+One step = one gdr_prefill call (both kernels: per-chunk prep, then the sequential state scan)
+over the long-prefill workload: B = 1, 16 key / 32 value heads, Dk = Dv = 128, L = 16384,
+bf16 q/k/v, fp32 g/beta/state, zero initial state, final state returned. Inputs, outputs and
+the workspace are resident in HBM before the timed region. Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --copy-probe      # a plain device copy of known size, for HBM counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated-delta prefill tokens·heads/s and % MFMA roofline at L=16384, H=32, D=128"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+CHUNK, D = 64, 128
+
+
+def algorithmic(B, L, Hk, Hv, esz, n_s0, want_state):
+    """Algorithmic bytes and flops of one call.
+
+    Bytes: read q, k, v, g, beta, s0 (if any), lengths; write o and s_final (if wanted).
+    Flops per (token, value head): 6 D^2 + 10 C D (the chunked method counted with full 64x64
+    tiles: W S, Q S, K^T Delta over the state, plus Gram, W, U, Q K^T, P Delta within a chunk).
+    """
+    units = B * L * Hv
+    nbytes = (2 * B * L * Hk * D * esz          # q, k
+              + 2 * B * L * Hv * D * esz        # v, o
+              + 2 * B * L * Hv * 4              # g, beta (fp32)
+              + n_s0 * Hv * D * D * 4
+              + (B * Hv * D * D * 4 if want_state else 0))
+    flops = units * (6 * D * D + 10 * CHUNK * D)
+    return units, nbytes, flops
+
+
+def cpu_baseline(x, heads):
+    """The float64 oracle as it stands, on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle import gated_delta_rule
+    q, k, v = x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy()
+    g, beta = x.g.double().numpy(), x.beta.double().numpy()
+    L = q.shape[1]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        gated_delta_rule(q, k, v, g, beta, heads=list(range(heads)))
+        dt = time.perf_counter() - t0
+    return {"value": L * heads / dt, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {L} tokens of value heads 0..{heads - 1} of 32 (B=1), float64 numpy, "
+                      f"1 thread, {dt:.1f} s"}
+
+
+def copy_probe(nbytes=1 << 30, reps=3):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--copy-probe", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if a.copy_probe:
+        copy_probe()
+        return
+    import gated_deltanet_prefill_gdr_amd as gdr
+    from workloads import CONFIGS
+
+    spec = CONFIGS[5]
+    x = spec.draw()
+    B, L, Hk, Hv, Dk, Dv = x.shape
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v, g, beta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
+    o = torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
+    s_final = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
+    desc = gdr.make_desc(B, L, Hk, Hv, 0, True, False)
+    ws = torch.empty(gdr.workspace_size(desc), device=dev, dtype=torch.uint8)
+
+    def step():
+        gdr.prefill(q, k, v, g, beta, out=o, s_final=s_final, workspace=ws)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdr.timing_enable(True)
+    gdr.timing_read()                      # drop anything recorded before the timed region
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(a.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern = gdr.timing_read()
+    gdr.timing_enable(False)
+    ms = start.elapsed_time(stop) / a.steps
+
+    units, nbytes, flops = algorithmic(B, L, Hk, Hv, 2, 0, True)
+    per_kernel = {n: (t / max(c, 1), c) for n, (t, c) in kern.items()}
+    dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
+    k_ms = per_kernel[dominant][0]
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", "traffic_gdr_scan_l16384_bf16.json")
+    if os.path.exists(prof):
+        with open(prof) as f:
+            traffic = json.load(f).get(dominant)
+    line = {
+        "metric": METRIC,
+        "value": units / (ms * 1e-3),
+        "unit": "tokens·heads/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, beta~U(0.2,0.9), g~-U(0,0.5))",
+        "config": {"workload": "long prefill B=1 L=16384 Hk=16 Hv=32 Dk=Dv=128 bf16 q/k/v fp32 g/beta/state, "
+                               "zero initial state, final state returned",
+                   "B": B, "L": L, "Hk": Hk, "Hv": Hv, "D": Dk, "global_batch": B, "seq_len": L,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant},
+        "path": {"ms": ms, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": nbytes, "alg_flops": flops,
+                 "kernel_ms": {n: t for n, (t, c) in per_kernel.items()}},
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(x, a.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

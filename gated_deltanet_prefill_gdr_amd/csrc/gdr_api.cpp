@@ -1,0 +1,242 @@
+// C ABI of the chunked gated delta rule prefill (declared in include/gdr.h).
+//
+// Host side only: argument validation (no GPU call before every host-checkable argument has
+// passed), workspace sizing, the two kernel launches on the caller's stream, and optional
+// per-kernel HIP-event timing for benchmarks.
+#include "gdr.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "gdr_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status fail(gdr_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+size_t dtype_size(int dt) { return dt == GDR_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range(const char* name, const void* p, size_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlap(const Range& a, const Range& b) {
+  return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+int num_chunks(int L) { return (L + gdr::kChunk - 1) / gdr::kChunk; }
+
+gdr_status check_desc(const gdr_desc* d) {
+  if (!d) return fail(GDR_EINVAL, "desc is NULL");
+  if (d->B < 0 || d->L < 0) return fail(GDR_EINVAL, "B (%d) and L (%d) must be >= 0", d->B, d->L);
+  if (d->Hk <= 0 || d->Hv <= 0) return fail(GDR_EINVAL, "Hk (%d) and Hv (%d) must be > 0", d->Hk, d->Hv);
+  if (d->Hv % d->Hk) return fail(GDR_EINVAL, "Hv (%d) must be a multiple of Hk (%d)", d->Hv, d->Hk);
+  if (d->qkv_dtype != GDR_F32 && d->qkv_dtype != GDR_BF16)
+    return fail(GDR_EINVAL, "qkv_dtype %d is not a gdr_dtype", d->qkv_dtype);
+  if (d->beta_dtype != GDR_F32 && d->beta_dtype != d->qkv_dtype)
+    return fail(GDR_EINVAL, "beta_dtype must be GDR_F32 or qkv_dtype");
+  if (d->Dk != gdr::kHeadDim || d->Dv != gdr::kHeadDim)
+    return fail(GDR_EUNSUPPORTED, "Dk = %d, Dv = %d: only Dk = Dv = 128 is built", d->Dk, d->Dv);
+  if (d->Hv > 65535 || d->Hk > 65535 || d->B > 65535)
+    return fail(GDR_EUNSUPPORTED, "B, Hk and Hv must each be <= 65535 (grid limits)");
+  return GDR_OK;
+}
+
+gdr_status check_all(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                     const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                     const void* o, const float* s_final, const void* ws, size_t ws_bytes) {
+  gdr_status st = check_desc(d);
+  if (st != GDR_OK) return st;
+  const size_t B = d->B, L = d->L, Hk = d->Hk, Hv = d->Hv, Dd = gdr::kHeadDim;
+  const size_t esz = dtype_size(d->qkv_dtype), bsz = dtype_size(d->beta_dtype);
+  const bool any_tokens = B * L > 0;
+  if (any_tokens) {
+    if (!q || !k || !v || !g || !beta || !o) return fail(GDR_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+      return fail(GDR_EINVAL, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, bsz)) return fail(GDR_EINVAL, "g and beta must be element-aligned");
+  }
+  if (s0_row && !s0) return fail(GDR_EINVAL, "s0_row given without s0");
+  if (s0) {
+    if (d->n_s0 < 1) return fail(GDR_EINVAL, "n_s0 must be >= 1 when s0 is given");
+    if (!s0_row && size_t(d->n_s0) < B) return fail(GDR_EINVAL, "n_s0 (%d) < B (%d) with identity s0_row", d->n_s0, d->B);
+    if (!aligned(s0, 16)) return fail(GDR_EINVAL, "s0 must be 16-byte aligned");
+  }
+  if (s_final && !aligned(s_final, 16)) return fail(GDR_EINVAL, "s_final must be 16-byte aligned");
+  if (lengths && !aligned(lengths, 4)) return fail(GDR_EINVAL, "lengths must be 4-byte aligned");
+  if (s0_row && !aligned(s0_row, 4)) return fail(GDR_EINVAL, "s0_row must be 4-byte aligned");
+  if (s_final && s0 && reinterpret_cast<const void*>(s_final) == reinterpret_cast<const void*>(s0) && s0_row)
+    return fail(GDR_EINVAL, "s_final may alias s0 only when s0_row is NULL");
+
+  const size_t need = gdr_prefill_workspace_size(d);
+  if (need > 0) {
+    if (!ws) return fail(GDR_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
+    if (ws_bytes < need) return fail(GDR_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    if (!aligned(ws, 256)) return fail(GDR_EINVAL, "workspace must be 256-byte aligned");
+  }
+
+  const size_t state_bytes = Hv * Dd * Dd * sizeof(float);
+  const Range inputs[] = {
+      range("q", q, B * L * Hk * Dd * esz),   range("k", k, B * L * Hk * Dd * esz),
+      range("v", v, B * L * Hv * Dd * esz),   range("g", g, B * L * Hv * sizeof(float)),
+      range("beta", beta, B * L * Hv * bsz),  range("lengths", lengths, lengths ? B * 4 : 0),
+      range("s0", s0, s0 ? size_t(d->n_s0) * state_bytes : 0), range("s0_row", s0_row, s0_row ? B * 4 : 0),
+  };
+  const Range outs[] = {
+      range("o", o, B * L * Hv * Dd * esz),
+      range("s_final", s_final, s_final ? B * state_bytes : 0),
+      range("workspace", ws, need),
+  };
+  for (const Range& out : outs) {
+    for (const Range& in : inputs) {
+      if (!overlap(out, in)) continue;
+      if (std::strcmp(out.name, "s_final") == 0 && std::strcmp(in.name, "s0") == 0 && out.lo == in.lo) continue;
+      return fail(GDR_EINVAL, "%s overlaps %s", out.name, in.name);
+    }
+  }
+  for (size_t i = 0; i < 3; ++i)
+    for (size_t j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return fail(GDR_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+  return GDR_OK;
+}
+
+// ---------------------------------------------------------------- timing
+struct TimingRecord {
+  int kernel;
+  hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::vector<TimingRecord> g_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep", "gdr_scan"};
+
+}  // namespace
+
+extern "C" {
+
+size_t gdr_prefill_workspace_size(const gdr_desc* d) {
+  if (check_desc(d) != GDR_OK) return size_t(-1);
+  if (size_t(d->B) * d->L == 0) return 0;
+  return gdr::workspace_layout(d->B, d->Hv, num_chunks(d->L), dtype_size(d->qkv_dtype)).total;
+}
+
+gdr_status gdr_prefill_check(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                             const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                             const void* o, const float* s_final, const void* ws, size_t ws_bytes) {
+  return check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, ws, ws_bytes);
+}
+
+gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                       const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row, void* o,
+                       float* s_final, void* ws, size_t ws_bytes, void* stream) {
+  gdr_status st = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, ws, ws_bytes);
+  if (st != GDR_OK) return st;
+  if (d->B == 0) return GDR_OK;
+  if (d->L == 0 && !s_final) return GDR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int NC = num_chunks(d->L);
+  const int bf16 = d->qkv_dtype == GDR_BF16;
+  const gdr::WorkspaceLayout wl = gdr::workspace_layout(d->B, d->Hv, NC, dtype_size(d->qkv_dtype));
+  char* wsb = static_cast<char*>(ws);
+
+  auto timed = [&](int kernel, auto&& launch) -> hipError_t {
+    TimingRecord rec{kernel, nullptr, nullptr};
+    if (g_timing) {
+      rec.start = take_event();
+      rec.stop = take_event();
+      if (rec.start) (void)hipEventRecord(rec.start, s);
+    }
+    hipError_t e = launch();
+    if (g_timing && rec.start && rec.stop) {
+      (void)hipEventRecord(rec.stop, s);
+      g_records.push_back(rec);
+    }
+    return e;
+  };
+
+  if (NC > 0) {
+    gdr::PrepParams pp{q, k, g, beta, lengths, wsb + wl.tb_off, wsb + wl.p_off,
+                       reinterpret_cast<float*>(wsb + wl.scal_off), d->B, d->L, d->Hk, d->Hv, NC};
+    hipError_t e = timed(GDR_KERNEL_PREP, [&] { return gdr::launch_prep(pp, bf16, d->beta_dtype == GDR_BF16, s); });
+    if (e != hipSuccess) return fail(GDR_EHIP, "prep launch: %s", hipGetErrorString(e));
+  }
+  gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final,
+                     NC > 0 ? wsb + wl.tb_off : nullptr, NC > 0 ? wsb + wl.p_off : nullptr,
+                     NC > 0 ? reinterpret_cast<const float*>(wsb + wl.scal_off) : nullptr,
+                     d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0};
+  hipError_t e = timed(GDR_KERNEL_SCAN, [&] { return gdr::launch_scan(sp, bf16, s); });
+  if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+gdr_status gdr_timing_enable(int on) {
+  g_timing = on != 0;
+  return GDR_OK;
+}
+
+gdr_status gdr_timing_read(double* total_ms, int64_t* launches, int n_kernels) {
+  if (n_kernels < 0 || (n_kernels > 0 && (!total_ms || !launches)))
+    return fail(GDR_EINVAL, "timing_read: bad output arrays");
+  for (int i = 0; i < n_kernels; ++i) {
+    total_ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  gdr_status st = GDR_OK;
+  for (const TimingRecord& r : g_records) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      st = fail(GDR_EHIP, "timing_read: event query failed");
+    if (r.kernel < n_kernels) {
+      total_ms[r.kernel] += ms;
+      launches[r.kernel] += 1;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_records.clear();
+  return st;
+}
+
+const char* gdr_kernel_name(int kernel_id) {
+  if (kernel_id < 0 || kernel_id >= GDR_KERNEL_COUNT) return "";
+  return kKernelNames[kernel_id];
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+/*
+ * gdr.h - C ABI of the chunked gated delta rule prefill for AMD MI355X (gfx950).
+ *
+ * What it computes. Per batch row b and value head h, with key head kh = h / (Hv / Hk)
+ * (each key head serves Hv/Hk consecutive value heads, the head sharing of the model page
+ * "deg model" / model.py, function _linear_layer, repeat_interleave along the head axis):
+ *
+ *   q_hat_t = q_t / sqrt(|q_t|^2 + 1e-6) * Dk^-1/2,   k_hat_t = k_t / sqrt(|k_t|^2 + 1e-6)
+ *   beta'_t = beta_t * [t < len_b],                    g'_t = g_t * [t < len_b]
+ *   S <- s0[s0_row[b], h]  (or zeros)
+ *   for t in 0 .. L-1:  S <- exp(g'_t) S;  delta = beta'_t (v_t - S^T k_hat_t);
+ *                       S <- S + k_hat_t delta^T;  o_t = S^T q_hat_t
+ *   s_final[b, h] = S
+ *
+ * This is the float64 truth recurrence of the kernel-test page (r15_kernel_test.py, function
+ * truth_f64) and the per-token reference of the model page (model.py, function
+ * delta_rule_reference, with _l2norm's eps inside the rsqrt), with the exact right-pad guard
+ * of model.py's _dn_gates (pads neither write nor decay). The library evaluates it in
+ * 64-token chunks (per-chunk UT/WY transform with a 64x64 unit-triangular inverse, then a
+ * sequential inter-chunk state scan); the result is the same recurrence up to rounding.
+ * The output at a pad position is what the recurrence gives there (the frozen state read
+ * with that position's q); it is not zeroed.
+ *
+ * Layouts (row-major, contiguous, every pointer 16-byte aligned):
+ *   q, k      [B, L, Hk, Dk]        qkv_dtype
+ *   v, o      [B, L, Hv, Dv]        qkv_dtype
+ *   g         [B, L, Hv]            float32 (log decay, expected <= 0; g > 0 is outside the
+ *                                   method's domain and its result is unspecified)
+ *   beta      [B, L, Hv]            beta_dtype (float32, or qkv_dtype)
+ *   lengths   [B]                   int32, right-pad lengths in [0, L]; NULL = all L valid
+ *   s0        [n_s0, Hv, Dk, Dv]    float32, key index first; NULL = zero initial state
+ *   s0_row    [B]                   int32 rows of s0 each batch row starts from (the fork
+ *                                   model's h0 / h0_idx of model.py, _fork_linear_layer);
+ *                                   NULL = row b starts from s0[b]
+ *   s_final   [B, Hv, Dk, Dv]       float32; NULL = not wanted
+ *   workspace gdr_prefill_workspace_size(desc) bytes, 256-byte aligned
+ * Dk = Dv = 128 are compiled in. q/k/v/beta/g/lengths/s0/s0_row are device pointers to
+ * memory the caller owns and keeps alive until the stream has finished the call; the library
+ * keeps no device allocation of its own and does not retain any pointer after returning.
+ *
+ * Errors. Every argument that can be checked on the host is checked before anything is
+ * launched: GDR_EINVAL, GDR_EUNSUPPORTED and GDR_EWORKSPACE mean nothing was launched and no
+ * output was touched (GDR_EHIP may come after a first launch). The
+ * message of the last non-OK status on the calling thread is gdr_last_error(). Values that
+ * live in device memory (lengths, s0_row) are checked by the kernels themselves: a row whose
+ * length is outside [0, L], or whose s0_row entry is outside [0, n_s0), gets NaN in all of
+ * its o and s_final entries (no memory outside the buffers is ever accessed).
+ * gdr_prefill is asynchronous on `stream`; launch failures return GDR_EHIP.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_EINVAL = -1,        /* a null, misaligned, overlapping or inconsistent argument */
+  GDR_EUNSUPPORTED = -2,  /* a valid request this build does not implement (Dk, Dv != 128) */
+  GDR_EWORKSPACE = -3,    /* workspace missing or smaller than gdr_prefill_workspace_size */
+  GDR_EHIP = -4           /* the HIP runtime reported an error while launching */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+typedef struct {
+  int32_t B, L;           /* batch rows, tokens per row (B, L >= 0) */
+  int32_t Hk, Hv;         /* key heads, value heads; Hv % Hk == 0 */
+  int32_t Dk, Dv;         /* head dims; must be 128 */
+  int32_t n_s0;           /* rows in s0 (ignored when s0 is NULL) */
+  int32_t qkv_dtype;      /* gdr_dtype of q, k, v and o */
+  int32_t beta_dtype;     /* gdr_dtype of beta: GDR_F32 or qkv_dtype */
+} gdr_desc;
+
+/* Bytes of device workspace gdr_prefill needs for this shape (0 when B*L == 0), or
+ * (size_t)-1 when the descriptor itself is invalid (see gdr_last_error). The workspace holds
+ * per-chunk intermediates (the chunk's inverse T*diag(beta), the decayed causal q.k scores
+ * and per-token scalars) and is fully overwritten by every call. */
+size_t gdr_prefill_workspace_size(const gdr_desc* desc);
+
+/* Host-only validation of a gdr_prefill call (same arguments, no stream). Touches no GPU. */
+gdr_status gdr_prefill_check(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                             const float* g, const void* beta, const int32_t* lengths,
+                             const float* s0, const int32_t* s0_row, const void* o,
+                             const float* s_final, const void* workspace, size_t workspace_bytes);
+
+/* The chunked gated delta rule prefill. `stream` is a hipStream_t (NULL = the null stream).
+ * s_final may be the same pointer as s0 (in-place continuation, as the fork model's store
+ * buffer is) only when s0_row is NULL; no other output may overlap any input. */
+gdr_status gdr_prefill(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                       const float* g, const void* beta, const int32_t* lengths, const float* s0,
+                       const int32_t* s0_row, void* o, float* s_final, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* gdr_last_error(void);
+
+/* Kernel timing, for benchmarks. When enabled, gdr_prefill records a HIP event pair on
+ * `stream` around each kernel it launches. gdr_timing_read waits for the recorded events,
+ * writes per-kernel sums of elapsed milliseconds and launch counts for kernel ids
+ * 0 .. n_kernels-1 (GDR_KERNEL_*), and clears the record. Not thread-safe. */
+enum { GDR_KERNEL_PREP = 0, GDR_KERNEL_SCAN = 1, GDR_KERNEL_COUNT = 2 };
+gdr_status gdr_timing_enable(int on);
+gdr_status gdr_timing_read(double* total_ms, int64_t* launches, int n_kernels);
+
+/* Name of a kernel id ("" if out of range), as it appears in profiler traces. */
+const char* gdr_kernel_name(int kernel_id);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDR_H_ */

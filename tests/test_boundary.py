@@ -1,0 +1,187 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, sizes its
+workspace, and rejects every invalid argument on the host before touching a GPU.
+
+No compute call is made here: gdr_prefill is only called with arguments that fail host
+validation (it returns before any HIP call), and valid argument sets go to the host-only
+gdr_prefill_check. The pointers are fake integers; nothing dereferences them.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_deltanet_prefill_gdr_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gdr.library()
+    names = header_functions()
+    assert "gdr_prefill" in names and "gdr_prefill_check" in names and len(names) >= 7
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_kernel_names():
+    assert [gdr.kernel_name(i) for i in range(2)] == ["gdr_prep", "gdr_scan"]
+    assert gdr.kernel_name(5) == ""
+
+
+BASE = 1 << 32   # fake, 256-byte aligned device addresses, far apart
+
+
+class Call:
+    """A valid argument set (fake pointers) that single fields can be broken in."""
+
+    def __init__(self, B=2, L=130, Hk=2, Hv=4, bf16=True, s0=True, s0_row=False, lengths=True, s_final=True):
+        self.desc = gdr.make_desc(B, L, Hk, Hv, n_s0=B if s0 else 0, qkv_bf16=bf16)
+        esz = 2 if bf16 else 4
+        sizes = {"q": B * L * Hk * 128 * esz, "k": B * L * Hk * 128 * esz, "v": B * L * Hv * 128 * esz,
+                 "g": B * L * Hv * 4, "beta": B * L * Hv * 4, "lengths": B * 4, "s0": B * Hv * 128 * 128 * 4,
+                 "s0_row": B * 4, "o": B * L * Hv * 128 * esz, "s_final": B * Hv * 128 * 128 * 4}
+        addr = BASE
+        self.p = {}
+        for name in ("q", "k", "v", "g", "beta", "lengths", "s0", "s0_row", "o", "s_final"):
+            self.p[name] = addr
+            addr += (sizes[name] + 4095) // 4096 * 4096 + 4096
+        if not s0:
+            self.p["s0"] = 0
+        if not s0_row:
+            self.p["s0_row"] = 0
+        if not lengths:
+            self.p["lengths"] = 0
+        if not s_final:
+            self.p["s_final"] = 0
+        self.ws_bytes = gdr.workspace_size(self.desc)
+        self.p["ws"] = addr
+
+    def ptrs(self):
+        return [self.p[n] for n in ("q", "k", "v", "g", "beta", "lengths", "s0", "s0_row", "o", "s_final", "ws")]
+
+    def check(self):
+        return gdr.check(self.desc, self.ptrs(), self.ws_bytes)
+
+    def prefill(self):
+        lib = gdr.library()
+        return lib.gdr_prefill(ctypes.byref(self.desc), *[x or None for x in self.ptrs()], self.ws_bytes, None)
+
+
+def test_valid_calls_pass_host_check():
+    for kw in ({}, {"bf16": False}, {"s0": False}, {"s0_row": True}, {"lengths": False, "s_final": False}):
+        assert Call(**kw).check() == OK, (kw, gdr.last_error())
+
+
+def test_workspace_size():
+    d = gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)
+    ws = gdr.workspace_size(d)
+    # per (head, chunk): two 64x64 bf16 matrices and 4x64 floats
+    assert ws >= 32 * 256 * (2 * 64 * 64 * 2 + 4 * 64 * 4)
+    assert ws < 32 * 256 * (2 * 64 * 64 * 2 + 4 * 64 * 4) + 4096
+    assert gdr.workspace_size(gdr.make_desc(0, 100, 1, 1)) == 0
+    assert gdr.workspace_size(gdr.make_desc(3, 0, 1, 1)) == 0
+    # fp32 doubles the matrices; a partial chunk counts as a whole one
+    assert gdr.workspace_size(gdr.make_desc(1, 65, 1, 1)) == gdr.workspace_size(gdr.make_desc(1, 128, 1, 1))
+    with pytest.raises(gdr.GdrError):
+        gdr.workspace_size(gdr.make_desc(1, 64, 3, 4))
+
+
+def broken(mutate):
+    c = Call()
+    mutate(c)
+    st_check = c.check()
+    st_run = c.prefill()   # fails in host validation, before any HIP call
+    assert st_check == st_run
+    return st_check, gdr.last_error()
+
+
+@pytest.mark.parametrize("field,value,status,msg", [
+    ("B", -1, EINVAL, "must be >= 0"),
+    ("L", -5, EINVAL, "must be >= 0"),
+    ("Hk", 0, EINVAL, "must be > 0"),
+    ("Hv", 3, EINVAL, "multiple of Hk"),
+    ("Dk", 64, EUNSUP, "128"),
+    ("Dv", 256, EUNSUP, "128"),
+    ("qkv_dtype", 7, EINVAL, "not a gdr_dtype"),
+    ("beta_dtype", 5, EINVAL, "beta_dtype"),
+    ("n_s0", 0, EINVAL, "n_s0"),
+    ("n_s0", 1, EINVAL, "n_s0"),
+])
+def test_desc_errors(field, value, status, msg):
+    st, err = broken(lambda c: setattr(c.desc, field, value))
+    assert st == status and msg in err
+
+
+def test_beta_dtype_mismatch():
+    def m(c):
+        c.desc.qkv_dtype = gdr.GDR_F32
+        c.desc.beta_dtype = gdr.GDR_BF16
+        c.ws_bytes = gdr.workspace_size(gdr.make_desc(2, 130, 2, 4, n_s0=2))
+    st, err = broken(m)
+    assert st == EINVAL and "beta_dtype" in err
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "beta", "o"])
+def test_null_required_pointer(name):
+    st, err = broken(lambda c: c.p.__setitem__(name, 0))
+    assert st == EINVAL and "non-NULL" in err
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "o", "s0", "s_final"])
+def test_misaligned_pointer(name):
+    st, err = broken(lambda c: c.p.__setitem__(name, c.p[name] + 8))
+    assert st == EINVAL and "aligned" in err
+
+
+def test_misaligned_workspace():
+    st, err = broken(lambda c: c.p.__setitem__("ws", c.p["ws"] + 16))
+    assert st == EINVAL and "workspace" in err
+
+
+def test_workspace_missing_or_small():
+    st, err = broken(lambda c: c.p.__setitem__("ws", 0))
+    assert st == EWS and "NULL" in err
+    st, err = broken(lambda c: setattr(c, "ws_bytes", c.ws_bytes - 1))
+    assert st == EWS and "needed" in err
+
+
+def test_s0_row_without_s0():
+    def m(c):
+        c.p["s0"] = 0
+        c.p["s0_row"] = c.p["lengths"] + 1024
+    st, err = broken(m)
+    assert st == EINVAL and "s0_row" in err
+
+
+def test_in_place_state():
+    c = Call()
+    c.p["s_final"] = c.p["s0"]
+    assert c.check() == OK                      # in place without s0_row: allowed
+    c.p["s0_row"] = c.p["lengths"] + 4096
+    assert c.check() == EINVAL and "alias" in gdr.last_error()
+
+
+@pytest.mark.parametrize("out,inp", [("o", "q"), ("o", "v"), ("s_final", "k"), ("ws", "g"), ("o", "s0"),
+                                     ("s_final", "beta")])
+def test_outputs_must_not_overlap_inputs(out, inp):
+    st, err = broken(lambda c: c.p.__setitem__(out, c.p[inp] + 256))
+    assert st == EINVAL and "overlaps" in err
+
+
+def test_outputs_must_not_overlap_each_other():
+    st, err = broken(lambda c: c.p.__setitem__("s_final", c.p["o"] + 4096))
+    assert st == EINVAL and "overlaps" in err
+
+
+def test_empty_problems_need_no_pointers():
+    for B, L in ((0, 100), (3, 0)):
+        d = gdr.make_desc(B, L, 1, 2)
+        assert gdr.check(d, [0] * 11, 0) == OK

@@ -1,0 +1,223 @@
+"""HIP path vs the float64 oracle, through the C ABI, on an MI355X.
+
+Bar: max |o_gpu - o_oracle| / max |o_oracle| <= 1e-4 for float32 inputs and <= 2e-2 for
+bfloat16 inputs, over all positions and over valid positions only; the same ratio for the
+final state. Large workloads are checked on sampled rows / heads (each (row, value head) is an
+independent recurrence, so the oracle on a subset is exact).
+"""
+import numpy as np
+import pytest
+import torch
+
+from workloads import CONFIGS, draw
+from gpu_helpers import TOL, compare, run_gpu, run_oracle, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _name_case(request):
+    print(f"\n[case] {request.node.nodeid}", flush=True)
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def check(x, o, s, rows=None, heads=None, label=""):
+    tol = TOL[x.q.dtype]
+    e_all, e_valid, e_s = compare(x, o, s, rows=rows, heads=heads, label=label)
+    assert torch.isfinite(o).all() and torch.isfinite(s).all()
+    assert e_all <= tol and e_valid <= tol and e_s <= tol, (e_all, e_valid, e_s)
+
+
+# ------------------------------------------------------------------ the five workloads
+@pytest.mark.parametrize("i", [1, 2, 3])
+def test_config_full(i):
+    x = CONFIGS[i].draw()
+    o, s = run_gpu(x)
+    check(x, o, s, label=CONFIGS[i].name)
+
+
+def test_config4_forks_sampled_rows():
+    x = CONFIGS[4].draw()
+    o, s = run_gpu(x)
+    lens = x.lengths.numpy()
+    rows = sorted({int(lens.argmin()), int(lens.argmax()), 0, 33})
+    check(x, o, s, rows=rows, label=f"{CONFIGS[4].name} rows={rows}")
+
+
+def test_config5_long_sampled_heads():
+    x = CONFIGS[5].draw()
+    o, s = run_gpu(x)
+    heads = [0, 1, 17, 31]
+    check(x, o, s, heads=heads, label=f"{CONFIGS[5].name} heads={heads}")
+
+
+# ------------------------------------------------------------------ shapes and tails
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 130, 200, 333])
+def test_lengths_and_tails(dtype, L):
+    x = draw(2, L, 2, 4, 128, "R1", 300 + L, dtype, lengths=[L, max(L // 2, 1) - 1 if L > 1 else 0],
+             s0_rows=2)
+    o, s = run_gpu(x)
+    check(x, o, s, label=f"L={L} {dtype}")
+
+
+@pytest.mark.parametrize("regime", ["R2", "R3", "R4", "LONG"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_regimes(regime, dtype):
+    x = draw(1, 256, 2, 4, 128, regime, 400, dtype, s0_rows=1 if regime == "R4" else 0)
+    o, s = run_gpu(x)
+    check(x, o, s, label=f"{regime} {dtype}")
+
+
+def test_no_head_sharing_and_ratio_4():
+    for Hk, Hv in ((3, 3), (1, 4)):
+        x = draw(1, 150, Hk, Hv, 128, "R1", 500 + Hv, torch.bfloat16, s0_rows=1)
+        o, s = run_gpu(x)
+        check(x, o, s, label=f"Hk={Hk} Hv={Hv}")
+
+
+def test_bf16_beta():
+    x = draw(1, 200, 2, 4, 128, "R1", 501, torch.bfloat16)
+    x.beta = x.beta.to(torch.bfloat16)
+    o, s = run_gpu(x)
+    check(x, o, s, label="bf16 beta")
+
+
+# ------------------------------------------------------------------ edge cases
+def test_zero_length_rows_keep_state():
+    x = draw(3, 100, 2, 4, 128, "R1", 502, torch.float32, lengths=[0, 100, 0], s0_rows=3)
+    o, s = run_gpu(x)
+    check(x, o, s, label="zero-length rows")
+    assert torch.equal(s[0].cpu(), x.s0[0]) and torch.equal(s[2].cpu(), x.s0[2])
+
+
+def test_empty_sequence_copies_state():
+    x = draw(2, 0, 2, 4, 128, "R1", 503, torch.float32, s0_rows=2)
+    o, s = run_gpu(x)
+    assert o.shape == (2, 0, 4, 128)
+    assert torch.equal(s.cpu(), x.s0)
+
+
+def test_empty_batch():
+    x = draw(0, 64, 2, 4, 128, "R1", 504, torch.bfloat16)
+    o, s = run_gpu(x)
+    assert o.shape == (0, 64, 4, 128) and s.shape == (0, 4, 128, 128)
+
+
+def test_out_of_range_device_indices_give_nan_rows():
+    import gated_deltanet_prefill_gdr_amd as gdr
+    x = draw(3, 70, 1, 2, 128, "R1", 505, torch.bfloat16, s0_rows=2)
+    dev = "cuda"
+    lengths = torch.tensor([70, 71, 5], dtype=torch.int32, device=dev)        # row 1 invalid
+    s0_row = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)           # row 2 invalid
+    o, s = gdr.prefill(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.g.to(dev), x.beta.to(dev), valid=lengths,
+                       s0=x.s0.to(dev), s0_row=s0_row)
+    torch.cuda.synchronize()
+    assert torch.isnan(o[1].float()).all() and torch.isnan(s[1]).all()
+    assert torch.isnan(o[2].float()).all() and torch.isnan(s[2]).all()
+    assert torch.isfinite(o[0].float()).all() and torch.isfinite(s[0]).all()
+
+
+def test_valid_mask_equals_lengths():
+    x = draw(2, 150, 2, 4, 128, "R1", 506, torch.bfloat16, lengths=[150, 77])
+    o1, s1 = run_gpu(x)
+    import gated_deltanet_prefill_gdr_amd as gdr
+    mask = (torch.arange(150)[None] < x.lengths[:, None]).float().cuda()
+    o2, s2 = gdr.prefill(x.q.cuda(), x.k.cuda(), x.v.cuda(), x.g.cuda(), x.beta.cuda(), valid=mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------------ properties
+def test_deterministic_bitwise():
+    x = draw(2, 300, 2, 4, 128, "R1", 507, torch.bfloat16, lengths=[300, 123], s0_rows=2)
+    o1, s1 = run_gpu(x)
+    o2, s2 = run_gpu(x)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_batch_invariance_bitwise():
+    # A row's result does not depend on the other rows of the batch (fork rows).
+    x = draw(5, 256, 2, 4, 128, "R1", 508, torch.bfloat16, lengths=[256, 40, 200, 1, 129], s0_rows=1,
+             s0_row=[0] * 5)
+    o, s = run_gpu(x)
+    for b in (1, 3):
+        xb = draw(5, 256, 2, 4, 128, "R1", 508, torch.bfloat16, lengths=[256, 40, 200, 1, 129], s0_rows=1,
+                  s0_row=[0] * 5)
+        for n in ("q", "k", "v", "g", "beta", "lengths", "s0_row"):
+            setattr(xb, n, getattr(xb, n)[b:b + 1].contiguous())
+        ob, sb = run_gpu(xb)
+        assert torch.equal(ob[0], o[b]) and torch.equal(sb[0], s[b])
+
+
+def test_pad_garbage_is_ignored():
+    kw = dict(lengths=[200, 90], s0_rows=2)
+    x = draw(2, 200, 2, 4, 128, "R1", 509, torch.bfloat16, **kw)
+    y = draw(2, 200, 2, 4, 128, "R1", 509, torch.bfloat16, zero_pads=False, **kw)
+    assert not torch.equal(x.beta, y.beta)
+    o1, s1 = run_gpu(x)
+    o2, s2 = run_gpu(y)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_head_pairs_identical():
+    x = draw(1, 200, 2, 4, 128, "R1", 510, torch.bfloat16)
+    x.v[:, :, 1::2] = x.v[:, :, 0::2]
+    x.g[:, :, 1::2] = x.g[:, :, 0::2]
+    x.beta[:, :, 1::2] = x.beta[:, :, 0::2]
+    o, s = run_gpu(x)
+    assert torch.equal(o[:, :, 0::2], o[:, :, 1::2]) and torch.equal(s[:, 0::2], s[:, 1::2])
+
+
+def test_split_continuation():
+    x = draw(1, 320, 2, 4, 128, "R2", 511, torch.float32, s0_rows=1)
+    o, s = run_gpu(x)
+    cut = 130   # not a chunk boundary
+    xa = draw(1, 320, 2, 4, 128, "R2", 511, torch.float32, s0_rows=1)
+    xb = draw(1, 320, 2, 4, 128, "R2", 511, torch.float32, s0_rows=1)
+    for n in ("q", "k", "v", "g", "beta"):
+        setattr(xa, n, getattr(x, n)[:, :cut].contiguous())
+        setattr(xb, n, getattr(x, n)[:, cut:].contiguous())
+    oa, sa = run_gpu(xa)
+    xb.s0 = sa.cpu()
+    ob, sb = run_gpu(xb)
+    assert rel_err(torch.cat([oa, ob], 1).cpu().numpy(), o.cpu().numpy()) < 1e-4
+    assert rel_err(sb.cpu().numpy(), s.cpu().numpy()) < 1e-4
+
+
+def test_joint_linearity_2_pow_8():
+    # Scaling (v, S0) by 2^8 scales (o, S_final) by 2^8; power-of-two scaling commutes with
+    # every rounding on the path, so the GPU result scales exactly.
+    x = draw(1, 200, 2, 4, 128, "R2", 512, torch.bfloat16, s0_rows=1)   # nothing subnormal
+    o1, s1 = run_gpu(x)
+    x.v = x.v * 256
+    x.s0 = x.s0 * 256
+    o2, s2 = run_gpu(x)
+    assert torch.equal(o2, o1 * 256) and torch.equal(s2, s1 * 256)
+
+
+def test_in_place_state_continuation():
+    import gated_deltanet_prefill_gdr_amd as gdr
+    x = draw(2, 100, 2, 4, 128, "R1", 513, torch.float32, s0_rows=2)
+    o_ref, s_ref = run_gpu(x)
+    st = x.s0.cuda()
+    o, s = gdr.prefill(x.q.cuda(), x.k.cuda(), x.v.cuda(), x.g.cuda(), x.beta.cuda(), s0=st, s_final=st)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == st.data_ptr()
+    assert torch.equal(o, o_ref) and torch.equal(st, s_ref)
+
+
+def test_kernel_timing_records_both_kernels():
+    import gated_deltanet_prefill_gdr_amd as gdr
+    x = draw(1, 256, 2, 4, 128, "R1", 514, torch.bfloat16)
+    gdr.timing_enable(True)
+    try:
+        run_gpu(x)
+        run_gpu(x)
+        t = gdr.timing_read()
+    finally:
+        gdr.timing_enable(False)
+    assert t["gdr_prep"][1] == 2 and t["gdr_scan"][1] == 2
+    assert t["gdr_prep"][0] > 0 and t["gdr_scan"][0] > 0
