@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -60,8 +62,10 @@ gdr_status check_desc(const gdr_desc* d) {
     return fail(GDR_EINVAL, "beta_dtype must be GDR_F32 or qkv_dtype");
   if (d->Dk != gdr::kHeadDim || d->Dv != gdr::kHeadDim)
     return fail(GDR_EUNSUPPORTED, "Dk = %d, Dv = %d: only Dk = Dv = 128 is built", d->Dk, d->Dv);
-  if (d->Hv > 65535 || d->Hk > 65535 || d->B > 65535)
-    return fail(GDR_EUNSUPPORTED, "B, Hk and Hv must each be <= 65535 (grid limits)");
+  if (d->Hv > 65535 || d->Hk > 65535 || d->B > 65535 || int64_t(d->B) * d->Hv * (gdr::kHeadDim / 16) > INT32_MAX)
+    return fail(GDR_EUNSUPPORTED, "B, Hk, Hv <= 65535 and B*Hv*8 < 2^31 are required (grid limits)");
+  if (int64_t(d->L) * std::max(d->Hk, d->Hv) * gdr::kHeadDim * 4 >= (int64_t(1) << 32))
+    return fail(GDR_EUNSUPPORTED, "L * max(Hk, Hv) * 128 * 4 bytes must stay below 4 GiB per batch row");
   return GDR_OK;
 }
 
@@ -152,7 +156,7 @@ extern "C" {
 size_t gdr_prefill_workspace_size(const gdr_desc* d) {
   if (check_desc(d) != GDR_OK) return size_t(-1);
   if (size_t(d->B) * d->L == 0) return 0;
-  return gdr::workspace_layout(d->B, d->Hv, num_chunks(d->L), dtype_size(d->qkv_dtype)).total;
+  return gdr::workspace_bytes(d->B, d->Hv, num_chunks(d->L), dtype_size(d->qkv_dtype));
 }
 
 gdr_status gdr_prefill_check(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
@@ -171,8 +175,6 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int NC = num_chunks(d->L);
   const int bf16 = d->qkv_dtype == GDR_BF16;
-  const gdr::WorkspaceLayout wl = gdr::workspace_layout(d->B, d->Hv, NC, dtype_size(d->qkv_dtype));
-  char* wsb = static_cast<char*>(ws);
 
   auto timed = [&](int kernel, auto&& launch) -> hipError_t {
     TimingRecord rec{kernel, nullptr, nullptr};
@@ -190,14 +192,11 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
   };
 
   if (NC > 0) {
-    gdr::PrepParams pp{q, k, g, beta, lengths, wsb + wl.tb_off, wsb + wl.p_off,
-                       reinterpret_cast<float*>(wsb + wl.scal_off), d->B, d->L, d->Hk, d->Hv, NC};
+    gdr::PrepParams pp{q, k, g, beta, lengths, ws, d->B, d->L, d->Hk, d->Hv, NC};
     hipError_t e = timed(GDR_KERNEL_PREP, [&] { return gdr::launch_prep(pp, bf16, d->beta_dtype == GDR_BF16, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "prep launch: %s", hipGetErrorString(e));
   }
-  gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final,
-                     NC > 0 ? wsb + wl.tb_off : nullptr, NC > 0 ? wsb + wl.p_off : nullptr,
-                     NC > 0 ? reinterpret_cast<const float*>(wsb + wl.scal_off) : nullptr,
+  gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final, NC > 0 ? ws : nullptr,
                      d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0};
   hipError_t e = timed(GDR_KERNEL_SCAN, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));

@@ -81,14 +81,16 @@ def test_valid_calls_pass_host_check():
 
 
 def test_workspace_size():
-    d = gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)
-    ws = gdr.workspace_size(d)
-    # per (head, chunk): two 64x64 bf16 matrices and 4x64 floats
-    assert ws >= 32 * 256 * (2 * 64 * 64 * 2 + 4 * 64 * 4)
-    assert ws < 32 * 256 * (2 * 64 * 64 * 2 + 4 * 64 * 4) + 4096
+    # one record per (row, value head, chunk): the 6 lower-triangle operand blocks (64 lanes x 8)
+    # of the chunk's T diag(beta) and of its decayed causal scores, in q's dtype, plus 4 x 64 floats
+    rec_bf16 = 2 * 6 * 512 * 2 + 4 * 64 * 4
+    rec_f32 = 2 * 6 * 512 * 4 + 4 * 64 * 4
+    assert rec_bf16 == 13312 and rec_f32 == 25600
+    assert gdr.workspace_size(gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)) == 32 * 256 * rec_bf16
+    assert gdr.workspace_size(gdr.make_desc(2, 130, 2, 4)) == 2 * 4 * 3 * rec_f32
     assert gdr.workspace_size(gdr.make_desc(0, 100, 1, 1)) == 0
     assert gdr.workspace_size(gdr.make_desc(3, 0, 1, 1)) == 0
-    # fp32 doubles the matrices; a partial chunk counts as a whole one
+    # a partial chunk counts as a whole one
     assert gdr.workspace_size(gdr.make_desc(1, 65, 1, 1)) == gdr.workspace_size(gdr.make_desc(1, 128, 1, 1))
     with pytest.raises(gdr.GdrError):
         gdr.workspace_size(gdr.make_desc(1, 64, 3, 4))
