@@ -74,7 +74,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-probe", action="store_true")
     a = ap.parse_args()
     if a.gpus != 1:

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
 HEAD_DIM = 128
 GDR_F32, GDR_BF16 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_EUNSUPPORTED", -3: "GDR_EWORKSPACE", -4: "GDR_EHIP"}
-KERNELS = ("gdr_prep", "gdr_scan")
+KERNELS = ("gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine")
 
 
 class GdrError(RuntimeError):

@@ -1,7 +1,7 @@
 // C ABI of the chunked gated delta rule prefill (declared in include/gdr.h).
 //
 // Host side only: argument validation (no GPU call before every host-checkable argument has
-// passed), workspace sizing, the two kernel launches on the caller's stream, and optional
+// passed), workspace sizing, the kernel launches on the caller's stream, and optional
 // per-kernel HIP-event timing for benchmarks.
 #include "gdr.h"
 
@@ -64,8 +64,8 @@ gdr_status check_desc(const gdr_desc* d) {
     return fail(GDR_EUNSUPPORTED, "Dk = %d, Dv = %d: only Dk = Dv = 128 is built", d->Dk, d->Dv);
   if (d->Hv > 65535 || d->Hk > 65535 || d->B > 65535 || int64_t(d->B) * d->Hv * (gdr::kHeadDim / 16) > INT32_MAX)
     return fail(GDR_EUNSUPPORTED, "B, Hk, Hv <= 65535 and B*Hv*8 < 2^31 are required (grid limits)");
-  if (int64_t(d->L) * std::max(d->Hk, d->Hv) * gdr::kHeadDim * 4 >= (int64_t(1) << 32))
-    return fail(GDR_EUNSUPPORTED, "L * max(Hk, Hv) * 128 * 4 bytes must stay below 4 GiB per batch row");
+  if ((int64_t(d->L) + 2 * gdr::kChunk) * std::max(d->Hk, d->Hv) * gdr::kHeadDim * 4 >= (int64_t(1) << 32))
+    return fail(GDR_EUNSUPPORTED, "(L + 128) * max(Hk, Hv) * 128 * 4 bytes must stay below 4 GiB per batch row");
   return GDR_OK;
 }
 
@@ -147,7 +147,7 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep", "gdr_scan"};
+const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine"};
 
 }  // namespace
 
@@ -196,8 +196,18 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
     hipError_t e = timed(GDR_KERNEL_PREP, [&] { return gdr::launch_prep(pp, bf16, d->beta_dtype == GDR_BF16, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "prep launch: %s", hipGetErrorString(e));
   }
-  gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final, NC > 0 ? ws : nullptr,
-                     d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0};
+  const gdr::SegPlan plan = gdr::seg_plan(d->B, d->Hv, NC, bf16);
+  float* seg = plan.P > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                     gdr::records_bytes(d->B, d->Hv, NC, dtype_size(d->qkv_dtype)))
+                          : nullptr;
+  gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final, NC > 0 ? ws : nullptr, seg,
+                     d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0, plan.P, plan.Ls};
+  if (plan.P > 1) {
+    hipError_t e = timed(GDR_KERNEL_TRANSITION, [&] { return gdr::launch_transition(sp, s); });
+    if (e != hipSuccess) return fail(GDR_EHIP, "transition launch: %s", hipGetErrorString(e));
+    e = timed(GDR_KERNEL_COMBINE, [&] { return gdr::launch_combine(sp, s); });
+    if (e != hipSuccess) return fail(GDR_EHIP, "combine launch: %s", hipGetErrorString(e));
+  }
   hipError_t e = timed(GDR_KERNEL_SCAN, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));
   return GDR_OK;

@@ -27,8 +27,38 @@ inline size_t record_bytes(size_t elem) {
   return 2 * size_t(kFragBlocks) * kBlockElems * elem + 4 * kChunk * sizeof(float);
 }
 
-inline size_t workspace_bytes(int B, int Hv, int NC, size_t elem) {
+// Segments of the bf16 scan. The chunks of each (row, value head) are split into P runs of
+// Ls consecutive chunks (the last run may be shorter) that are scanned in parallel; P = 1 for
+// float32 and whenever the rows and heads alone give enough workgroups.
+constexpr int kSegTargetWorkgroups = 256;   // one per compute unit
+struct SegPlan {
+  int P, Ls;
+};
+inline SegPlan seg_plan(int B, int Hv, int NC, bool bf16) {
+  if (!bf16 || NC <= 1) return SegPlan{1, NC};
+  const int64_t heads = int64_t(B) * Hv;
+  int64_t P = (kSegTargetWorkgroups + heads - 1) / heads;
+  if (P > NC) P = NC;
+  if (P < 1) P = 1;
+  const int Ls = (int)((NC + P - 1) / P);
+  return SegPlan{(NC + Ls - 1) / Ls, Ls};
+}
+
+// Segment states (bf16 with P > 1), after the records: per (row b, value head h) P slots of
+// 128 x 256 floats, slot (b*Hv + h)*P + j. Columns 0..127 of slot j: first the local state
+// B_{j-1} that segment j-1 reaches from a zero state, then (after the combine) the true state
+// entering segment j. Columns 128..255 of slot j: the transition M_j of segment j (column k
+// is the state segment j reaches from e_k with zero values), key index as row.
+constexpr size_t kSlotFloats = size_t(kHeadDim) * 2 * kHeadDim;
+
+inline size_t records_bytes(int B, int Hv, int NC, size_t elem) {
   return size_t(B) * Hv * NC * record_bytes(elem);
+}
+
+inline size_t workspace_bytes(int B, int Hv, int NC, size_t elem) {
+  const SegPlan sp = seg_plan(B, Hv, NC, elem == 2);
+  const size_t seg = sp.P > 1 ? size_t(B) * Hv * sp.P * kSlotFloats * sizeof(float) : 0;
+  return records_bytes(B, Hv, NC, elem) + seg;
 }
 
 struct PrepParams {
@@ -51,10 +81,16 @@ struct ScanParams {
   void* o;
   float* s_final;
   const void* ws;    // records written by the prep kernel
+  float* seg;        // segment states (bf16 with P > 1), see above
   int B, L, Hk, Hv, NC, n_s0;
+  int P, Ls;         // segments and chunks per segment
 };
 
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);
+// bf16 with P > 1: segment transitions (all segments but the last), then the combine that
+// turns them into the state entering every segment; launch_scan always runs last.
+hipError_t launch_transition(const ScanParams& p, hipStream_t s);
+hipError_t launch_combine(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s);
 
 }  // namespace gdr

@@ -1,26 +1,19 @@
-// Sequential inter-chunk state scan of the chunked gated delta rule (gfx950).
+// Inter-chunk state scan of the chunked gated delta rule (gfx950).
 //
 // Per chunk (S = state entering the chunk, [Dk, Dv], fp32; a, c, d, e^{gamma_63}, Tb and P from
 // the chunk record written by the prep kernel; K, Q the raw chunk rows):
 //   X = K S,  R = V - diag(a) X,  Delta = Tb R,  O = diag(c) Q S + P Delta,
 //   S <- e^{gamma_63} S + K^T diag(d) Delta
 // which is the per-token recurrence of the kernel-test page (r15_kernel_test.py, function
-// truth_f64) unrolled over 64 tokens. The state columns evolve independently, so the value
-// dimension is split across workgroups.
+// truth_f64) unrolled over 64 tokens. The value columns of the state evolve independently.
 //
-// gdr_scan_bf16: one workgroup per (row, value head, 16-column slice) = 8 per head. Its four
-// waves share each chunk: wave w computes token tile w (rows 16w..16w+15) of X, Q S, R, Delta
-// and O, and 32 key rows of the state update. Each wave loads its own operand rows (K and Q
-// rows, Tb and P operand blocks, scalars, V) straight into registers two chunks ahead; only K
-// goes through LDS (for the transposed K^T operand of the state update) together with bf16
-// copies of S, R and Delta, exchanged as ready-made MFMA B operands (three barriers per chunk).
-// Workgroups are numbered so that the 8 slices of a head, and the value heads of one key head,
-// run on the same XCD and share its L2.
-//
-// State row order. Wave w holds key rows 32w..32w+31 in two 16x16 accumulator tiles; tile s,
-// row r stands for key index 32w + 8(r >> 2) + 4s + (r & 3). With that order the eight B-operand
-// slots of lane group G are the eight consecutive key indices 32w + 8G .. 32w + 8G + 7, so every
-// A operand along the key index (K and Q rows) is one contiguous 16-byte load per lane.
+// bf16: segment-parallel. The map from the state entering a run of chunks to the state leaving
+// it is affine, S -> M S + B, with M independent of the values. The chunks of each (row, head)
+// are cut into P segments; gdr_transition_bf16 runs every segment but the last from the
+// augmented start [identity | 0] (giving M_j and B_j), gdr_combine chains
+// S_{j+1} = M_j S_j + B_j over the segments, and gdr_scan_bf16 runs every segment again from
+// its true entering state, writing outputs (and, for the last one, the final state). With
+// P = 1 only gdr_scan_bf16 runs.
 //
 // gdr_scan_f32: float32 inputs; one workgroup per (row, value head, 64-column slice), each wave
 // owning 16 columns and walking all chunks on its own (fp32 MFMA, K^T staged in LDS).
@@ -29,306 +22,475 @@
 namespace gdr {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int kSlices16 = D / 16;   // 16-column slices of a head
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// ====================================================================== bf16 cooperative scan
-constexpr int kSlices = D / 16;                                        // workgroups per (row, head)
+// ====================================================================== bf16 segment scan
 constexpr int kRecB = 2 * kFragBlocks * kBlockElems * 2 + 4 * C * 4;   // bf16 record bytes (13312)
 constexpr int kScOff = 2 * kFragBlocks * kBlockElems * 2;              // scalars within the record
-constexpr int kBufK = C * D * 2;                                       // one 64x128 bf16 K tile
+constexpr int kBufK = C * D * 2;                                       // one 64x128 bf16 tile
 
-// LDS: two K tiles (64 rows x 256 B; the 16-byte chunk j of row r is stored at position
-// j ^ (r & 15), which spreads row reads, row writes and transposing reads over the banks) and
-// the operand exchanges.
-struct ScanSmemB {
-  __attribute__((aligned(16))) unsigned char k[2][kBufK];
-  bf16x8 sx[4][64];   // S (bf16) as B operands, k block = 32 key rows
-  bf16x8 rx[2][64];   // R, k block = 32 tokens
-  bf16x8 dx[2][64];   // Delta
-  bf16x8 ddx[2][64];  // diag(d) Delta
-};
-
-// One chunk's operands for one lane, loaded three chunks ahead.
-struct OperandsB {
-  bf16x8 kf[4], qf[4];   // K, Q rows of token tile w, key block kb (8 consecutive key indices)
-  bf16x8 tbf[2], pf[2];  // Tb, P operand blocks of token tile w
-  f4 a, c, d;            // per-token scalars of this lane's four tokens
-  float egc;             // e^{gamma_63}
-  uint32_t v[4];         // V of this lane's four tokens: the 4-byte word holding this lane's column
+// LDS staging of one chunk (all 4 waves read every part of it). Tiles of 64 rows x 256 bytes:
+// K and Q rows with the 16-byte chunk q of row r at position q ^ (r & 15), V rows with it at
+// q ^ 2(r & 7) (these spread the row, column and transposing reads over the banks); the
+// record as written by the prep kernel. Two buffers: chunk c + 1 is loaded while chunk c is
+// computed.
+template <bool kOut> struct SegCfg {
+  static constexpr int NSL = kOut ? 2 : 4;              // 16-column slices per wave
+  static constexpr int kK = 0, kV = kBufK, kRec = 2 * kBufK;
+  static constexpr int kQ = kRec + kRecB;               // outputs only
+  static constexpr int kBuf = kOut ? kQ + kBufK : kRec + kRecB;
+  static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
 };
 
 __device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (row & 15)); }
+__device__ __forceinline__ int swz_v(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (2 * (row & 7))); }
 
-// K^T operand for state tile s of wave w (key index 32w + 8(m >> 2) + 4s + (m & 3) in row m),
-// k = tokens of block kb, from the swizzled K tile. In each 16-lane group the transposing read
-// hands lane j element (j & 3) of the 8 bytes that lanes 4i + (j >> 2) address, i = 0..3; lane
-// n therefore points at K[t0 + (n >> 2)][32w + 8(n & 3) + 4s].
-__device__ __forceinline__ Frag<__bf16> kt_frag(const unsigned char* tile, int w, int s, int kb, int G, int n16) {
-  const int j = 4 * w + (n16 & 3), sub = 8 * s;
-  const int r0 = 32 * kb + 4 * G + (n16 >> 2), r1 = r0 + 16;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + swz(r0, j) + sub));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + swz(r1, j) + sub));
-  Frag<__bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-  return f;
+// Range-checked buffer descriptor as four scalar words, for the loads below.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, kBufferConfig};
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
-__device__ __forceinline__ f4 as_f4(uint4 x) { return __builtin_bit_cast(f4, x); }
+// 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
+// range: zeros). Written as inline assembly so that the compiler neither waits for these loads
+// at every barrier nor moves LDS accesses across them; the kernel counts them itself (vmcnt).
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t off, const unsigned char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(r)
+               : "memory", "m0");
+}
 
-// Loop-carried values of one wave between chunks (c = the chunk about to start):
-//   Y   = K_c S_{c-1} (token tile w; K_0 S_0 before the first chunk)   fp32 accumulator tile
-//   G   = (K_c K_{c-1}^T) rows of token tile w, as A operands over the tokens of chunk c-1
-//   Dd  = diag(d_{c-1}) Delta_{c-1}, as B operands over the tokens of chunk c-1
-//   eg  = e^{gamma_63} of chunk c-1
-// so that X_c = K_c S_c = eg Y + G Dd (S_c = eg S_{c-1} + K_{c-1}^T Dd), i.e. the product with
-// the state entering the chunk is formed one chunk early and only the short correction G Dd
-// sits on the critical path between chunks.
-struct CarryB {
-  f4 y;
-  bf16x8 g[2], dd[2];
-  float eg;
-};
+// Wait until at most N vector-memory operations of this wave are outstanding and all of its
+// LDS accesses are done, then meet the other waves. Memory clobbers keep every LDS access on
+// its side of the wait and the barrier.
+template <int N> __device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N == 0 || N == 8, "extend the list of encodings");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
-__global__ __launch_bounds__(256) void gdr_scan_bf16(ScanParams p) {
-  __shared__ __attribute__((aligned(16))) ScanSmemB sm;
+__device__ __forceinline__ bf16x8 pack8(const f4& lo, const f4& hi) {
+  bf16x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = (__bf16)lo[i];
+    f[4 + i] = (__bf16)hi[i];
+  }
+  return f;
+}
+__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// K^T operand for state tile (key block kb, half s2), k = tokens of token block kb2, from the
+// swizzled K tile. In each 16-lane group the transposing read hands lane m element (m & 3) of
+// the 8 bytes that lanes 4i + (m >> 2) address, i = 0..3; lane n therefore points at
+// K[32 kb2 + 4G + (n >> 2) (+16)][32 kb + 8(n & 3) + 4 s2], and lane m receives key
+// 32 kb + 8(m >> 2) + 4 s2 + (m & 3) for the tokens of slots 0..7.
+__device__ __forceinline__ bf16x8 kt_frag(const unsigned char* tile, int kb, int s2, int kb2, int G, int n16) {
+  const int q = 4 * kb + (n16 & 3), sub = 8 * s2;
+  const int r0 = 32 * kb2 + 4 * G + (n16 >> 2), r1 = r0 + 16;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + swz(r0, q) + sub));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + swz(r1, q) + sub));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// V[t0 + i][col0 + n16], i = 0..3, for the 16 columns starting at col0 (a multiple of 16):
+// lane n points at V[t0 + (n >> 2)][col0 + 4(n & 3)], and the transposing read gives lane m
+// column col0 + m of the four rows.
+__device__ __forceinline__ f4 v_col4(const unsigned char* vt, int t0, int col0, int n16) {
+  const int t = t0 + (n16 >> 2), col = col0 + 4 * (n16 & 3);
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + swz_v(t, col >> 3) + 2 * (col & 7)));
+  const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+  return f4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+}
+
+// Hardware workgroup i runs on XCD i % 8; number logical workgroups so that consecutive ones
+// (neighbouring heads of one segment, which share key and query rows) stay on one XCD.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
+}
+
+__device__ __forceinline__ bool row_is_bad(const ScanParams& p, int b, int& srow) {
+  const int len = p.lengths ? p.lengths[b] : p.L;
+  srow = p.s0 ? (p.s0_row ? p.s0_row[b] : b) : 0;
+  return (len < 0 || len > p.L) || (p.s0 && (srow < 0 || srow >= p.n_s0));
+}
+
+// One segment (chunks [Ls j, Ls j + Ls) of row b, value head h) on one workgroup. Each wave
+// owns NSL 16-column slices of the state (all 128 key rows, fp32 accumulators) and runs the
+// whole chunk recurrence for them on its own: the accumulator layout of one product is the
+// operand layout of the next, so the waves share only the staged chunk, never results.
+//
+// State layout. Slice sl, key block kb (32 keys), half s2: a 16x16 accumulator tile whose row r
+// stands for key 32 kb + 8(r >> 2) + 4 s2 + (r & 3). Lane (n16, G) thus holds keys
+// 32 kb + 8G + 4 s2 + i of column n16, and the two halves together are the eight consecutive
+// keys 32 kb + 8G .. 32 kb + 8G + 7: one bf16 MFMA operand along the key index, matching a single
+// 16-byte read of a K or Q row.
+//
+// kOut = true (outputs): the value columns 32w + 16 sl + n16 start from the state entering the
+// segment and the chunk outputs are written; the last segment writes the final state.
+// kOut = false (transition): each wave holds value columns 32w + 16 sl + n16 (sl = 0, 1) from a
+// zero state (the local state B_j) and identity columns 32w + 16(sl - 2) + n16 (sl = 2, 3) with
+// zero values (the transition M_j), 256 columns in all, written to the augmented column
+// index seg_col; nothing but the two end states is written.
+template <bool kOut>
+__device__ __forceinline__ int seg_col(int w, int sl) {
+  return kOut ? 32 * w + 16 * sl : (sl < 2 ? 32 * w + 16 * sl : D + 32 * w + 16 * (sl - 2));
+}
+
+template <bool kOut>
+__device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds, int b, int h, int j) {
+  using Cfg = SegCfg<kOut>;
+  constexpr int NSL = Cfg::NSL;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, kept in a scalar register
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, G = lane >> 4;
-  // XCD-aware numbering: hardware workgroup i runs on XCD i % 8; consecutive logical ids
-  // (the slices of one head, then the heads of one key head) are kept on one XCD.
-  const int nwg = gridDim.x;                       // B * Hv * kSlices, a multiple of 8
-  const int lam = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int slice = lam % kSlices;
-  const int h = (lam / kSlices) % p.Hv;
-  const int b = lam / (kSlices * p.Hv);
   const int kh = h / (p.Hv / p.Hk);
-  const int col0 = 16 * slice, ncol = col0 + n16;
+  const int c_begin = j * p.Ls, c_end = min(c_begin + p.Ls, p.NC);
   const __bf16* qg = reinterpret_cast<const __bf16*>(p.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(p.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(p.v);
   __bf16* og = reinterpret_cast<__bf16*>(p.o);
-  const unsigned char* wsb = reinterpret_cast<const unsigned char*>(p.ws);
-  const size_t row_stride_v = (size_t)p.Hv * D;
+  const size_t slot0 = ((size_t)b * p.Hv + h) * p.P;   // this head's first segment slot
 
-  const int len = p.lengths ? p.lengths[b] : p.L;
-  const int srow = p.s0 ? (p.s0_row ? p.s0_row[b] : b) : 0;
-  if ((len < 0 || len > p.L) || (p.s0 && (srow < 0 || srow >= p.n_s0))) {
+  int srow = 0;
+  if (kOut && row_is_bad(p, b, srow)) {
     const float nan = __builtin_nanf("");
-    for (int i = tid; i < p.L * 16; i += 256)
-      og[((size_t)b * p.L + i / 16) * row_stride_v + (size_t)h * D + col0 + i % 16] = (__bf16)nan;
-    if (p.s_final)
-      for (int i = tid; i < D * 16; i += 256)
-        p.s_final[(((size_t)b * p.Hv + h) * D + i / 16) * D + col0 + i % 16] = nan;
+    const int t_end = min(c_end * C, p.L);
+    for (int i = c_begin * C * D + tid; i < t_end * D; i += 256)
+      og[((size_t)b * p.L + i / D) * p.Hv * D + (size_t)h * D + i % D] = (__bf16)nan;
+    if (p.s_final && j == p.P - 1)
+      for (int i = tid; i < D * D; i += 256) p.s_final[((size_t)b * p.Hv + h) * D * D + i] = nan;
     return;
   }
 
-  // Range-checked buffer descriptors: rows past L and chunks past the last one read as zeros
-  // and output rows past L are dropped, so the loads below are unconditional and branch-free.
   const uint32_t kq_row = (uint32_t)p.Hk * D * 2, vo_row = (uint32_t)p.Hv * D * 2;
-  const size_t kq_base = (size_t)b * p.L * p.Hk * D, vo_base = (size_t)b * p.L * p.Hv * D + (size_t)h * D + col0;
-  const uint32_t vo_bytes = p.L > 0 ? (uint32_t)(p.L - 1) * vo_row + 32 : 0;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + kq_base, (uint32_t)p.L * kq_row);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + kq_base, (uint32_t)p.L * kq_row);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + vo_base, vo_bytes);
+  const size_t kq_base = (size_t)b * p.L * p.Hk * D, vo_base = ((size_t)b * p.L * p.Hv + h) * D;
+  const uint32_t vo_bytes = p.L > 0 ? (uint32_t)(p.L - 1) * vo_row + D * 2 : 0;
+  const i32x4 rk = rsrc_words(kg + kq_base, (uint32_t)p.L * kq_row);
+  const i32x4 rq = rsrc_words(qg + kq_base, (uint32_t)p.L * kq_row);
+  const i32x4 rv = rsrc_words(vg + vo_base, vo_bytes);
+  const i32x4 rr = rsrc_words(reinterpret_cast<const unsigned char*>(p.ws) + ((size_t)b * p.Hv + h) * p.NC * kRecB,
+                              (uint32_t)p.NC * kRecB);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + vo_base, vo_bytes);
-  const __amdgpu_buffer_rsrc_t rr = make_rsrc(wsb + ((size_t)b * p.Hv + h) * p.NC * kRecB, (uint32_t)p.NC * kRecB);
-  const int t4 = 16 * w + 4 * G;                   // first of this lane's four tokens in a chunk
-  const uint32_t kq_lane = (uint32_t)(16 * w + n16) * kq_row + (uint32_t)kh * D * 2 + 16 * G;
-  const uint32_t blk0 = 1024 * frag_block(w, 0) + 16 * lane;
 
-  auto load = [&](OperandsB& f, int c) {
-    const uint32_t kq = (uint32_t)c * C * kq_row + kq_lane;
+  // This wave's share of chunk c: K (and Q) and V rows 16w .. 16w + 15 (four 1-KB loads each),
+  // record blocks w, w + 4 (, w + 8) and the scalar block 12 (loaded by every wave; the same
+  // bytes land on the same place).
+  auto issue = [&](int c) {
+    unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
+    const uint32_t t0 = (uint32_t)c * C;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f.kf[kb] = as_bf16x8(buf_load16(rk, kq + 64 * kb));
-      f.qf[kb] = as_bf16x8(buf_load16(rq, kq + 64 * kb));
+    for (int m = 0; m < 4; ++m) {
+      const int r = 16 * w + 4 * m + (lane >> 4), pos = lane & 15;
+      const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ (r & 15));
+      dma16(rk, kq, Bf + Cfg::kK + (16 * w + 4 * m) * 256);
+      if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (16 * w + 4 * m) * 256);
+      dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (16 * w + 4 * m) * 256);
     }
-    const uint32_t rec = (uint32_t)c * kRecB;
+    const uint32_t rec = (uint32_t)c * kRecB + 16 * lane;
+    if constexpr (kOut) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {   // block kb = 1 of tiles 0 and 1 is never used (upper triangle)
-      f.tbf[kb] = as_bf16x8(buf_load16(rr, rec + blk0 + 1024 * kb));
-      f.pf[kb] = as_bf16x8(buf_load16(rr, rec + kFragBlocks * 1024 + blk0 + 1024 * kb));
+      for (int m = 0; m < 3; ++m) dma16(rr, rec + 1024 * (w + 4 * m), Bf + Cfg::kRec + 1024 * (w + 4 * m));
+    } else {
+      dma16(rr, rec + 1024 * w, Bf + Cfg::kRec + 1024 * w);                                // Tb blocks 0..3
+      dma16(rr, rec + 1024 * min(w + 4, 5), Bf + Cfg::kRec + 1024 * min(w + 4, 5));        // Tb blocks 4, 5
     }
-    f.a = as_f4(buf_load16(rr, rec + kScOff + 4 * t4));
-    f.c = as_f4(buf_load16(rr, rec + kScOff + 4 * (C + t4)));
-    f.d = as_f4(buf_load16(rr, rec + kScOff + 4 * (2 * C + t4)));
-    f.egc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, rec + kScOff + 4 * 3 * C, 0, 0));
-    const uint32_t vrow = ((uint32_t)c * C + t4) * vo_row + 4 * (n16 >> 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f.v[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vrow + i * vo_row, 0, 0);
+    dma16(rr, rec + kScOff, Bf + Cfg::kRec + kScOff);
   };
 
-  // ---- state key rows of wave w (order above), this slice's 16 columns
-  f4 S[2];
+  // ---- state entering the segment
+  f4 S[NSL][4][2];
   {
-    const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
+    const float* src = nullptr;
+    size_t pitch = 0;
+    if constexpr (kOut) {
+      if (p.P > 1) {
+        src = p.seg + (slot0 + j) * kSlotFloats;
+        pitch = 2 * D;
+      } else if (p.s0) {
+        src = p.s0 + ((size_t)srow * p.Hv + h) * D * D;
+        pitch = D;
+      }
+    }
+    if (src) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[s][i] = s0 ? s0[(32 * w + 8 * G + 4 * s + i) * D + ncol] : 0.f;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              S[sl][kb][s2][i] = src[(32 * kb + 8 * G + 4 * s2 + i) * pitch + seg_col<kOut>(w, sl) + n16];
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)   // zero, or e_k for the identity columns
+              S[sl][kb][s2][i] = (seg_col<kOut>(w, sl) + n16 - D == 32 * kb + 8 * G + 4 * s2 + i) ? 1.f : 0.f;
+    }
   }
-  auto publish_state = [&]() {
-    bf16x8 f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[i] = (__bf16)S[0][i];
-      f[4 + i] = (__bf16)S[1][i];
-    }
-    sm.sx[w][lane] = f;
-  };
 
-  const int nkb = (w >> 1) + 1;   // token blocks of 32 that reach token tile w (lower triangle)
-  // One chunk: f = operands of chunk c, fn = operands of chunk c+1 (only its K rows are used).
-  auto chunk = [&](const OperandsB& f, const OperandsB& fn, CarryB& cy, int c) {
-    unsigned char* Kt = sm.k[c & 1];
-    // -- this wave's K rows into the shared K tile of chunk c
+  issue(c_begin);
+  wait_and_barrier<0>();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    // chunk c has landed for every wave, and every wave is done with chunk c - 1's buffer
+    wait_and_barrier<Cfg::kStores>();
+    if (c + 1 < c_end) issue(c + 1);
+
+    const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
+    const unsigned char* Kt = Bf + Cfg::kK;
+    const unsigned char* Vt = Bf + Cfg::kV;
+    const unsigned char* Rc = Bf + Cfg::kRec;
+    const float* sc = reinterpret_cast<const float*>(Rc + kScOff);
+
+    bf16x8 Sop[NSL][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) *reinterpret_cast<bf16x8*>(Kt + swz(16 * w + n16, 4 * kb + G)) = f.kf[kb];
-    // -- critical: X_c = eg Y + G Dd, R = V - diag(a) X  -> exchange
-    {
-      f4 X = cy.eg * cy.y;
+    for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag<__bf16> Ga, Db;
-        Ga.v = cy.g[kb];
-        Db.v = cy.dd[kb];
-        mma(X, Ga, Db);
-      }
-      bf16x4 rv;
+      for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
+
+    // X = K S
+    f4 X[NSL][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        rv[i] = (__bf16)(__builtin_bit_cast(float, (n16 & 1) ? (f.v[i] & 0xffff0000u) : (f.v[i] << 16)) - f.a[i] * X[i]);
-      reinterpret_cast<bf16x4*>(&sm.rx[w >> 1][lane])[w & 1] = rv;
-    }
-    __syncthreads();
-    // -- critical: Delta = Tb R for token tile w  -> exchange Delta and diag(d) Delta
-    {
-      f4 Dl = f4_splat(0.f);
+    for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb < nkb) {
-          Frag<__bf16> Rf, Tf;
-          Rf.v = sm.rx[kb][lane];
-          Tf.v = f.tbf[kb];
-          mma(Dl, Tf, Rf);
-        }
-      }
-      bf16x4 d1, d2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d1[i] = (__bf16)Dl[i];
-        d2[i] = (__bf16)(f.d[i] * Dl[i]);
-      }
-      reinterpret_cast<bf16x4*>(&sm.dx[w >> 1][lane])[w & 1] = d1;
-      reinterpret_cast<bf16x4*>(&sm.ddx[w >> 1][lane])[w & 1] = d2;
-    }
-    // -- off the critical path (state S_c is in sx): OQ = Q_c S_c, Y' = K_{c+1} S_c, and
-    //    G' = K_{c+1} K_c^T formed as its transpose K_c K_{c+1}^T, whose accumulator layout is
-    //    exactly the A-operand layout G' needs
-    f4 OQ = f4_splat(0.f), Yn = f4_splat(0.f);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      Frag<__bf16> Sf, Qa, Kn;
-      Sf.v = sm.sx[kb][lane];
-      Qa.v = f.qf[kb];
-      Kn.v = fn.kf[kb];
-      mma(OQ, Qa, Sf);
-      mma(Yn, Kn, Sf);
-    }
-    f4 Gt[4];
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      Gt[jt] = f4_splat(0.f);
+      for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = f4_splat(0.f);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        Frag<__bf16> Ka, Kn;
-        Ka.v = *reinterpret_cast<const bf16x8*>(Kt + swz(16 * jt + n16, 4 * kb + G));
-        Kn.v = fn.kf[kb];
-        mma(Gt[jt], Ka, Kn);
+        const bf16x8 kf = lds16(Kt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = mfma(kf, Sop[sl][kb], X[sl][mt]);
       }
     }
-    __syncthreads();
-    // -- O = diag(c) OQ + P Delta (token tile w);  S <- e^{gamma_63} S + K^T diag(d) Delta
-    Frag<__bf16> Df[2], Ddf[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      Df[kb].v = sm.dx[kb][lane];
-      Ddf[kb].v = sm.ddx[kb][lane];
-    }
+    // R = V - diag(a) X  (zero values for the identity columns)
+    bf16x8 Rop[NSL][2];
     {
-      f4 O = f.c * OQ;
+      f4 a4[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (kb < nkb) {
-          Frag<__bf16> Pf;
-          Pf.v = f.pf[kb];
-          mma(O, Pf, Df[kb]);
+      for (int mt = 0; mt < 4; ++mt) a4[mt] = *reinterpret_cast<const f4*>(sc + 16 * mt + 4 * G);
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        const bool has_v = kOut || sl < 2;   // compile-time after unrolling
+        f4 R[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          R[mt] = -a4[mt] * X[sl][mt];
+          if (has_v) R[mt] += v_col4(Vt, 16 * mt + 4 * G, seg_col<kOut>(w, sl), n16);
+        }
+        Rop[sl][0] = pack8(R[0], R[1]);
+        Rop[sl][1] = pack8(R[2], R[3]);
+      }
+    }
+    // Delta = Tb R (lower-triangular blocks only)
+    f4 Dl[NSL][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = f4_splat(0.f);
+#pragma unroll
+      for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
+        const bf16x8 tf = lds16(Rc + 1024 * frag_block(mt, kb2) + 16 * lane);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = mfma(tf, Rop[sl][kb2], Dl[sl][mt]);
+      }
+    }
+    bf16x8 Ddop[NSL][2];
+    {
+      f4 d4[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) d4[mt] = *reinterpret_cast<const f4*>(sc + 2 * C + 16 * mt + 4 * G);
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        Ddop[sl][0] = pack8(Dl[sl][0] * d4[0], Dl[sl][1] * d4[1]);
+        Ddop[sl][1] = pack8(Dl[sl][2] * d4[2], Dl[sl][3] * d4[3]);
+      }
+    }
+    // O^T = diag(c) (S^T Q^T) + Delta^T P^T: the accumulator lane (token n16, G) holds the four
+    // consecutive columns 4G .. 4G + 3 of one token, stored as one 8-byte write.
+    if constexpr (kOut) {
+      const unsigned char* Qt = Bf + Cfg::kQ;
+      bf16x8 Dop[NSL][2];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        Dop[sl][0] = pack8(Dl[sl][0], Dl[sl][1]);
+        Dop[sl][1] = pack8(Dl[sl][2], Dl[sl][3]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f4 Ot[NSL];
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[sl] = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[sl] = mfma(Sop[sl][kb], qf, Ot[sl]);
+        }
+        const float cc = sc[C + 16 * mt + n16];
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[sl] *= cc;
+#pragma unroll
+        for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
+          const bf16x8 pf = lds16(Rc + 1024 * (kFragBlocks + frag_block(mt, kb2)) + 16 * lane);
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[sl] = mfma(Dop[sl][kb2], pf, Ot[sl]);
+        }
+        const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) {
+          const bf16x4 ob = {(__bf16)Ot[sl][0], (__bf16)Ot[sl][1], (__bf16)Ot[sl][2], (__bf16)Ot[sl][3]};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, orow + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
         }
       }
-      const uint32_t ob = ((uint32_t)c * C + t4) * vo_row + 2 * n16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) buf_store_bf16(ro, ob + i * vo_row, (__bf16)O[i]);
     }
-    S[0] *= f.egc;
-    S[1] *= f.egc;
+    // S <- e^{gamma_63} S + K^T diag(d) Delta
+    const float egc = sc[3 * C];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      mma(S[0], kt_frag(Kt, w, 0, kb, G, n16), Ddf[kb]);
-      mma(S[1], kt_frag(Kt, w, 1, kb, G, n16), Ddf[kb]);
-    }
-    publish_state();   // read again after the next chunk's first barrier
-    cy.y = Yn;
-    cy.eg = f.egc;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      cy.dd[kb] = Ddf[kb].v;
-      cy.g[kb] = acc_frag<__bf16>(Gt[2 * kb], Gt[2 * kb + 1], f4_splat(1.f), f4_splat(1.f)).v;
-    }
-  };
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] *= egc;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const bf16x8 kt = kt_frag(Kt, kb, s2, kb2, G, n16);
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] = mfma(kt, Ddop[sl][kb2], S[sl][kb][s2]);
+        }
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS may still be in flight when the workgroup ends
 
-  OperandsB f0, f1, f2;
-  load(f0, 0);
-  load(f1, 1);
-  load(f2, 2);
-  publish_state();
-  // Let the first chunks land before the loop: the loop then starts from the same
-  // outstanding-load pattern as its own steady state, so its waits stay exact.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  CarryB cy;
-  cy.y = f4_splat(0.f);
+  // ---- end state
+  if (kOut && !(p.s_final && j == p.P - 1)) return;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    Frag<__bf16> Sf, Ka;
-    Sf.v = sm.sx[kb][lane];
-    Ka.v = f0.kf[kb];
-    mma(cy.y, Ka, Sf);                 // Y = K_0 S_0
-  }
-  cy.eg = 1.f;
+  for (int sl = 0; sl < NSL; ++sl) {
+    float* dst;
+    size_t pitch;
+    if constexpr (kOut) {
+      dst = p.s_final + ((size_t)b * p.Hv + h) * D * D;
+      pitch = D;
+    } else {
+      dst = p.seg + (slot0 + (sl < 2 ? j + 1 : j)) * kSlotFloats;   // B_j into slot j+1, M_j into slot j
+      pitch = 2 * D;
+    }
+    const int col = seg_col<kOut>(w, sl) + n16;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    cy.g[kb] = bf16x8{};
-    cy.dd[kb] = bf16x8{};
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(32 * kb + 8 * G + 4 * s2 + i) * pitch + col] = S[sl][kb][s2][i];
   }
-  int c = 0;
-  for (; c + 2 < p.NC; c += 3) {   // straight-line body: three chunks, each set reloaded after use
-    chunk(f0, f1, cy, c);
-    load(f0, c + 3);
-    chunk(f1, f2, cy, c + 1);
-    load(f1, c + 4);
-    chunk(f2, f0, cy, c + 2);
-    load(f2, c + 5);
-  }
-  if (c < p.NC) chunk(f0, f1, cy, c);
-  if (c + 1 < p.NC) chunk(f1, f2, cy, c + 1);
+}
 
-  if (p.s_final) {
-    float* sf = p.s_final + ((size_t)b * p.Hv + h) * D * D;
+// Outputs: one workgroup per (row, segment, value head), heads fastest.
+__global__ __launch_bounds__(256) void gdr_scan_bf16(ScanParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<true>::kBuf];
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lam % p.Hv, j = (lam / p.Hv) % p.P, b = lam / (p.Hv * p.P);
+  seg_body<true>(p, lds, b, h, j);
+}
+
+// Transitions: one workgroup per (row, segment < P - 1, value head).
+__global__ __launch_bounds__(256) void gdr_transition_bf16(ScanParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<false>::kBuf];
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
+  seg_body<false>(p, lds, b, h, j);
+}
+
+// Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero). One
+// workgroup per (row, value head, 16-column slice); wave w computes key rows 32w .. 32w + 31
+// (tiles 2w, 2w + 1, plain row order) and the waves exchange the state each step as bf16
+// hi + lo operand pairs, so that with M = Mh + Ml the products Mh Sh + Mh Sl + Ml Sh keep
+// about 16 significant bits more than bf16 alone.
+__global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
+  __shared__ bf16x8 sx[2][2][4][64];   // [step parity][hi, lo][wave][lane]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, G = lane >> 4;
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = lam % kSlices16, h = (lam / kSlices16) % p.Hv, b = lam / (kSlices16 * p.Hv);
+  int srow = 0;
+  if (row_is_bad(p, b, srow)) return;   // the output pass writes NaN for this row
+  const int col = 16 * slice + n16;
+  float* slots = p.seg + ((size_t)b * p.Hv + h) * p.P * kSlotFloats;
+
+  f4 S[2];
+  const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+  for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sf[(32 * w + 8 * G + 4 * s + i) * D + ncol] = S[s][i];
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * w + 16 * s2 + 4 * G + i;
+      S[s2][i] = s0 ? s0[row * D + col] : 0.f;
+      slots[row * 2 * D + col] = S[s2][i];
+    }
+  for (int jj = 0; jj + 1 < p.P; ++jj) {
+    const float* M = slots + jj * kSlotFloats + D;   // M_jj, row pitch 2D
+    float* Bn = slots + (jj + 1) * kSlotFloats;       // B_jj, replaced by the state entering jj + 1
+    f4 Bv[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bv[s2][i] = Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
+    bf16x8 mh[2][4], ml[2][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float* mrow = M + (32 * w + 16 * s2 + n16) * 2 * D + 32 * kb + 4 * G;
+        const f4 m0 = *reinterpret_cast<const f4*>(mrow), m1 = *reinterpret_cast<const f4*>(mrow + 16);
+        mh[s2][kb] = pack8(m0, m1);
+        f4 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r0[i] = m0[i] - (float)mh[s2][kb][i];
+          r1[i] = m1[i] - (float)mh[s2][kb][4 + i];
+        }
+        ml[s2][kb] = pack8(r0, r1);
+      }
+    {
+      const bf16x8 hi = pack8(S[0], S[1]);
+      f4 r0, r1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r0[i] = S[0][i] - (float)hi[i];
+        r1[i] = S[1][i] - (float)hi[4 + i];
+      }
+      sx[jj & 1][0][w][lane] = hi;
+      sx[jj & 1][1][w][lane] = pack8(r0, r1);
+    }
+    __syncthreads();
+    f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 sh = sx[jj & 1][0][kb][lane], sl = sx[jj & 1][1][kb][lane];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        acc[s2] = mfma(mh[s2][kb], sh, acc[s2]);
+        acc[s2] = mfma(mh[s2][kb], sl, acc[s2]);
+        acc[s2] = mfma(ml[s2][kb], sh, acc[s2]);
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      S[s2] = acc[s2] + Bv[s2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+    }
   }
 }
 
@@ -505,9 +667,19 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
   }
 }
 
+hipError_t launch_transition(const ScanParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(gdr_transition_bf16, dim3(p.B * p.Hv * (p.P - 1)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const ScanParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(gdr_combine, dim3(p.B * p.Hv * kSlices16), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s) {
   if (qkv_bf16) {
-    hipLaunchKernelGGL(gdr_scan_bf16, dim3(p.B * p.Hv * kSlices), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(gdr_scan_bf16, dim3(p.B * p.Hv * p.P), dim3(256), 0, s, p);
   } else {
     hipLaunchKernelGGL(gdr_scan_f32, dim3(D / 64, p.Hv, p.B), dim3(256), 0, s, p);
   }

@@ -79,7 +79,9 @@ typedef struct {
 /* Bytes of device workspace gdr_prefill needs for this shape (0 when B*L == 0), or
  * (size_t)-1 when the descriptor itself is invalid (see gdr_last_error). The workspace holds
  * per-chunk intermediates (the chunk's inverse T*diag(beta), the decayed causal q.k scores
- * and per-token scalars) and is fully overwritten by every call. */
+ * and per-token scalars) and, for bf16 sequences long enough to be cut into segments that are
+ * scanned in parallel, each segment's state map and entering state. Every call writes all of
+ * it before reading it. */
 size_t gdr_prefill_workspace_size(const gdr_desc* desc);
 
 /* Host-only validation of a gdr_prefill call (same arguments, no stream). Touches no GPU. */
@@ -103,7 +105,13 @@ const char* gdr_last_error(void);
  * `stream` around each kernel it launches. gdr_timing_read waits for the recorded events,
  * writes per-kernel sums of elapsed milliseconds and launch counts for kernel ids
  * 0 .. n_kernels-1 (GDR_KERNEL_*), and clears the record. Not thread-safe. */
-enum { GDR_KERNEL_PREP = 0, GDR_KERNEL_SCAN = 1, GDR_KERNEL_COUNT = 2 };
+enum {
+  GDR_KERNEL_PREP = 0,        /* per-chunk transform: norms, decays, T diag(beta), scores */
+  GDR_KERNEL_SCAN = 1,        /* state scan writing o (and s_final) */
+  GDR_KERNEL_TRANSITION = 2,  /* bf16 long sequences: per-segment state maps */
+  GDR_KERNEL_COMBINE = 3,     /* bf16 long sequences: chains the segment maps */
+  GDR_KERNEL_COUNT = 4
+};
 gdr_status gdr_timing_enable(int on);
 gdr_status gdr_timing_read(double* total_ms, int64_t* launches, int n_kernels);
 
