@@ -26,7 +26,7 @@ CHUNK, D = 64, 128
 
 
 def algorithmic(B, L, Hk, Hv, esz, n_s0, want_state):
-    """Algorithmic bytes and flops of one call.
+    """Algorithmic bytes and flops of one call (the whole path).
 
     Bytes: read q, k, v, g, beta, s0 (if any), lengths; write o and s_final (if wanted).
     Flops per (token, value head): 6 D^2 + 10 C D (the chunked method counted with full 64x64
@@ -40,6 +40,51 @@ def algorithmic(B, L, Hk, Hv, esz, n_s0, want_state):
               + (B * Hv * D * D * 4 if want_state else 0))
     flops = units * (6 * D * D + 10 * CHUNK * D)
     return units, nbytes, flops
+
+
+def kernel_bytes(name, B, L, Hk, Hv, esz, P):
+    """Bytes a kernel of the path must read and write through its own interface, one launch.
+
+    Intermediates count where they cross HBM: the per-chunk record (T diag(beta) and decayed
+    scores in q's dtype, 4 x 64 fp32 scalars) and the segment slots (128 x 256 fp32 each).
+    """
+    NC = (L + CHUNK - 1) // CHUNK
+    rec = 2 * 6 * 512 * esz + 4 * CHUNK * 4
+    rec_tb = 6 * 512 * esz + 4 * CHUNK * 4          # the part the transitions read
+    slot = D * 2 * D * 4
+    qk = B * L * Hk * D * esz
+    vo = B * L * Hv * D * esz
+    gb = 2 * B * L * Hv * 4
+    recs = B * Hv * NC * rec
+    frac = (P - 1) / P if P > 1 else 0.0                 # share of chunks in the first P-1 segments
+    if name == "gdr_prep":
+        return 2 * qk + gb + recs
+    if name == "gdr_transition":
+        return frac * (qk + vo + B * Hv * NC * rec_tb) + B * Hv * (P - 1) * slot
+    if name == "gdr_combine":
+        return B * Hv * (P - 1) * (slot * 3 // 2) + B * Hv * P * slot // 2
+    if name == "gdr_scan":
+        return 2 * qk + 2 * vo + recs + B * Hv * D * D * 4 + (B * Hv * P * slot // 2 if P > 1 else 0)
+    raise KeyError(name)
+
+
+def seg_plan(B, Hv, NC, bf16=True):
+    """Number of segments the library cuts each (row, head) into (mirrors the C side)."""
+    if not bf16 or NC <= 1:
+        return 1
+    P = min(NC, max(1, -(-256 // (B * Hv))))
+    Ls = -(-NC // P)
+    return -(-NC // Ls)
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_deltanet_prefill_gdr_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(x, heads):
@@ -120,15 +165,19 @@ def main():
     ms = start.elapsed_time(stop) / a.steps
 
     units, nbytes, flops = algorithmic(B, L, Hk, Hv, 2, 0, True)
-    per_kernel = {n: (t / max(c, 1), c) for n, (t, c) in kern.items()}
+    P = seg_plan(B, Hv, (L + CHUNK - 1) // CHUNK)
+    per_kernel = {n: (t / max(c, 1), c) for n, (t, c) in kern.items() if c > 0}
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
     k_ms = per_kernel[dominant][0]
-    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    k_bytes = kernel_bytes(dominant, B, L, Hk, Hv, 2, P)
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
     traffic = None
-    prof = os.path.join(ROOT, "profiles", "traffic_gdr_scan_l16384_bf16.json")
+    prof = os.path.join(ROOT, "profiles", "traffic_l16384_bf16.json")
     if os.path.exists(prof):
         with open(prof) as f:
-            traffic = json.load(f).get(dominant)
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash():   # counters of these very kernels only
+            traffic = tr.get("kernels", {}).get(dominant, {}).get("hbm_bytes")
     line = {
         "metric": METRIC,
         "value": units / (ms * 1e-3),
@@ -147,11 +196,13 @@ def main():
                    "B": B, "L": L, "Hk": Hk, "Hv": Hv, "D": Dk, "global_batch": B, "seq_len": L,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
+                     "kernel_bytes": k_bytes, "kernel_ms": k_ms},
         "path": {"ms": ms, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                  "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": nbytes, "alg_flops": flops,
-                 "kernel_ms": {n: t for n, (t, c) in per_kernel.items()}},
+                 "kernel_ms": {n: t for n, (t, c) in per_kernel.items()}, "segments": P,
+                 "source_hash": source_hash()},
         "cpu_baseline": None,
     }
     if not a.no_cpu_baseline:

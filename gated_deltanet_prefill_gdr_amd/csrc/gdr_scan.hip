@@ -31,20 +31,32 @@ constexpr int kRecB = 2 * kFragBlocks * kBlockElems * 2 + 4 * C * 4;   // bf16 r
 constexpr int kScOff = 2 * kFragBlocks * kBlockElems * 2;              // scalars within the record
 constexpr int kBufK = C * D * 2;                                       // one 64x128 bf16 tile
 
-// LDS staging of one chunk (all 4 waves read every part of it). Tiles of 64 rows x 256 bytes:
-// K and Q rows with the 16-byte chunk q of row r at position q ^ (r & 15), V rows with it at
-// q ^ 2(r & 7) (these spread the row, column and transposing reads over the banks); the
-// record as written by the prep kernel. Two buffers: chunk c + 1 is loaded while chunk c is
+// LDS staging of one chunk (every wave reads every part of it): K, V (and Q) tiles of 64 rows x
+// 256 bytes, swizzled as below, and the record as written by the prep kernel. Two buffers: chunk c + 1 is loaded while chunk c is
 // computed.
+#ifndef GDR_SEG_WAVES_OUT
+#define GDR_SEG_WAVES_OUT 8
+#endif
+#ifndef GDR_SEG_WAVES_TRANSITION
+#define GDR_SEG_WAVES_TRANSITION 8
+#endif
 template <bool kOut> struct SegCfg {
-  static constexpr int NSL = kOut ? 2 : 4;              // 16-column slices per wave
+  static constexpr int NW = kOut ? GDR_SEG_WAVES_OUT : GDR_SEG_WAVES_TRANSITION;   // waves per workgroup
+  static constexpr int NSL = (kOut ? 8 : 16) / NW;      // 16-column slices per wave
   static constexpr int kK = 0, kV = kBufK, kRec = 2 * kBufK;
   static constexpr int kQ = kRec + kRecB;               // outputs only
   static constexpr int kBuf = kOut ? kQ + kBufK : kRec + kRecB;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
+  static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (row & 15)); }
+// K and Q tiles: the 16-byte chunk q of row r sits at position q ^ f(r), f swapping the two
+// 2-bit fields of r mod 16. Sixteen consecutive rows of one chunk (the row operands) and four
+// consecutive rows of four consecutive chunks (the transposing reads) then both land on 16
+// distinct positions, i.e. on all 64 banks once. V tiles: position q ^ 2(r & 7), which keeps the
+// two chunks of eight consecutive rows read together apart.
+__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ swz_f(row)); }
 __device__ __forceinline__ int swz_v(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (2 * (row & 7))); }
 
 // Range-checked buffer descriptor as four scalar words, for the loads below.
@@ -58,7 +70,8 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
 // at every barrier nor moves LDS accesses across them; the kernel counts them itself (vmcnt).
 __device__ __forceinline__ void dma16(const i32x4& r, uint32_t off, const unsigned char* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(r)
+  // M0 is not otherwise used by these kernels; one wait state separates its write from the load.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(r)
                : "memory", "m0");
 }
 
@@ -66,8 +79,9 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t off, const unsign
 // LDS accesses are done, then meet the other waves. Memory clobbers keep every LDS access on
 // its side of the wait and the barrier.
 template <int N> __device__ __forceinline__ void wait_and_barrier() {
-  static_assert(N == 0 || N == 8, "extend the list of encodings");
+  static_assert(N == 0 || N == 4 || N == 8, "extend the list of encodings");   // stores per chunk
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
@@ -131,21 +145,29 @@ __device__ __forceinline__ bool row_is_bad(const ScanParams& p, int b, int& srow
 // keys 32 kb + 8G .. 32 kb + 8G + 7: one bf16 MFMA operand along the key index, matching a single
 // 16-byte read of a K or Q row.
 //
-// kOut = true (outputs): the value columns 32w + 16 sl + n16 start from the state entering the
+// kOut = true (outputs): the value columns seg_col + n16 start from the state entering the
 // segment and the chunk outputs are written; the last segment writes the final state.
-// kOut = false (transition): each wave holds value columns 32w + 16 sl + n16 (sl = 0, 1) from a
-// zero state (the local state B_j) and identity columns 32w + 16(sl - 2) + n16 (sl = 2, 3) with
-// zero values (the transition M_j), 256 columns in all, written to the augmented column
-// index seg_col; nothing but the two end states is written.
+// kOut = false (transition): the first half of each wave's slices hold value columns from a
+// zero state (the local state B_j), the second half identity columns with zero values (the
+// transition M_j), 256 columns in all (augmented index seg_col); nothing but the two end states
+// is written.
+// Column of slice sl of wave w: value columns for the outputs; for the transitions the first
+// half of a wave's slices are value columns (local state) and the second half identity columns
+// (transition), stored at augmented index 128 + k.
 template <bool kOut>
 __device__ __forceinline__ int seg_col(int w, int sl) {
-  return kOut ? 32 * w + 16 * sl : (sl < 2 ? 32 * w + 16 * sl : D + 32 * w + 16 * (sl - 2));
+  constexpr int NSL = SegCfg<kOut>::NSL, H = NSL / 2;
+  if constexpr (kOut) return 16 * (w * NSL + sl);
+  else return sl < H ? 16 * (w * H + sl) : D + 16 * (w * H + sl - H);
+}
+template <bool kOut> __device__ __forceinline__ constexpr bool seg_has_v(int sl) {
+  return kOut || sl < SegCfg<kOut>::NSL / 2;
 }
 
 template <bool kOut>
 __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds, int b, int h, int j) {
   using Cfg = SegCfg<kOut>;
-  constexpr int NSL = Cfg::NSL;
+  constexpr int NSL = Cfg::NSL, NW = Cfg::NW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, G = lane >> 4;
@@ -161,10 +183,10 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   if (kOut && row_is_bad(p, b, srow)) {
     const float nan = __builtin_nanf("");
     const int t_end = min(c_end * C, p.L);
-    for (int i = c_begin * C * D + tid; i < t_end * D; i += 256)
+    for (int i = c_begin * C * D + tid; i < t_end * D; i += 64 * NW)
       og[((size_t)b * p.L + i / D) * p.Hv * D + (size_t)h * D + i % D] = (__bf16)nan;
     if (p.s_final && j == p.P - 1)
-      for (int i = tid; i < D * D; i += 256) p.s_final[((size_t)b * p.Hv + h) * D * D + i] = nan;
+      for (int i = tid; i < D * D; i += 64 * NW) p.s_final[((size_t)b * p.Hv + h) * D * D + i] = nan;
     return;
   }
 
@@ -178,29 +200,31 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
                               (uint32_t)p.NC * kRecB);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + vo_base, vo_bytes);
 
-  // This wave's share of chunk c: K (and Q) and V rows 16w .. 16w + 15 (four 1-KB loads each),
-  // record blocks w, w + 4 (, w + 8) and the scalar block 12 (loaded by every wave; the same
-  // bytes land on the same place).
+  // This wave's share of chunk c: K (and Q) and V rows R w .. R w + R - 1 (R = 64 / NW, loads
+  // of four rows each) and the record blocks w, w + NW, ... (outputs: blocks 0..12; transitions:
+  // the Tb blocks 0..5 and the scalar block 12).
+  constexpr int R = C / NW;
   auto issue = [&](int c) {
     unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const uint32_t t0 = (uint32_t)c * C;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int r = 16 * w + 4 * m + (lane >> 4), pos = lane & 15;
-      const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ (r & 15));
-      dma16(rk, kq, Bf + Cfg::kK + (16 * w + 4 * m) * 256);
-      if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (16 * w + 4 * m) * 256);
-      dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (16 * w + 4 * m) * 256);
+    for (int m = 0; m < R / 4; ++m) {
+      const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
+      const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
+      dma16(rk, kq, Bf + Cfg::kK + (R * w + 4 * m) * 256);
+      if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
+      dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (R * w + 4 * m) * 256);
     }
     const uint32_t rec = (uint32_t)c * kRecB + 16 * lane;
-    if constexpr (kOut) {
+    constexpr int nblk = kOut ? 13 : 7;
 #pragma unroll
-      for (int m = 0; m < 3; ++m) dma16(rr, rec + 1024 * (w + 4 * m), Bf + Cfg::kRec + 1024 * (w + 4 * m));
-    } else {
-      dma16(rr, rec + 1024 * w, Bf + Cfg::kRec + 1024 * w);                                // Tb blocks 0..3
-      dma16(rr, rec + 1024 * min(w + 4, 5), Bf + Cfg::kRec + 1024 * min(w + 4, 5));        // Tb blocks 4, 5
+    for (int i0 = 0; i0 < nblk; i0 += NW) {
+      const int i = i0 + w;
+      if (i < nblk) {   // wave-uniform
+        const int blk = (kOut || i < 6) ? i : 12;
+        dma16(rr, rec + 1024 * blk, Bf + Cfg::kRec + 1024 * blk);
+      }
     }
-    dma16(rr, rec + kScOff, Bf + Cfg::kRec + kScOff);
   };
 
   // ---- state entering the segment
@@ -281,7 +305,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       for (int mt = 0; mt < 4; ++mt) a4[mt] = *reinterpret_cast<const f4*>(sc + 16 * mt + 4 * G);
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) {
-        const bool has_v = kOut || sl < 2;   // compile-time after unrolling
+        const bool has_v = seg_has_v<kOut>(sl);   // compile-time after unrolling
         f4 R[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -382,7 +406,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       dst = p.s_final + ((size_t)b * p.Hv + h) * D * D;
       pitch = D;
     } else {
-      dst = p.seg + (slot0 + (sl < 2 ? j + 1 : j)) * kSlotFloats;   // B_j into slot j+1, M_j into slot j
+      dst = p.seg + (slot0 + (seg_has_v<kOut>(sl) ? j + 1 : j)) * kSlotFloats;   // B_j into slot j+1, M_j into slot j
       pitch = 2 * D;
     }
     const int col = seg_col<kOut>(w, sl) + n16;
@@ -396,7 +420,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 }
 
 // Outputs: one workgroup per (row, segment, value head), heads fastest.
-__global__ __launch_bounds__(256) void gdr_scan_bf16(ScanParams p) {
+__global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<true>::kBuf];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % p.P, b = lam / (p.Hv * p.P);
@@ -404,7 +428,7 @@ __global__ __launch_bounds__(256) void gdr_scan_bf16(ScanParams p) {
 }
 
 // Transitions: one workgroup per (row, segment < P - 1, value head).
-__global__ __launch_bounds__(256) void gdr_transition_bf16(ScanParams p) {
+__global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<false>::kBuf];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
@@ -668,7 +692,7 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
 }
 
 hipError_t launch_transition(const ScanParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(gdr_transition_bf16, dim3(p.B * p.Hv * (p.P - 1)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(gdr_transition_bf16, dim3(p.B * p.Hv * (p.P - 1)), dim3(64 * SegCfg<false>::NW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -679,7 +703,7 @@ hipError_t launch_combine(const ScanParams& p, hipStream_t s) {
 
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s) {
   if (qkv_bf16) {
-    hipLaunchKernelGGL(gdr_scan_bf16, dim3(p.B * p.Hv * p.P), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(gdr_scan_bf16, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
   } else {
     hipLaunchKernelGGL(gdr_scan_f32, dim3(D / 64, p.Hv, p.B), dim3(256), 0, s, p);
   }
