@@ -4,6 +4,8 @@ The pages print no output values for this method, so the oracle is pinned agains
 mathematics fixes: closed forms of special regimes, exact invariants, and an independent
 chunked formulation on tiny shapes. Each test names the mistake it is there to catch.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -292,3 +294,19 @@ def test_generator_correlated_keys():
     u = k.mean(1, keepdim=True)
     cos = (k * u).sum(-1) / (k.norm(dim=-1) * u.norm(dim=-1))
     assert cos.min() > 0.8        # keys cluster around one direction per key head
+
+
+def test_golden_regression_fixture():
+    """The oracle still reproduces its frozen output on one tiny case (tests/golden)."""
+    import json
+    import importlib.util
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    with open(os.path.join(here, "oracle_small.json")) as f:
+        ref = json.load(f)
+    spec = importlib.util.spec_from_file_location("make_golden", os.path.join(here, "make_golden.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert mod.CASE == {k: (v if not isinstance(v, list) else v) for k, v in ref["case"].items()}
+    o, s = mod.compute()
+    np.testing.assert_allclose(o, np.array(ref["o"]), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(s, np.array(ref["s_final"]), rtol=1e-12, atol=1e-15)
