@@ -62,8 +62,9 @@ gdr_status check_desc(const gdr_desc* d) {
     return fail(GDR_EINVAL, "beta_dtype must be GDR_F32 or qkv_dtype");
   if (d->Dk != gdr::kHeadDim || d->Dv != gdr::kHeadDim)
     return fail(GDR_EUNSUPPORTED, "Dk = %d, Dv = %d: only Dk = Dv = 128 is built", d->Dk, d->Dv);
-  if (d->Hv > 65535 || d->Hk > 65535 || d->B > 65535 || int64_t(d->B) * d->Hv * (gdr::kHeadDim / 16) > INT32_MAX)
-    return fail(GDR_EUNSUPPORTED, "B, Hk, Hv <= 65535 and B*Hv*8 < 2^31 are required (grid limits)");
+  if (d->Hv > 65535 || d->Hk > 65535 || d->B > 65535 || int64_t(d->B) * d->Hv * (gdr::kHeadDim / 16) > INT32_MAX ||
+      int64_t(d->B) * d->Hv * num_chunks(d->L) > INT32_MAX)
+    return fail(GDR_EUNSUPPORTED, "B, Hk, Hv <= 65535, B*Hv*8 < 2^31 and B*Hv*ceil(L/64) < 2^31 are required (grid limits)");
   if ((int64_t(d->L) + 2 * gdr::kChunk) * std::max(d->Hk, d->Hv) * gdr::kHeadDim * 4 >= (int64_t(1) << 32))
     return fail(GDR_EUNSUPPORTED, "(L + 128) * max(Hk, Hv) * 128 * 4 bytes must stay below 4 GiB per batch row");
   return GDR_OK;

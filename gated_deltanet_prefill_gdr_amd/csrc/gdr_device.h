@@ -138,6 +138,12 @@ __device__ __forceinline__ int block_kb(int blk) { return blk < 2 ? 0 : (blk - 2
 // Column (within the 64-token chunk) of slot j of lane group G in token block kb.
 __device__ __forceinline__ int slot_col(int kb, int G, int j) { return 32 * kb + (j < 4 ? 4 * G + j : 12 + 4 * G + j); }
 
+// Hardware workgroup i runs on XCD i % 8. Logical workgroup lam = xcd_remap(i, n) numbers them so
+// that consecutive logical ids run on one XCD (and share its L2); a bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
+}
+
 }  // namespace gdr
 
 #endif  // GDR_DEVICE_H_

@@ -1,20 +1,29 @@
-// Per-chunk preparation for the chunked gated delta rule (gfx950).
+// Per-chunk transform of the chunked gated delta rule (gfx950).
 //
-// One workgroup (4 waves) per (row b, key head kh, chunk c). From the chunk's raw q and k it
-// forms, for every value head h served by kh (h = kh*r .. kh*r + r-1):
+// One workgroup (4 waves) per (row b, value head h, chunk c), with key head kh = h / (Hv / Hk).
+// From the chunk's raw q, k, g and beta it forms
 //   rk_t = (|k_t|^2 + 1e-6)^-1/2,  rq_t = (|q_t|^2 + 1e-6)^-1/2 * 128^-1/2   (model page model.py,
 //          function _l2norm, eps inside the rsqrt; q scaled by Dk^-1/2 as in delta_rule_reference)
 //   beta'_t, g'_t with the right-pad guard (model.py, _dn_gates: pads neither write nor decay)
 //   gamma_t = inclusive cumulative sum of g' within the chunk
 //   A[t][i] = beta'_t e^{gamma_t - gamma_i} rk_t rk_i (k_t . k_i)   (i < t)
 //   T = (I + A)^-1, Tb = T diag(beta'),  P[t][i] = rq_t rk_i e^{gamma_t - gamma_i} (q_t . k_i)  (i <= t)
-// and writes the chunk record (lower-triangle 16x16 tiles of Tb and P, then the per-token scalars
-// a = e^gamma rk, c = e^gamma rq, d = rk e^{gamma_63 - gamma} and e^{gamma_63}). The Gram K K^T
-// and Q K^T run on MFMA once per key head and serve all r value heads. Exponents are only taken
-// of non-positive differences on the kept triangle ("direct" decay from in-chunk differences).
+// and writes the chunk record: Tb and P as MFMA operand blocks (lower triangle only), then the
+// per-token scalars a = e^gamma rk, c = e^gamma rq, d = rk e^{gamma_63 - gamma} and e^{gamma_63}.
+// Exponents are only taken of non-positive differences on the kept triangle ("direct" decay
+// from in-chunk differences), so nothing over- or underflows however strong the decay.
 //
-// The inverse is blocked: the four 16x16 diagonal blocks by forward substitution (one lane per
-// column), then T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ with fp32 MFMA, one wave per block column.
+// Phases (one barrier each):
+//   1. stage q, k rows in LDS, row norms, gates and gamma;
+//   2. Gram tiles on MFMA, balanced over the waves: wave w forms the K K^T tiles of row 3 - w and
+//      the K Q^T tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator layout is
+//      exactly the operand layout of P, so P goes from registers straight to the record;
+//   3. A (fp32) into LDS over the staging area;
+//   4. T of the four 16x16 diagonal blocks by forward substitution, one lane per column, all in
+//      registers (wave 0);
+//   5. off-diagonal blocks by the 2x2 block rule T_BA = -T_BB A_BA T_AA, first within each
+//      32-row half (T_10, T_32), then across the halves, on fp32 MFMA;
+//   6. Tb = T diag(beta') gathered into operand order.
 #include "gdr_device.h"
 
 namespace gdr {
@@ -28,11 +37,109 @@ template <typename T>
 struct PrepSmem {
   static constexpr int PK = PrepLayout<T>::PK;
   union {
-    struct { T k[C * PK]; T q[C * PK]; } in;                                   // staging of q, k
-    struct { float a[C * kFP]; float t[C * kFP]; float p[C * kFP]; float sc[4 * C]; } out;
+    struct { T k[C * PK]; T q[C * PK]; } in;   // phases 1-2
+    struct { float a[C * kFP]; float t[C * kFP]; } m;   // phases 3-6
   } u;
   float rk[C], rq[C], gam[C], bet[C];
 };
+
+// fp32 16x16 tile product with the k index of step s, lane group G standing for 4G + s: the A
+// operand is row m of a row-major LDS tile (one 16-byte read per lane), the B operand the
+// accumulator layout of the right factor (element s of lane (n, G) is row 4G + s).
+__device__ __forceinline__ void mma_lds_acc(f4& acc, const float* a_tile, int n16, int G, const f4& b) {
+  const f4 av = *reinterpret_cast<const f4*>(a_tile + n16 * kFP + 4 * G);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], b[s], acc, 0, 0, 0);
+}
+// The right factor in accumulator layout, read from a row-major LDS tile.
+__device__ __forceinline__ f4 tile_acc(const float* tile, int n16, int G) {
+  f4 x;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) x[s] = tile[(4 * G + s) * kFP + n16];
+  return x;
+}
+__device__ __forceinline__ void store_acc(float* tile, int n16, int G, const f4& x) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) tile[(4 * G + s) * kFP + n16] = x[s];
+}
+__device__ __forceinline__ const float* blk(const float* m, int I, int J) { return m + 16 * I * kFP + 16 * J; }
+__device__ __forceinline__ float* blk(float* m, int I, int J) { return m + 16 * I * kFP + 16 * J; }
+
+// Phase 2 of wave W: the Gram tiles, P into the record (and the scalars for wave 0). Kept a
+// template on W so that every tile choice is fixed at compile time.
+template <int W, typename T, int PK>
+__device__ __forceinline__ void gram_phase(const T* ks, const T* qs, const float* gam2, const float* rk,
+                                           const float* rq, int n16, int G, int lane, unsigned char* pbase,
+                                           f4 (&gk)[4]) {
+  constexpr int Ik = 3 - W, Iq = W;
+  f4 gq[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    gk[J] = f4_splat(0.f);
+    gq[J] = f4_splat(0.f);
+  }
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    const Frag<T> ak = lds_frag(ks, PK, 16 * Ik + n16, 32 * kb, G);
+    const Frag<T> bq = lds_frag(qs, PK, 16 * Iq + n16, 32 * kb, G);
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+      if (J > Ik && J > Iq) continue;
+      const Frag<T> kj = lds_frag(ks, PK, 16 * J + n16, 32 * kb, G);
+      if (J <= Ik) mma(gk[J], ak, kj);   // (K K^T)[16 Ik + 4G + e][16 J + n16]
+      if (J <= Iq) mma(gq[J], kj, bq);   // (K Q^T)[16 J + 4G + e][16 Iq + n16] = P^T
+    }
+  }
+  // P[t][i], t = 16 Iq + n16, i = 16 J + 4G + e; each lane writes its eight slots of block (Iq, kb)
+  const int t = 16 * Iq + n16;
+  const float gt = gam2[t], rqt = rq[t];
+  f4 pv[4];
+#pragma unroll
+  for (int J = 0; J < 4; ++J) {
+    pv[J] = f4_splat(0.f);
+    if (J > Iq) continue;
+    const f4 gi = *reinterpret_cast<const f4*>(gam2 + 16 * J + 4 * G);
+    const f4 ri = *reinterpret_cast<const f4*>(rk + 16 * J + 4 * G);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * J + 4 * G + e;
+      const float x = rqt * ri[e] * __builtin_amdgcn_exp2f(fminf(gt - gi[e], 0.f)) * gq[J][e];
+      pv[J][e] = (i <= t) ? x : 0.f;
+    }
+  }
+#pragma unroll
+  for (int kb = 0; kb <= (Iq >> 1); ++kb) {
+    const Frag<T> f = acc_frag<T>(pv[2 * kb], pv[2 * kb + 1], f4_splat(1.f), f4_splat(1.f));
+    unsigned char* dst = pbase + (size_t)frag_block(Iq, kb) * kBlockElems * sizeof(T) + (size_t)lane * 8 * sizeof(T);
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<bf16x8*>(dst) = f.v;
+    } else {
+      *reinterpret_cast<f4*>(dst) = f4{f.v[0], f.v[1], f.v[2], f.v[3]};
+      *reinterpret_cast<f4*>(dst + 16) = f4{f.v[4], f.v[5], f.v[6], f.v[7]};
+    }
+  }
+}
+
+// Phase 3 of wave W: its K K^T tiles (row I = 3 - W) scaled into A.
+template <int W>
+__device__ __forceinline__ void a_phase(float* A, const float* gam2, const float* rk, const float* bet, int n16, int G,
+                                        const f4 (&gk)[4]) {
+  constexpr int I = 3 - W;
+  const f4 gr = *reinterpret_cast<const f4*>(gam2 + 16 * I + 4 * G);
+  const f4 rr = *reinterpret_cast<const f4*>(rk + 16 * I + 4 * G);
+  const f4 br = *reinterpret_cast<const f4*>(bet + 16 * I + 4 * G);
+#pragma unroll
+  for (int J = 0; J <= I; ++J) {
+    const int col = 16 * J + n16;
+    const float gc = gam2[col], rc = rk[col];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = 16 * I + 4 * G + e;
+      const float x = br[e] * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * rr[e] * rc * gk[J][e];
+      A[row * kFP + col] = row > col ? x : 0.f;
+    }
+  }
+}
 
 template <typename T, typename TB>
 __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
@@ -40,195 +147,215 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
   constexpr int PK = PrepSmem<T>::PK;
   constexpr int VN = Vec16<T>::N;     // elements per 16-byte vector
   constexpr int VPR = D / VN;         // vectors per 128-wide row
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NV = (C * VPR) / 256; // 16-byte vectors of q (and of k) per thread
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, G = lane >> 4;
-  const int c = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+  // consecutive logical workgroups: the value heads of one key head, then the key heads, then
+  // the chunks; kept on one XCD so that the q, k rows they share are read once from HBM
   const int r = p.Hv / p.Hk;
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);
+  const int hr = lam % r, kh = (lam / r) % p.Hk, c = (lam / p.Hv) % p.NC, b = lam / (p.Hv * p.NC);
+  const int h = kh * r + hr;
   const int t0 = c * C;
   int len = p.lengths ? p.lengths[b] : p.L;
   len = len < 0 ? 0 : (len > p.L ? p.L : len);
-  const T* qg = reinterpret_cast<const T*>(p.q);
-  const T* kg = reinterpret_cast<const T*>(p.k);
+  constexpr int kMatBytes = kFragBlocks * kBlockElems * (int)sizeof(T);   // Tb (or P) part of a record
+  constexpr int kRecBytes = 2 * kMatBytes + 4 * C * (int)sizeof(float);
+  unsigned char* rec = reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + h) * p.NC + c) * kRecBytes;
+  constexpr float kLog2e = 1.4426950408889634f;
 
-  // ---- stage q, k; squared row norms reduced over the VPR lanes that share a row
+  // ---- 1. stage q, k (range-checked loads: rows past L read as zeros, all issued at once);
+  //         squared row norms over the VPR lanes that share a row; gates and gamma (wave 0)
+  {
+    const uint32_t row_bytes = (uint32_t)p.Hk * D * sizeof(T);
+    const size_t base = (size_t)b * p.L * p.Hk * D;
+    const __amdgpu_buffer_rsrc_t rsk = make_rsrc(reinterpret_cast<const T*>(p.k) + base, (uint32_t)p.L * row_bytes);
+    const __amdgpu_buffer_rsrc_t rsq = make_rsrc(reinterpret_cast<const T*>(p.q) + base, (uint32_t)p.L * row_bytes);
+    uint4 kv[NV], qv[NV];
 #pragma unroll
-  for (int m = 0; m < (C * VPR) / 256; ++m) {
-    const int idx = tid + 256 * m, row = idx / VPR, cv = idx % VPR;
-    const int t = t0 + row;
-    Vec16<T> kv, qv;
-    kv.raw = make_uint4(0, 0, 0, 0);
-    qv.raw = make_uint4(0, 0, 0, 0);
-    if (t < p.L) {
-      const size_t off = ((size_t)b * p.L + t) * p.Hk * D + (size_t)kh * D + cv * VN;
-      kv.raw = *reinterpret_cast<const uint4*>(kg + off);
-      qv.raw = *reinterpret_cast<const uint4*>(qg + off);
+    for (int m = 0; m < NV; ++m) {
+      const int idx = tid + 256 * m, row = idx / VPR, cv = idx % VPR;
+      const uint32_t off = (uint32_t)(t0 + row) * row_bytes + (uint32_t)(kh * D + cv * VN) * sizeof(T);
+      kv[m] = buf_load16(rsk, off);
+      qv[m] = buf_load16(rsq, off);
     }
-    *reinterpret_cast<uint4*>(&sm.u.in.k[row * PK + cv * VN]) = kv.raw;
-    *reinterpret_cast<uint4*>(&sm.u.in.q[row * PK + cv * VN]) = qv.raw;
-    float sk = 0.f, sq = 0.f;
-#pragma unroll
-    for (int e = 0; e < VN; ++e) {
-      const float x = to_f(kv.get(e)), y = to_f(qv.get(e));
-      sk += x * x;
-      sq += y * y;
-    }
-#pragma unroll
-    for (int off = 1; off < VPR; off <<= 1) {
-      sk += __shfl_xor(sk, off);
-      sq += __shfl_xor(sq, off);
-    }
-    if (cv == 0) {
-      sm.rk[row] = 1.0f / sqrtf(sk + 1e-6f);
-      sm.rq[row] = (1.0f / sqrtf(sq + 1e-6f)) * 0.08838834764831845f;   // * 128^-1/2
-    }
-  }
-  __syncthreads();
-
-  // ---- lower-triangle tiles of K K^T and Q K^T (10 each); wave w owns tiles w, w+4, w+8
-  f4 gacc[3], qacc[3];
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    gacc[s] = f4_splat(0.f);
-    qacc[s] = f4_splat(0.f);
-    const int ti = wave + 4 * s;
-    if (ti < kTiles) {
-      const int I = tile_row(ti), J = tile_col(ti);
-#pragma unroll
-      for (int kb = 0; kb < D / 32; ++kb) {
-        const Frag<T> bk = lds_frag(sm.u.in.k, PK, 16 * J + n16, 32 * kb, G);
-        mma(gacc[s], lds_frag(sm.u.in.k, PK, 16 * I + n16, 32 * kb, G), bk);
-        mma(qacc[s], lds_frag(sm.u.in.q, PK, 16 * I + n16, 32 * kb, G), bk);
-      }
-    }
-  }
-  __syncthreads();   // the q/k staging area is reused below
-
-  const TB* betag = reinterpret_cast<const TB*>(p.beta);
-  constexpr int kRecBytes = 2 * kFragBlocks * kBlockElems * sizeof(T) + 4 * C * sizeof(float);
-  constexpr int kMatVecs = kFragBlocks * kBlockElems / VN;   // 16-byte vectors of Tb (and of P)
-
-  for (int hr = 0; hr < r; ++hr) {
-    const int h = kh * r + hr;
-    char* rec = reinterpret_cast<char*>(p.ws) + (((size_t)b * p.Hv + h) * p.NC + c) * kRecBytes;
-
-    // -- guarded gates and inclusive cumulative decay (wave 0, lane = token)
+    float gv = 0.f, bv = 0.f;
     if (wave == 0) {
       const int t = t0 + lane;
-      float gv = 0.f, bv = 0.f;
+      const size_t off = ((size_t)b * p.L + t) * p.Hv + h;
       if (t < len) {
-        const size_t off = ((size_t)b * p.L + t) * p.Hv + h;
         gv = p.g[off];
-        bv = to_f(betag[off]);
+        bv = to_f(reinterpret_cast<const TB*>(p.beta)[off]);
       }
+    }
+#pragma unroll
+    for (int m = 0; m < NV; ++m) {
+      const int idx = tid + 256 * m, row = idx / VPR, cv = idx % VPR;
+      *reinterpret_cast<uint4*>(&sm.u.in.k[row * PK + cv * VN]) = kv[m];
+      *reinterpret_cast<uint4*>(&sm.u.in.q[row * PK + cv * VN]) = qv[m];
+      Vec16<T> kx, qx;
+      kx.raw = kv[m];
+      qx.raw = qv[m];
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) {
+        const float x = to_f(kx.get(e)), y = to_f(qx.get(e));
+        sk += x * x;
+        sq += y * y;
+      }
+#pragma unroll
+      for (int off = 1; off < VPR; off <<= 1) {
+        sk += __shfl_xor(sk, off);
+        sq += __shfl_xor(sq, off);
+      }
+      if (cv == 0) {
+        sm.rk[row] = 1.0f / sqrtf(sk + 1e-6f);
+        sm.rq[row] = (1.0f / sqrtf(sq + 1e-6f)) * 0.08838834764831845f;   // * 128^-1/2
+      }
+    }
+    if (wave == 0) {
       float x = gv;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const float y = __shfl_up(x, off);
         if (lane >= off) x += y;
       }
-      const float gC = __shfl(x, 63);
-      sm.gam[lane] = x;
+      sm.gam[lane] = x * kLog2e;   // gamma in base 2: e^{u - v} = 2^{(u - v) log2 e}
       sm.bet[lane] = bv;
-      const float eg = expf(x);
-      sm.u.out.sc[lane] = eg * sm.rk[lane];
-      sm.u.out.sc[C + lane] = eg * sm.rq[lane];
-      sm.u.out.sc[2 * C + lane] = sm.rk[lane] * expf(gC - x);
-      sm.u.out.sc[3 * C + lane] = (lane == 0) ? expf(gC) : 0.f;
     }
-    __syncthreads();
+  }
+  __syncthreads();
 
-    // -- A (strictly lower, fp32) and P (lower incl. diagonal, tile layout), from the Gram tiles
+  // ---- 2. Gram tiles: K K^T row 3 - wave, K Q^T column wave (P^T), five tiles per wave; P into
+  //         the record straight from the accumulators; the scalars (wave 0)
+  f4 gk[4];
+  {
+    unsigned char* pbase = rec + kMatBytes;
+    switch (wave) {
+      case 0: gram_phase<0, T, PK>(sm.u.in.k, sm.u.in.q, sm.gam, sm.rk, sm.rq, n16, G, lane, pbase, gk); break;
+      case 1: gram_phase<1, T, PK>(sm.u.in.k, sm.u.in.q, sm.gam, sm.rk, sm.rq, n16, G, lane, pbase, gk); break;
+      case 2: gram_phase<2, T, PK>(sm.u.in.k, sm.u.in.q, sm.gam, sm.rk, sm.rq, n16, G, lane, pbase, gk); break;
+      default: gram_phase<3, T, PK>(sm.u.in.k, sm.u.in.q, sm.gam, sm.rk, sm.rq, n16, G, lane, pbase, gk); break;
+    }
+    if (wave == 0) {
+      const float g2 = sm.gam[lane], g2C = sm.gam[C - 1];
+      const float eg = __builtin_amdgcn_exp2f(g2);
+      const float rkl = sm.rk[lane], rql = sm.rq[lane];
+      float* sc = reinterpret_cast<float*>(rec + 2 * kMatBytes);
+      sc[lane] = eg * rkl;
+      sc[C + lane] = eg * rql;
+      sc[2 * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
+      sc[3 * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
+    }
+  }
+  __syncthreads();   // the staging area becomes A and T
+
+  // ---- 3. A, strictly lower, fp32
+  switch (wave) {
+    case 0: a_phase<0>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
+    case 1: a_phase<1>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
+    case 2: a_phase<2>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
+    default: a_phase<3>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
+  }
+  __syncthreads();
+
+  // ---- 4. diagonal blocks: lane 16 w' + j solves column j of block w' (wave 0); the block's
+  //         rows are read into registers first (16-byte reads, broadcast over the block's lanes)
+  if (wave == 0) {
+    const int o = 16 * G, j = n16;
+    f4 arow[16][4];
 #pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int ti = wave + 4 * s;
-      if (ti < kTiles) {
-        const int I = tile_row(ti), J = tile_col(ti);
-        const int col = 16 * J + n16;
-        const float gcol = sm.gam[col], rkcol = sm.rk[col];
+    for (int i = 1; i < 16; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = 16 * I + 4 * G + e;
-          const float dec = expf(row >= col ? sm.gam[row] - gcol : 0.f);
-          sm.u.out.a[row * kFP + col] = (row > col) ? sm.bet[row] * dec * sm.rk[row] * rkcol * gacc[s][e] : 0.f;
-          sm.u.out.p[row * kFP + col] = (row >= col) ? sm.rq[row] * rkcol * dec * qacc[s][e] : 0.f;
-        }
+      for (int s4 = 0; s4 < 4; ++s4)
+        if (4 * s4 < i) arow[i][s4] = *reinterpret_cast<const f4*>(&sm.u.m.a[(o + i) * kFP + o + 4 * s4]);
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+#pragma unroll
+      for (int i = k + 1; i < 16; ++i) x[i] -= arow[i][k >> 2][k & 3] * x[k];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.u.m.t[(o + i) * kFP + o + j] = x[i];
+  }
+  __syncthreads();
+
+  // ---- 5. off-diagonal blocks. Within each 32-row half: T_10 = -T_11 A_10 T_00 (wave 0),
+  //         T_32 = -T_33 A_32 T_22 (wave 1); waves 2, 3 meanwhile form A_20 T_00, A_30 T_00.
+  //         Across the halves (T_IJ for I in {2,3}, J in {0,1}), with Z = A_[23][01] T_[01][01]:
+  //         T_2J = -T_22 Z_2J, T_3J = -(T_32 Z_2J + T_33 Z_3J); wave 2: T_20, wave 3: T_30,
+  //         wave 0: T_21, wave 1: T_31.
+  const float* Am = sm.u.m.a;
+  float* Tm = sm.u.m.t;
+  f4 pre0 = f4_splat(0.f), pre1 = f4_splat(0.f);
+  if (wave < 2) {
+    const int I = 2 * wave + 1, J = 2 * wave;   // (1, 0) or (3, 2)
+    f4 x = f4_splat(0.f);
+    mma_lds_acc(x, blk(Am, I, J), n16, G, tile_acc(blk(Tm, J, J), n16, G));
+    f4 y = f4_splat(0.f);
+    mma_lds_acc(y, blk(Tm, I, I), n16, G, x);
+    store_acc(blk(Tm, I, J), n16, G, -y);
+  } else {
+    const f4 t00 = tile_acc(blk(Tm, 0, 0), n16, G);
+    mma_lds_acc(pre0, blk(Am, 2, 0), n16, G, t00);            // A_20 T_00
+    if (wave == 3) mma_lds_acc(pre1, blk(Am, 3, 0), n16, G, t00);   // A_30 T_00
+  }
+  __syncthreads();
+  {
+    const int J = (wave >= 2) ? 0 : 1;
+    const bool row3 = (wave & 1) != 0;   // waves 1, 3 produce row 3
+    const f4 tj1 = tile_acc(blk(Tm, 1, J), n16, G);   // T_10 (J = 0) or T_11 (J = 1)
+    f4 z2 = pre0;                                      // Z_2J = A_20 T_0J + A_21 T_1J (T_01 = 0)
+    mma_lds_acc(z2, blk(Am, 2, 1), n16, G, tj1);
+    f4 out = f4_splat(0.f);
+    if (!row3) {
+      mma_lds_acc(out, blk(Tm, 2, 2), n16, G, z2);
+      store_acc(blk(Tm, 2, J), n16, G, -out);
+    } else {
+      f4 z3 = pre1;                                    // Z_3J = A_30 T_0J + A_31 T_1J
+      mma_lds_acc(z3, blk(Am, 3, 1), n16, G, tj1);
+      mma_lds_acc(out, blk(Tm, 3, 2), n16, G, z2);
+      mma_lds_acc(out, blk(Tm, 3, 3), n16, G, z3);
+      store_acc(blk(Tm, 3, J), n16, G, -out);
+    }
+  }
+  __syncthreads();
+
+  // ---- 6. Tb = T diag(beta') in operand order (zero above the diagonal): wave w writes blocks
+  //         w and w + 4; lane (m, g) of block (tile I, kb) holds row 16 I + m, columns
+  //         32 kb + 4g + {0..3} and 32 kb + 16 + 4g + {0..3}
+#pragma unroll
+  for (int i2 = 0; i2 < 2; ++i2) {
+    const int bk = wave + 4 * i2;
+    if (bk < kFragBlocks) {
+      const int row = 16 * block_tile(bk) + n16, c0 = 32 * block_kb(bk) + 4 * G;
+      const f4 t_lo = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0]);
+      const f4 t_hi = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0 + 16]);
+      const f4 b_lo = *reinterpret_cast<const f4*>(&sm.bet[c0]);
+      const f4 b_hi = *reinterpret_cast<const f4*>(&sm.bet[c0 + 16]);
+      f4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = (c0 + e <= row) ? t_lo[e] * b_lo[e] : 0.f;
+        hi[e] = (c0 + 16 + e <= row) ? t_hi[e] * b_hi[e] : 0.f;
       }
-    }
-    __syncthreads();
-
-    // -- diagonal blocks by forward substitution (wave w: block w, lane = column)
-    if (lane < 16) {
-      const int o = 16 * wave, kcol = lane;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float s = (i == kcol) ? 1.f : 0.f;
-        const float* arow = &sm.u.out.a[(o + i) * kFP + o];
-#pragma unroll
-        for (int j = 0; j < i; ++j) s -= arow[j] * x[j];
-        x[i] = s;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.u.out.t[(o + i) * kFP + o + kcol] = x[i];
-    }
-    __syncthreads();
-
-    // -- off-diagonal blocks (wave J: block column J)
-    if (wave < 3) {
-      const int J = wave;
-      for (int I = J + 1; I < 4; ++I) {
-        f4 X = f4_splat(0.f);
-        for (int M = J; M < I; ++M) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const float av = sm.u.out.a[(16 * I + n16) * kFP + 16 * M + 4 * G + s];
-            const float bv = sm.u.out.t[(16 * M + 4 * G + s) * kFP + 16 * J + n16];
-            X = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, X, 0, 0, 0);
-          }
-        }
-        f4 Y = f4_splat(0.f);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float av = sm.u.out.t[(16 * I + n16) * kFP + 16 * I + 4 * G + s];
-          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(av, X[s], Y, 0, 0, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) sm.u.out.t[(16 * I + 4 * G + s) * kFP + 16 * J + n16] = -Y[s];
-      }
-    }
-    __syncthreads();
-
-    // -- the record, in 16-byte stores: Tb (formed here) and P in operand order, then scalars
-    for (int v = tid; v < kRecBytes / 16; v += 256) {
-      uint4 out;
-      if (v < 2 * kMatVecs) {
-        const bool is_p = v >= kMatVecs;
-        const int s0 = (v - (is_p ? kMatVecs : 0)) * VN;   // first slot of this vector
-        const int blk = s0 / kBlockElems, ln = (s0 % kBlockElems) / 8;
-        const int row = 16 * block_tile(blk) + (ln & 15), g = ln >> 4, kb = block_kb(blk);
-        Vec16<T> pk;
-#pragma unroll
-        for (int e = 0; e < VN; ++e) {
-          const int col = slot_col(kb, g, (s0 + e) % 8);
-          float x;
-          if (is_p)
-            x = col <= row ? sm.u.out.p[row * kFP + col] : 0.f;
-          else
-            x = col <= row ? sm.u.out.t[row * kFP + col] * sm.bet[col] : 0.f;
-          reinterpret_cast<T*>(&pk.raw)[e] = from_f<T>(x);
-        }
-        out = pk.raw;
+      const Frag<T> f = acc_frag<T>(lo, hi, f4_splat(1.f), f4_splat(1.f));
+      unsigned char* dst = rec + (size_t)bk * kBlockElems * sizeof(T) + (size_t)lane * 8 * sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x8*>(dst) = f.v;
       } else {
-        out = *reinterpret_cast<const uint4*>(&sm.u.out.sc[(v - 2 * kMatVecs) * 4]);
+        *reinterpret_cast<f4*>(dst) = f4{f.v[0], f.v[1], f.v[2], f.v[3]};
+        *reinterpret_cast<f4*>(dst + 16) = f4{f.v[4], f.v[5], f.v[6], f.v[7]};
       }
-      *reinterpret_cast<uint4*>(rec + 16 * (size_t)v) = out;
     }
-    __syncthreads();   // staging is reused by the next value head
   }
 }
 
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s) {
-  dim3 grid(p.NC, p.Hk, p.B);
+  const dim3 grid(p.B * p.Hv * p.NC);
   if (qkv_bf16) {
     if (beta_bf16)
       hipLaunchKernelGGL((gdr_prep<__bf16, __bf16>), grid, dim3(256), 0, s, p);

@@ -122,12 +122,6 @@ __device__ __forceinline__ f4 v_col4(const unsigned char* vt, int t0, int col0, 
   return f4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
 }
 
-// Hardware workgroup i runs on XCD i % 8; number logical workgroups so that consecutive ones
-// (neighbouring heads of one segment, which share key and query rows) stay on one XCD.
-__device__ __forceinline__ int xcd_remap(int id, int n) {
-  return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
-}
-
 __device__ __forceinline__ bool row_is_bad(const ScanParams& p, int b, int& srow) {
   const int len = p.lengths ? p.lengths[b] : p.L;
   srow = p.s0 ? (p.s0_row ? p.s0_row[b] : b) : 0;
