@@ -138,6 +138,11 @@ __device__ __forceinline__ int block_kb(int blk) { return blk < 2 ? 0 : (blk - 2
 // Column (within the 64-token chunk) of slot j of lane group G in token block kb.
 __device__ __forceinline__ int slot_col(int kb, int G, int j) { return 32 * kb + (j < 4 ? 4 * G + j : 12 + 4 * G + j); }
 
+// Workgroup barrier for waves that exchange data through LDS only: waits for this wave's LDS
+// accesses, not for its global loads and stores (which a plain __syncthreads would also drain),
+// and keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Hardware workgroup i runs on XCD i % 8. Logical workgroup lam = xcd_remap(i, n) numbers them so
 // that consecutive logical ids run on one XCD (and share its L2); a bijection on [0, n).
 __device__ __forceinline__ int xcd_remap(int id, int n) {

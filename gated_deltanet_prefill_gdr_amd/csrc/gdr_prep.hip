@@ -13,7 +13,8 @@
 // Exponents are only taken of non-positive differences on the kept triangle ("direct" decay
 // from in-chunk differences), so nothing over- or underflows however strong the decay.
 //
-// Phases (one barrier each):
+// Phases (one barrier each; the waves exchange data through LDS only, so the barriers do not
+// wait for the global stores of the record):
 //   1. stage q, k rows in LDS, row norms, gates and gamma;
 //   2. Gram tiles on MFMA, balanced over the waves: wave w forms the K K^T tiles of row 3 - w and
 //      the K Q^T tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator layout is
@@ -142,7 +143,7 @@ __device__ __forceinline__ void a_phase(float* A, const float* gam2, const float
 }
 
 template <typename T, typename TB>
-__global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
+__global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
   __shared__ __attribute__((aligned(16))) PrepSmem<T> sm;
   constexpr int PK = PrepSmem<T>::PK;
   constexpr int VN = Vec16<T>::N;     // elements per 16-byte vector
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
       sm.bet[lane] = bv;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 2. Gram tiles: K K^T row 3 - wave, K Q^T column wave (P^T), five tiles per wave; P into
   //         the record straight from the accumulators; the scalars (wave 0)
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
       sc[3 * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
     }
   }
-  __syncthreads();   // the staging area becomes A and T
+  lds_barrier();   // the staging area becomes A and T
 
   // ---- 3. A, strictly lower, fp32
   switch (wave) {
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
     case 2: a_phase<2>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
     default: a_phase<3>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 4. diagonal blocks: lane 16 w' + j solves column j of block w' (wave 0); the block's
   //         rows are read into registers first (16-byte reads, broadcast over the block's lanes)
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sm.u.m.t[(o + i) * kFP + o + j] = x[i];
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 5. off-diagonal blocks. Within each 32-row half: T_10 = -T_11 A_10 T_00 (wave 0),
   //         T_32 = -T_33 A_32 T_22 (wave 1); waves 2, 3 meanwhile form A_20 T_00, A_30 T_00.
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
     mma_lds_acc(pre0, blk(Am, 2, 0), n16, G, t00);            // A_20 T_00
     if (wave == 3) mma_lds_acc(pre1, blk(Am, 3, 0), n16, G, t00);   // A_30 T_00
   }
-  __syncthreads();
+  lds_barrier();
   {
     const int J = (wave >= 2) ? 0 : 1;
     const bool row3 = (wave & 1) != 0;   // waves 1, 3 produce row 3
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(256) void gdr_prep(PrepParams p) {
       store_acc(blk(Tm, 3, J), n16, G, -out);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- 6. Tb = T diag(beta') in operand order (zero above the diagonal): wave w writes blocks
   //         w and w + 4; lane (m, g) of block (tile I, kb) holds row 16 I + m, columns
