@@ -59,11 +59,6 @@ __device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row 
 __device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ swz_f(row)); }
 __device__ __forceinline__ int swz_v(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (2 * (row & 7))); }
 
-// Range-checked buffer descriptor as four scalar words, for the loads below.
-__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, kBufferConfig};
-}
 
 // 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
 // range: zeros). Written as inline assembly so that the compiler neither waits for these loads
