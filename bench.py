@@ -6,6 +6,7 @@ bf16 q/k/v, fp32 g/beta/state, zero initial state, final state returned. Inputs,
 the workspace are resident in HBM before the timed region. Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --decode          # one fork decode step instead (gdr_decode, 64 rows x 1 token)
   python bench.py --copy-probe      # a plain device copy of known size, for HBM counter scaling
 """
 from __future__ import annotations
@@ -113,6 +114,55 @@ def copy_probe(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "reps": reps}))
 
 
+def bench_decode(a):
+    """One decode step of the fork workload: every row continues its own state by one token, in
+    place (s_final is s0). Bound by the state read and write; the token rows are tiny."""
+    import torch
+    import gated_deltanet_prefill_gdr_amd as gdr
+    from workloads import draw
+    B, L, Hk, Hv = a.rows, 1, 16, 32
+    x = draw(B, L, Hk, Hv, D, "R1", 4242, torch.bfloat16, s0_rows=B)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v, g, beta, s0 = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta, x.s0))
+    o = torch.empty(B, L, Hv, D, device=dev, dtype=v.dtype)
+
+    def step():
+        gdr.decode(q, k, v, g, beta, s0=s0, out=o, s_final=s0)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdr.timing_enable(True)
+    gdr.timing_read()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern = gdr.timing_read()
+    gdr.timing_enable(False)
+    ms = start.elapsed_time(stop) / a.steps
+    k_ms = kern["gdr_decode"][0] / max(kern["gdr_decode"][1], 1)
+    units, nbytes, _ = algorithmic(B, L, Hk, Hv, 2, B, True)
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": "gated-delta fork decode step tokens·heads/s (64 rows x 1 token, H=32, D=128)",
+        "value": units / (ms * 1e-3), "unit": "tokens·heads/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q/k/v, beta~U(0.2,0.9), g~-U(0.05,3), state 0.1 N(0,1))",
+        "config": {"workload": f"fork decode B={B} L=1 Hk={Hk} Hv={Hv} Dk=Dv=128 bf16 q/k/v, per-row fp32 "
+                               "state continued in place", "B": B, "L": L, "Hk": Hk, "Hv": Hv, "D": D},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "gdr_decode",
+                     "kernel_bytes": nbytes, "kernel_ms": k_ms},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +171,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--rows", type=int, default=64)
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -130,6 +182,9 @@ def main():
     import torch
     if a.copy_probe:
         copy_probe()
+        return
+    if a.decode:
+        bench_decode(a)
         return
     import gated_deltanet_prefill_gdr_amd as gdr
     from workloads import CONFIGS

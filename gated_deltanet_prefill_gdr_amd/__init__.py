@@ -20,13 +20,13 @@ import ctypes
 import os
 
 __all__ = ["prefill", "workspace_size", "check", "last_error", "library", "timing_enable",
-           "timing_read", "kernel_name", "GdrError", "KERNELS", "LIB_PATH"]
+           "timing_read", "kernel_name", "GdrError", "KERNELS", "LIB_PATH", "decode"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
 HEAD_DIM = 128
 GDR_F32, GDR_BF16 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_EUNSUPPORTED", -3: "GDR_EWORKSPACE", -4: "GDR_EHIP"}
-KERNELS = ("gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine")
+KERNELS = ("gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine", "gdr_decode")
 
 
 class GdrError(RuntimeError):
@@ -57,6 +57,8 @@ def library() -> ctypes.CDLL:
     lib.gdr_prefill_check.restype = i32
     lib.gdr_prefill.argtypes = [ctypes.POINTER(Desc)] + [vp] * 11 + [sz, vp]
     lib.gdr_prefill.restype = i32
+    lib.gdr_decode.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10 + [vp]
+    lib.gdr_decode.restype = i32
     lib.gdr_last_error.argtypes = []
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_timing_enable.argtypes = [i32]
@@ -140,13 +142,8 @@ def _lengths_from_valid(valid, B, L, device):
     return lengths.to(device)
 
 
-def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=True, out=None,
-            s_final=None, workspace=None):
-    """Run the chunked gated delta rule on torch's current stream; see the module docstring.
-
-    out / s_final / workspace may be given to reuse buffers (s_final may be s0 itself, for an
-    in-place continuation, when s0_row is None).
-    """
+def _inputs(q, k, v, g, beta, valid, s0, s0_row):
+    """Validate the torch arguments shared by prefill and decode; returns what the call needs."""
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
         raise ValueError("q, k must be [B, L, Hk, D] and v [B, L, Hv, Dv]")
@@ -183,6 +180,18 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=Tr
             s0_row = s0_row.to(dev)
         s0_row = s0_row.contiguous()
     desc = make_desc(B, L, Hk, Hv, n_s0, q.dtype == torch.bfloat16, beta.dtype == torch.bfloat16, Dk, Dv)
+    return desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev
+
+
+def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=True, out=None,
+            s_final=None, workspace=None):
+    """Run the chunked gated delta rule on torch's current stream; see the module docstring.
+
+    out / s_final / workspace may be given to reuse buffers (s_final may be s0 itself, for an
+    in-place continuation, when s0_row is None).
+    """
+    import torch
+    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row)
     need = workspace_size(desc)
     o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
     if want_state and s_final is None:
@@ -196,5 +205,23 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=Tr
         st = library().gdr_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                    _ptr(lengths), _ptr(s0), _ptr(s0_row), _ptr(o), _ptr(s_final),
                                    _ptr(workspace), need, stream)
+    _raise(st)
+    return o, s_final
+
+
+def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=True, out=None, s_final=None):
+    """The same recurrence token by token (gdr_decode): for short sequences over many rows, with
+    the same arguments and results as prefill and no workspace."""
+    import torch
+    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row)
+    o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
+    if want_state and s_final is None:
+        s_final = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
+    if not want_state:
+        s_final = None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = library().gdr_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                  _ptr(lengths), _ptr(s0), _ptr(s0_row), _ptr(o), _ptr(s_final), stream)
     _raise(st)
     return o, s_final

@@ -72,7 +72,7 @@ gdr_status check_desc(const gdr_desc* d) {
 
 gdr_status check_all(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
                      const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
-                     const void* o, const float* s_final, const void* ws, size_t ws_bytes) {
+                     const void* o, const float* s_final, const void* ws, size_t ws_bytes, bool need_ws = true) {
   gdr_status st = check_desc(d);
   if (st != GDR_OK) return st;
   const size_t B = d->B, L = d->L, Hk = d->Hk, Hv = d->Hv, Dd = gdr::kHeadDim;
@@ -96,7 +96,7 @@ gdr_status check_all(const gdr_desc* d, const void* q, const void* k, const void
   if (s_final && s0 && reinterpret_cast<const void*>(s_final) == reinterpret_cast<const void*>(s0) && s0_row)
     return fail(GDR_EINVAL, "s_final may alias s0 only when s0_row is NULL");
 
-  const size_t need = gdr_prefill_workspace_size(d);
+  const size_t need = need_ws ? gdr_prefill_workspace_size(d) : 0;
   if (need > 0) {
     if (!ws) return fail(GDR_EWORKSPACE, "workspace is NULL, %zu bytes needed", need);
     if (ws_bytes < need) return fail(GDR_EWORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
@@ -148,7 +148,8 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine"};
+const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine",
+                                                    "gdr_decode"};
 
 }  // namespace
 
@@ -211,6 +212,33 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
   }
   hipError_t e = timed(GDR_KERNEL_SCAN, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_decode(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                      const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row, void* o,
+                      float* s_final, void* stream) {
+  // same validation as gdr_prefill, with no workspace
+  gdr_status st = check_desc(d);
+  if (st != GDR_OK) return st;
+  st = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, nullptr, 0, /*need_ws=*/false);
+  if (st != GDR_OK) return st;
+  if (d->B == 0) return GDR_OK;
+  if (d->L == 0 && !s_final) return GDR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  gdr::DecodeParams dp{q, k, v, g, beta, lengths, s0, s0_row, o, s_final, d->B, d->L, d->Hk, d->Hv, s0 ? d->n_s0 : 0};
+  TimingRecord rec{GDR_KERNEL_DECODE, nullptr, nullptr};
+  if (g_timing) {
+    rec.start = take_event();
+    rec.stop = take_event();
+    if (rec.start) (void)hipEventRecord(rec.start, s);
+  }
+  hipError_t e = gdr::launch_decode(dp, d->qkv_dtype == GDR_BF16, d->beta_dtype == GDR_BF16, s);
+  if (g_timing && rec.start && rec.stop) {
+    (void)hipEventRecord(rec.stop, s);
+    g_records.push_back(rec);
+  }
+  if (e != hipSuccess) return fail(GDR_EHIP, "decode launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 

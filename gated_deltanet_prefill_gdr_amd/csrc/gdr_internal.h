@@ -1,4 +1,5 @@
-// Internal interface between the C ABI (gdr_api.cpp) and the HIP kernels (gdr_prep.hip, gdr_scan.hip).
+// Internal interface between the C ABI (gdr_api.cpp) and the HIP kernels (gdr_prep.hip,
+// gdr_scan.hip, gdr_decode.hip).
 #ifndef GDR_INTERNAL_H_
 #define GDR_INTERNAL_H_
 
@@ -86,7 +87,22 @@ struct ScanParams {
   int P, Ls;         // segments and chunks per segment
 };
 
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* beta;
+  const int32_t* lengths;
+  const float* s0;
+  const int32_t* s0_row;
+  void* o;
+  float* s_final;
+  int B, L, Hk, Hv, n_s0;
+};
+
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);
 // bf16 with P > 1: segment transitions (all segments but the last), then the combine that
 // turns them into the state entering every segment; launch_scan always runs last.
 hipError_t launch_transition(const ScanParams& p, hipStream_t s);

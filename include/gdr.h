@@ -98,6 +98,17 @@ gdr_status gdr_prefill(const gdr_desc* desc, const void* q, const void* k, const
                        const int32_t* s0_row, void* o, float* s_final, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* The same computation, token by token, for short sequences: decode steps and fork
+ * continuations over many rows (the fork model's fork_delta_rule with h0, h0_idx and an in-place
+ * store, model.py, _fork_linear_layer). Arguments, layouts, pad guard, s0_row gather, in-place
+ * rule and error behaviour are those of gdr_prefill; no workspace is needed. One workgroup per
+ * (row, value head) keeps the 128 x 128 state in registers for all L tokens, so the cost is one
+ * read of s0 and one write of s_final per (row, head) plus the token rows; any L is accepted, but
+ * for long sequences gdr_prefill is far faster. */
+gdr_status gdr_decode(const gdr_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                      const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                      void* o, float* s_final, void* stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdr_last_error(void);
 
@@ -110,7 +121,8 @@ enum {
   GDR_KERNEL_SCAN = 1,        /* state scan writing o (and s_final) */
   GDR_KERNEL_TRANSITION = 2,  /* bf16 long sequences: per-segment state maps */
   GDR_KERNEL_COMBINE = 3,     /* bf16 long sequences: chains the segment maps */
-  GDR_KERNEL_COUNT = 4
+  GDR_KERNEL_DECODE = 4,      /* gdr_decode */
+  GDR_KERNEL_COUNT = 5
 };
 gdr_status gdr_timing_enable(int on);
 gdr_status gdr_timing_read(double* total_ms, int64_t* launches, int n_kernels);

@@ -193,3 +193,31 @@ def test_empty_problems_need_no_pointers():
     for B, L in ((0, 100), (3, 0)):
         d = gdr.make_desc(B, L, 1, 2)
         assert gdr.check(d, [0] * 11, 0) == OK
+
+
+def decode_call(c):
+    lib = gdr.library()
+    return lib.gdr_decode(ctypes.byref(c.desc), *[x or None for x in c.ptrs()[:10]], None)
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda c: c.p.__setitem__("q", 0), EINVAL, "non-NULL"),
+    (lambda c: c.p.__setitem__("v", c.p["v"] + 8), EINVAL, "aligned"),
+    (lambda c: c.p.__setitem__("o", c.p["k"] + 256), EINVAL, "overlaps"),
+    (lambda c: (c.p.__setitem__("s_final", c.p["s0"]), c.p.__setitem__("s0_row", c.p["lengths"] + 4096)),
+     EINVAL, "alias"),
+    (lambda c: setattr(c.desc, "Dk", 64), EUNSUP, "Dk"),
+])
+def test_decode_rejects_invalid_arguments_on_host(mutate, status, msg):
+    """gdr_decode runs gdr_prefill's host validation (minus the workspace) before any launch."""
+    c = Call()
+    mutate(c)
+    assert decode_call(c) == status
+    assert msg in gdr.last_error()
+
+
+def test_decode_empty_problems_need_no_pointers():
+    lib = gdr.library()
+    for B, L in ((0, 5), (3, 0)):
+        d = gdr.make_desc(B, L, 1, 2)
+        assert lib.gdr_decode(ctypes.byref(d), *[None] * 10, None) == OK
