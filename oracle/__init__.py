@@ -7,6 +7,10 @@ package. Only the tests, the smoke check in ``__graft_entry__`` and the CPU-base
 * ``recurrence.gated_delta_rule``: the definition, a token-by-token float64 recurrence, as
   the kernel-test page (``r15_kernel_test.py``, function ``truth_f64``) and the model page
   (``model.py``, function ``delta_rule_reference``) state it.
+* ``layer``: the layer steps on either side of the delta rule (gate prologue, causal depthwise
+  conv + SiLU with tail continuation, gated RMSNorm), from the model page ``model.py``
+  (functions ``_dn_gates``, ``_conv_silu``, ``_gated_rms``); pinned in
+  ``tests/test_oracle_layer.py``.
 * ``chunked.gated_delta_rule_chunked``: a second float64 formulation that evaluates the same
   recurrence C tokens at a time with an explicit matrix inverse. It exists only to pin the
   chunk algebra against the recurrence on tiny shapes.
@@ -16,5 +20,7 @@ Every function here is pinned by the ``-m "not gpu"`` tests in ``tests/test_orac
 """
 from .recurrence import gated_delta_rule, l2norm, guard
 from .chunked import gated_delta_rule_chunked
+from .layer import dn_gates, conv_silu, gated_rmsnorm
 
-__all__ = ["gated_delta_rule", "gated_delta_rule_chunked", "l2norm", "guard"]
+__all__ = ["gated_delta_rule", "gated_delta_rule_chunked", "l2norm", "guard", "dn_gates", "conv_silu",
+           "gated_rmsnorm"]
