@@ -7,6 +7,7 @@ the workspace are resident in HBM before the timed region. Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --decode          # one fork decode step instead (gdr_decode, 64 rows x 1 token)
+  python bench.py --layer           # the layer steps around it (gates, conv + SiLU, gated RMSNorm)
   python bench.py --copy-probe      # a plain device copy of known size, for HBM counter scaling
 """
 from __future__ import annotations
@@ -163,6 +164,73 @@ def bench_decode(a):
     print(json.dumps(line), flush=True)
 
 
+def layer_bytes(B, L, Hk, Hv, K, esz):
+    """Algorithmic bytes of one launch of each layer step (read inputs once, write outputs once)."""
+    tok, Cm = B * L, (2 * Hk + Hv) * D
+    return {
+        "gdr_gates": tok * Hv * (2 * esz + esz + 4) + 2 * Hv * 4 + B * 4,
+        "gdr_conv_silu": 2 * tok * Cm * esz + 2 * B * (K - 1) * Cm * esz + Cm * K * 4,
+        "gdr_gated_rmsnorm": 3 * tok * Hv * D * esz + D * 4,
+    }
+
+
+def bench_layer(a):
+    """The layer steps at the long-prefill shape (B = 1, L = 16384, 16 key / 32 value heads, K = 4,
+    bf16): one step = gates + conv + SiLU (with the tail carried) + gated RMSNorm, each its own launch."""
+    import torch
+    import gated_deltanet_prefill_gdr_amd as gdr
+    from workloads import draw_layer
+    B, L, Hk, Hv, K = 1, 16384, 16, 32, 4
+    x = draw_layer(B, L, Hk, Hv, K, 5151, torch.bfloat16)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    t = {n: getattr(x, n).to(dev) for n in ("b_raw", "a_raw", "A_log", "dt_bias", "mixed", "tail", "conv_w", "x",
+                                             "z", "norm_w")}
+    beta = torch.empty(B, L, Hv, device=dev, dtype=torch.bfloat16)
+    g = torch.empty(B, L, Hv, device=dev, dtype=torch.float32)
+    q = torch.empty(B, L, Hk, D, device=dev, dtype=torch.bfloat16)
+    k, v = torch.empty_like(q), torch.empty(B, L, Hv, D, device=dev, dtype=torch.bfloat16)
+    new_tail, y = torch.empty_like(t["tail"]), torch.empty_like(t["x"])
+
+    def step():
+        gdr.gates(t["b_raw"], t["a_raw"], t["A_log"], t["dt_bias"], beta_out=beta, g_out=g)
+        gdr.conv_silu(t["mixed"], t["conv_w"], Hk, Hv, t["tail"], out=(q, k, v), new_tail=new_tail)
+        gdr.gated_rmsnorm(t["x"], t["z"], t["norm_w"], 1e-6, out=y)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    gdr.timing_enable(True)
+    gdr.timing_read()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    kern = {n: (ms / c, c) for n, (ms, c) in gdr.timing_read().items() if c > 0}
+    gdr.timing_enable(False)
+    ms = start.elapsed_time(stop) / a.steps
+    nb = layer_bytes(B, L, Hk, Hv, K, 2)
+    per = {n: {"ms": kern[n][0], "bytes": nb[n], "GB/s": nb[n] / (kern[n][0] * 1e-3) / 1e9,
+               "frac": nb[n] / (kern[n][0] * 1e-3) / 1e9 / HBM_PEAK_GBS} for n in nb}
+    dom = max(per, key=lambda n: per[n]["ms"])
+    line = {
+        "metric": "gated-delta layer steps (gates, conv + SiLU, gated RMSNorm) tokens·heads/s at L=16384, H=32",
+        "value": B * L * Hv / (ms * 1e-3), "unit": "tokens·heads/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) projections, mixed, z; U(-1,1)/2 conv taps)",
+        "config": {"workload": "layer steps B=1 L=16384 Hk=16 Hv=32 D=128 K=4 bf16", "B": B, "L": L, "Hk": Hk,
+                   "Hv": Hv, "K": K},
+        "roofline": {"bound": "hbm", "achieved": per[dom]["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": per[dom]["frac"], "traffic": None, "kernel": dom, "kernel_bytes": nb[dom],
+                     "kernel_ms": per[dom]["ms"]},
+        "kernels": per,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -173,6 +241,7 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--rows", type=int, default=64)
+    ap.add_argument("--layer", action="store_true")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -185,6 +254,9 @@ def main():
         return
     if a.decode:
         bench_decode(a)
+        return
+    if a.layer:
+        bench_layer(a)
         return
     import gated_deltanet_prefill_gdr_amd as gdr
     from workloads import CONFIGS

@@ -20,13 +20,15 @@ import ctypes
 import os
 
 __all__ = ["prefill", "workspace_size", "check", "last_error", "library", "timing_enable",
-           "timing_read", "kernel_name", "GdrError", "KERNELS", "LIB_PATH", "decode"]
+           "timing_read", "kernel_name", "GdrError", "KERNELS", "LIB_PATH", "decode", "gates", "conv_silu",
+           "gated_rmsnorm"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr.so")
 HEAD_DIM = 128
 GDR_F32, GDR_BF16 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_EUNSUPPORTED", -3: "GDR_EWORKSPACE", -4: "GDR_EHIP"}
-KERNELS = ("gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine", "gdr_decode")
+KERNELS = ("gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine", "gdr_decode", "gdr_gates", "gdr_conv_silu",
+           "gdr_gated_rmsnorm")
 
 
 class GdrError(RuntimeError):
@@ -59,6 +61,13 @@ def library() -> ctypes.CDLL:
     lib.gdr_prefill.restype = i32
     lib.gdr_decode.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10 + [vp]
     lib.gdr_decode.restype = i32
+    i64, f32 = ctypes.c_int64, ctypes.c_float
+    lib.gdr_gates.argtypes = [i32, i32, i32, i32] + [vp] * 7 + [vp]
+    lib.gdr_gates.restype = i32
+    lib.gdr_conv_silu.argtypes = [i32, i32, i32, i32, i32, i32] + [vp] * 8 + [vp]
+    lib.gdr_conv_silu.restype = i32
+    lib.gdr_gated_rmsnorm.argtypes = [i64, i32, vp, vp, vp, f32, vp, vp]
+    lib.gdr_gated_rmsnorm.restype = i32
     lib.gdr_last_error.argtypes = []
     lib.gdr_last_error.restype = ctypes.c_char_p
     lib.gdr_timing_enable.argtypes = [i32]
@@ -225,3 +234,109 @@ def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=Tru
                                   _ptr(lengths), _ptr(s0), _ptr(s0_row), _ptr(o), _ptr(s_final), stream)
     _raise(st)
     return o, s_final
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise ValueError("tensors must be float32 or bfloat16")
+
+
+def _on(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+
+
+def gates(b, a, A_log, dt_bias, valid=None, *, beta_out=None, g_out=None):
+    """Gate prologue (gdr_gates): beta = sigmoid(b) [valid], g = -exp(A_log) softplus(a + dt_bias) [valid].
+
+    b, a [B, L, Hv] float32 or bfloat16 (same dtype); A_log, dt_bias [Hv] float32. Returns
+    beta [B, L, Hv] in b's dtype and g [B, L, Hv] float32."""
+    import torch
+    if b.dim() != 3 or a.shape != b.shape or a.dtype != b.dtype:
+        raise ValueError("b and a must be [B, L, Hv] of one dtype")
+    B, L, Hv = b.shape
+    dev = b.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    code = _dtype_code(b)
+    if A_log.shape != (Hv,) or dt_bias.shape != (Hv,) or A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+        raise ValueError(f"A_log and dt_bias must be float32 [{Hv}]")
+    _on(dev, b=b, a=a, A_log=A_log, dt_bias=dt_bias)
+    lengths = _lengths_from_valid(valid, B, L, dev)
+    beta = beta_out if beta_out is not None else torch.empty_like(b)
+    g = g_out if g_out is not None else torch.empty(B, L, Hv, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = library().gdr_gates(B, L, Hv, code, _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias), _ptr(lengths),
+                                 _ptr(beta), _ptr(g), stream)
+    _raise(st)
+    return beta, g
+
+
+def conv_silu(mixed, w, Hk, Hv, tail=None, valid=None, *, want_tail=True, new_tail=None, out=None):
+    """Causal depthwise conv + SiLU with tail continuation and the q/k/v split (gdr_conv_silu).
+
+    mixed [B, L, (2 Hk + Hv) 128] float32 or bfloat16; w [Cm, K] float32; tail [B, K-1, Cm] in
+    mixed's dtype or None (zeros). Returns q [B, L, Hk, 128], k [B, L, Hk, 128], v [B, L, Hv, 128]
+    and new_tail [B, K-1, Cm] (None if not wanted; pass new_tail=tail to update it in place)."""
+    import torch
+    if mixed.dim() != 3:
+        raise ValueError("mixed must be [B, L, Cm]")
+    B, L, Cm = mixed.shape
+    if Cm != (2 * Hk + Hv) * HEAD_DIM:
+        raise ValueError(f"mixed has {Cm} channels, (2 Hk + Hv) * 128 = {(2 * Hk + Hv) * HEAD_DIM} expected")
+    dev = mixed.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    code = _dtype_code(mixed)
+    if w.dim() != 2 or w.shape[0] != Cm or w.dtype != torch.float32:
+        raise ValueError(f"w must be float32 [{Cm}, K]")
+    K = w.shape[1]
+    if tail is not None and (tail.shape != (B, K - 1, Cm) or tail.dtype != mixed.dtype):
+        raise ValueError(f"tail must be [{B}, {K - 1}, {Cm}] in mixed's dtype")
+    _on(dev, mixed=mixed, w=w, tail=tail, new_tail=new_tail)
+    lengths = _lengths_from_valid(valid, B, L, dev)
+    if out is None:
+        q = torch.empty(B, L, Hk, HEAD_DIM, device=dev, dtype=mixed.dtype)
+        k = torch.empty_like(q)
+        v = torch.empty(B, L, Hv, HEAD_DIM, device=dev, dtype=mixed.dtype)
+    else:
+        q, k, v = out
+    if want_tail and new_tail is None:
+        new_tail = torch.empty(B, K - 1, Cm, device=dev, dtype=mixed.dtype)
+    if not want_tail:
+        new_tail = None
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = library().gdr_conv_silu(B, L, Hk, Hv, K, code, _ptr(mixed), _ptr(tail), _ptr(w), _ptr(lengths),
+                                     _ptr(q), _ptr(k), _ptr(v), _ptr(new_tail), stream)
+    _raise(st)
+    return q, k, v, new_tail
+
+
+def gated_rmsnorm(x, z, w, eps, *, out=None):
+    """Gated RMSNorm over the last axis (128): w x / sqrt(mean(x^2) + eps) silu(z) (gdr_gated_rmsnorm).
+
+    x, z [..., 128] of one dtype (float32 or bfloat16); w [128] float32. out may be x (in place)."""
+    import torch
+    if x.shape != z.shape or x.dtype != z.dtype or x.shape[-1] != HEAD_DIM:
+        raise ValueError("x and z must share shape [..., 128] and dtype")
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    code = _dtype_code(x)
+    if w.shape != (HEAD_DIM,) or w.dtype != torch.float32:
+        raise ValueError("w must be float32 [128]")
+    _on(dev, x=x, z=z, w=w, out=out)
+    y = out if out is not None else torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = library().gdr_gated_rmsnorm(x.numel() // HEAD_DIM, code, _ptr(x), _ptr(z), _ptr(w), float(eps), _ptr(y),
+                                         stream)
+    _raise(st)
+    return y

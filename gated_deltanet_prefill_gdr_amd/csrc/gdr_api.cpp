@@ -148,8 +148,43 @@ hipEvent_t take_event() {
   return e;
 }
 
-const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine",
-                                                    "gdr_decode"};
+// Launch through `launch` (returns hipError_t), bracketed by timing events when timing is on.
+template <typename F>
+hipError_t timed(int kernel, hipStream_t s, F&& launch) {
+  TimingRecord rec{kernel, nullptr, nullptr};
+  if (g_timing) {
+    rec.start = take_event();
+    rec.stop = take_event();
+    if (rec.start) (void)hipEventRecord(rec.start, s);
+  }
+  hipError_t e = launch();
+  if (g_timing && rec.start && rec.stop) {
+    (void)hipEventRecord(rec.stop, s);
+    g_records.push_back(rec);
+  }
+  return e;
+}
+
+const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep",  "gdr_scan",      "gdr_transition",   "gdr_combine",
+                                                    "gdr_decode", "gdr_gates", "gdr_conv_silu", "gdr_gated_rmsnorm"};
+
+bool bad_dtype(int dt) { return dt != GDR_F32 && dt != GDR_BF16; }
+
+gdr_status check_overlaps(const Range* ins, size_t n_in, const Range* outs, size_t n_out,
+                          const char* inplace_out = nullptr, const char* inplace_in = nullptr) {
+  for (size_t o = 0; o < n_out; ++o) {
+    for (size_t i = 0; i < n_in; ++i) {
+      if (!overlap(outs[o], ins[i])) continue;
+      if (inplace_out && std::strcmp(outs[o].name, inplace_out) == 0 && std::strcmp(ins[i].name, inplace_in) == 0 &&
+          outs[o].lo == ins[i].lo)
+        continue;
+      return fail(GDR_EINVAL, "%s overlaps %s", outs[o].name, ins[i].name);
+    }
+    for (size_t j = o + 1; j < n_out; ++j)
+      if (overlap(outs[o], outs[j])) return fail(GDR_EINVAL, "%s overlaps %s", outs[o].name, outs[j].name);
+  }
+  return GDR_OK;
+}
 
 }  // namespace
 
@@ -178,24 +213,9 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
   const int NC = num_chunks(d->L);
   const int bf16 = d->qkv_dtype == GDR_BF16;
 
-  auto timed = [&](int kernel, auto&& launch) -> hipError_t {
-    TimingRecord rec{kernel, nullptr, nullptr};
-    if (g_timing) {
-      rec.start = take_event();
-      rec.stop = take_event();
-      if (rec.start) (void)hipEventRecord(rec.start, s);
-    }
-    hipError_t e = launch();
-    if (g_timing && rec.start && rec.stop) {
-      (void)hipEventRecord(rec.stop, s);
-      g_records.push_back(rec);
-    }
-    return e;
-  };
-
   if (NC > 0) {
     gdr::PrepParams pp{q, k, g, beta, lengths, ws, d->B, d->L, d->Hk, d->Hv, NC};
-    hipError_t e = timed(GDR_KERNEL_PREP, [&] { return gdr::launch_prep(pp, bf16, d->beta_dtype == GDR_BF16, s); });
+    hipError_t e = timed(GDR_KERNEL_PREP, s, [&] { return gdr::launch_prep(pp, bf16, d->beta_dtype == GDR_BF16, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "prep launch: %s", hipGetErrorString(e));
   }
   const gdr::SegPlan plan = gdr::seg_plan(d->B, d->Hv, NC, bf16);
@@ -205,12 +225,12 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
   gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final, NC > 0 ? ws : nullptr, seg,
                      d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0, plan.P, plan.Ls};
   if (plan.P > 1) {
-    hipError_t e = timed(GDR_KERNEL_TRANSITION, [&] { return gdr::launch_transition(sp, s); });
+    hipError_t e = timed(GDR_KERNEL_TRANSITION, s, [&] { return gdr::launch_transition(sp, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "transition launch: %s", hipGetErrorString(e));
-    e = timed(GDR_KERNEL_COMBINE, [&] { return gdr::launch_combine(sp, s); });
+    e = timed(GDR_KERNEL_COMBINE, s, [&] { return gdr::launch_combine(sp, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "combine launch: %s", hipGetErrorString(e));
   }
-  hipError_t e = timed(GDR_KERNEL_SCAN, [&] { return gdr::launch_scan(sp, bf16, s); });
+  hipError_t e = timed(GDR_KERNEL_SCAN, s, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }
@@ -227,18 +247,92 @@ gdr_status gdr_decode(const gdr_desc* d, const void* q, const void* k, const voi
   if (d->L == 0 && !s_final) return GDR_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   gdr::DecodeParams dp{q, k, v, g, beta, lengths, s0, s0_row, o, s_final, d->B, d->L, d->Hk, d->Hv, s0 ? d->n_s0 : 0};
-  TimingRecord rec{GDR_KERNEL_DECODE, nullptr, nullptr};
-  if (g_timing) {
-    rec.start = take_event();
-    rec.stop = take_event();
-    if (rec.start) (void)hipEventRecord(rec.start, s);
-  }
-  hipError_t e = gdr::launch_decode(dp, d->qkv_dtype == GDR_BF16, d->beta_dtype == GDR_BF16, s);
-  if (g_timing && rec.start && rec.stop) {
-    (void)hipEventRecord(rec.stop, s);
-    g_records.push_back(rec);
-  }
+  hipError_t e = timed(GDR_KERNEL_DECODE, s, [&] {
+    return gdr::launch_decode(dp, d->qkv_dtype == GDR_BF16, d->beta_dtype == GDR_BF16, s);
+  });
   if (e != hipSuccess) return fail(GDR_EHIP, "decode launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_gates(int32_t B, int32_t L, int32_t Hv, gdr_dtype ab_dtype, const void* b, const void* a,
+                     const float* A_log, const float* dt_bias, const int32_t* lengths, void* beta, float* g,
+                     void* stream) {
+  if (B < 0 || L < 0 || Hv <= 0) return fail(GDR_EINVAL, "gates: B (%d), L (%d) >= 0 and Hv (%d) > 0 required", B, L, Hv);
+  if (bad_dtype(ab_dtype)) return fail(GDR_EINVAL, "gates: ab_dtype %d is not a gdr_dtype", ab_dtype);
+  const size_t n = size_t(B) * L * Hv, esz = dtype_size(ab_dtype);
+  if (n == 0) return GDR_OK;
+  if (!b || !a || !A_log || !dt_bias || !beta || !g) return fail(GDR_EINVAL, "gates: b, a, A_log, dt_bias, beta and g must be non-NULL");
+  if (!aligned(b, esz) || !aligned(a, esz) || !aligned(beta, esz) || !aligned(g, 4) || !aligned(A_log, 4) ||
+      !aligned(dt_bias, 4) || (lengths && !aligned(lengths, 4)))
+    return fail(GDR_EINVAL, "gates: pointers must be element-aligned");
+  const Range ins[] = {range("b", b, n * esz), range("a", a, n * esz), range("A_log", A_log, Hv * 4u),
+                       range("dt_bias", dt_bias, Hv * 4u), range("lengths", lengths, lengths ? B * 4u : 0)};
+  const Range outs[] = {range("beta", beta, n * esz), range("g", g, n * 4)};
+  gdr_status st = check_overlaps(ins, 5, outs, 2);
+  if (st != GDR_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  gdr::GatesParams p{b, a, A_log, dt_bias, lengths, beta, g, B, L, Hv};
+  hipError_t e = timed(GDR_KERNEL_GATES, s, [&] { return gdr::launch_gates(p, ab_dtype == GDR_BF16, s); });
+  if (e != hipSuccess) return fail(GDR_EHIP, "gates launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_conv_silu(int32_t B, int32_t L, int32_t Hk, int32_t Hv, int32_t K, gdr_dtype dtype, const void* mixed,
+                         const void* tail, const float* w, const int32_t* lengths, void* q, void* k, void* v,
+                         void* new_tail, void* stream) {
+  if (B < 0 || L < 0 || Hk <= 0 || Hv <= 0)
+    return fail(GDR_EINVAL, "conv_silu: B (%d), L (%d) >= 0 and Hk (%d), Hv (%d) > 0 required", B, L, Hk, Hv);
+  if (K < 1 || K > gdr::kMaxConvTaps) return fail(GDR_EUNSUPPORTED, "conv_silu: K = %d, 1 <= K <= %d is built", K, gdr::kMaxConvTaps);
+  if (bad_dtype(dtype)) return fail(GDR_EINVAL, "conv_silu: dtype %d is not a gdr_dtype", dtype);
+  const size_t Dd = gdr::kHeadDim, esz = dtype_size(dtype);
+  const size_t Cm = (2 * size_t(Hk) + Hv) * Dd;
+  if (B > 65535 || (int64_t(L) + 63) / 64 > 65535 || Cm > (size_t(1) << 24))
+    return fail(GDR_EUNSUPPORTED, "conv_silu: B <= 65535, ceil(L/64) <= 65535 and (2 Hk + Hv) 128 <= 2^24 required (grid limits)");
+  if ((int64_t(L) + 64) * int64_t(Cm) * int64_t(esz) >= (int64_t(1) << 32))
+    return fail(GDR_EUNSUPPORTED, "conv_silu: (L + 64) * (2 Hk + Hv) * 128 elements must stay below 4 GiB per batch row");
+  const size_t K1 = size_t(K) - 1;
+  const bool work = size_t(B) * L > 0 || (new_tail && B > 0 && K1 > 0);
+  if (!work) return GDR_OK;
+  if (!w) return fail(GDR_EINVAL, "conv_silu: w must be non-NULL");
+  if (size_t(B) * L > 0 && (!mixed || !q || !k || !v)) return fail(GDR_EINVAL, "conv_silu: mixed, q, k and v must be non-NULL");
+  if (!aligned(mixed, 16) || !aligned(tail, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(new_tail, 16) || !aligned(w, 4) || (lengths && !aligned(lengths, 4)))
+    return fail(GDR_EINVAL, "conv_silu: mixed, tail, q, k, v and new_tail must be 16-byte aligned");
+  const size_t tok = size_t(B) * L;
+  const Range ins[] = {range("mixed", mixed, tok * Cm * esz), range("tail", tail, tail ? B * K1 * Cm * esz : 0),
+                       range("w", w, Cm * K * 4), range("lengths", lengths, lengths ? B * 4u : 0)};
+  const Range outs[] = {range("q", q, tok * Hk * Dd * esz), range("k", k, tok * Hk * Dd * esz),
+                        range("v", v, tok * Hv * Dd * esz), range("new_tail", new_tail, new_tail ? B * K1 * Cm * esz : 0)};
+  gdr_status st = check_overlaps(ins, 4, outs, 4, "new_tail", "tail");
+  if (st != GDR_OK) return st;
+  if (B == 0) return GDR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  gdr::ConvParams p{mixed, tail, w, lengths, q, k, v, new_tail, B, L, Hk, Hv, K};
+  // L = 0 with a tail to carry: one tile still runs (its stores fall past L and are dropped)
+  hipError_t e = timed(GDR_KERNEL_CONV, s, [&] { return gdr::launch_conv_silu(p, dtype == GDR_BF16, s); });
+  if (e != hipSuccess) return fail(GDR_EHIP, "conv_silu launch: %s", hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status gdr_gated_rmsnorm(int64_t rows, gdr_dtype dtype, const void* x, const void* z, const float* w, float eps,
+                             void* out, void* stream) {
+  if (rows < 0) return fail(GDR_EINVAL, "gated_rmsnorm: rows (%lld) must be >= 0", (long long)rows);
+  if (bad_dtype(dtype)) return fail(GDR_EINVAL, "gated_rmsnorm: dtype %d is not a gdr_dtype", dtype);
+  if (!(eps >= 0.f) || eps > 1e30f) return fail(GDR_EINVAL, "gated_rmsnorm: eps must be finite and >= 0");
+  if (rows > (int64_t(1) << 35)) return fail(GDR_EUNSUPPORTED, "gated_rmsnorm: rows must stay below 2^35");
+  if (rows == 0) return GDR_OK;
+  if (!x || !z || !w || !out) return fail(GDR_EINVAL, "gated_rmsnorm: x, z, w and out must be non-NULL");
+  if (!aligned(x, 16) || !aligned(z, 16) || !aligned(out, 16) || !aligned(w, 4))
+    return fail(GDR_EINVAL, "gated_rmsnorm: x, z and out must be 16-byte aligned");
+  const size_t bytes = size_t(rows) * gdr::kHeadDim * dtype_size(dtype);
+  const Range ins[] = {range("x", x, bytes), range("z", z, bytes), range("w", w, gdr::kHeadDim * 4)};
+  const Range outs[] = {range("out", out, bytes)};
+  gdr_status st = check_overlaps(ins, 3, outs, 1, "out", "x");
+  if (st != GDR_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  gdr::NormParams p{x, z, w, eps, out, rows};
+  hipError_t e = timed(GDR_KERNEL_NORM, s, [&] { return gdr::launch_gated_rmsnorm(p, dtype == GDR_BF16, s); });
+  if (e != hipSuccess) return fail(GDR_EHIP, "gated_rmsnorm launch: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 

@@ -112,6 +112,7 @@ __device__ __forceinline__ Frag<float> acc_frag<float>(const f4& t0, const f4& t
 
 // Raw buffer access with hardware range checking: loads past `bytes` return zeros and stores
 // past it are dropped, so bounds need no branches. Offsets are 32-bit byte offsets from `base`.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferConfig = 0x00020000;   // descriptor word 3 for the gfx9 family
 

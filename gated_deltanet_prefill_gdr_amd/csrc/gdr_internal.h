@@ -1,5 +1,5 @@
 // Internal interface between the C ABI (gdr_api.cpp) and the HIP kernels (gdr_prep.hip,
-// gdr_scan.hip, gdr_decode.hip).
+// gdr_scan.hip, gdr_decode.hip, gdr_layer.hip).
 #ifndef GDR_INTERNAL_H_
 #define GDR_INTERNAL_H_
 
@@ -100,6 +100,45 @@ struct DecodeParams {
   float* s_final;
   int B, L, Hk, Hv, n_s0;
 };
+
+// Layer steps around the delta rule (gdr_layer.hip).
+struct GatesParams {
+  const void* b;          // [B, L, Hv] raw beta projection
+  const void* a;          // [B, L, Hv] raw decay projection
+  const float* A_log;     // [Hv]
+  const float* dt_bias;   // [Hv]
+  const int32_t* lengths;
+  void* beta;             // [B, L, Hv], dtype of b
+  float* g;               // [B, L, Hv]
+  int B, L, Hv;
+};
+
+struct ConvParams {
+  const void* mixed;      // [B, L, Cm], Cm = (2 Hk + Hv) 128
+  const void* tail;       // [B, K-1, Cm] or null (zeros)
+  const float* w;         // [Cm, K]
+  const int32_t* lengths;
+  void* q;                // [B, L, Hk, 128]
+  void* k;                // [B, L, Hk, 128]
+  void* v;                // [B, L, Hv, 128]
+  void* new_tail;         // [B, K-1, Cm] or null; may be tail itself
+  int B, L, Hk, Hv, K;
+};
+
+struct NormParams {
+  const void* x;          // [rows, 128]
+  const void* z;          // [rows, 128]
+  const float* w;         // [128]
+  float eps;
+  void* out;              // [rows, 128]; may be x itself
+  int64_t rows;
+};
+
+constexpr int kMaxConvTaps = 8;
+
+hipError_t launch_gates(const GatesParams& p, int bf16, hipStream_t s);
+hipError_t launch_conv_silu(const ConvParams& p, int bf16, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const NormParams& p, int bf16, hipStream_t s);
 
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);

@@ -22,7 +22,7 @@
 namespace gdr {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kSlices16 = D / 16;   // 16-column slices of a head
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 

@@ -109,6 +109,45 @@ gdr_status gdr_decode(const gdr_desc* desc, const void* q, const void* k, const 
                       const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
                       void* o, float* s_final, void* stream);
 
+/* ---- Layer steps on either side of the delta rule (model page, model.py, _linear_layer and
+ * _fork_linear_layer). Same conventions as above: device pointers the caller owns, asynchronous
+ * on `stream`, every host-checkable argument validated before any launch (a non-OK status
+ * means nothing was launched), a row whose device-side length is outside [0, L] gets NaN
+ * outputs. Head dimension 128. */
+
+/* Gate prologue (model.py, _dn_gates): per (row b, token t, value head h)
+ *   beta[b,t,h] = sigmoid(b_raw[b,t,h]) * [t < len_b]
+ *   g[b,t,h]    = -exp(A_log[h]) * softplus(a_raw[b,t,h] + dt_bias[h]) * [t < len_b]
+ * b_raw, a_raw [B, L, Hv] in ab_dtype (the raw projections); A_log, dt_bias [Hv] float32;
+ * lengths [B] int32 or NULL; outputs beta [B, L, Hv] in ab_dtype and g [B, L, Hv] float32,
+ * ready for gdr_prefill / gdr_decode (pads are exact no-ops). Computed in float32, each output
+ * rounded once. Outputs must not overlap inputs. */
+gdr_status gdr_gates(int32_t B, int32_t L, int32_t Hv, gdr_dtype ab_dtype, const void* b_raw, const void* a_raw,
+                     const float* A_log, const float* dt_bias, const int32_t* lengths, void* beta, float* g,
+                     void* stream);
+
+/* Causal depthwise convolution + SiLU with conv-tail continuation and the q/k/v split
+ * (model.py, _conv_silu, and the tail gather of _linear_layer). With Cm = (2 Hk + Hv) * 128
+ * channels and ext = [tail ; mixed] along time (K-1 + L rows):
+ *   pre[b,t,c] = sum_{j=0}^{K-1} ext[b, t+j, c] * w[c, j],   out = silu(pre)
+ *   q = out[..., 0:Hk*128] -> [B, L, Hk, 128], k = the next Hk*128 channels, v = the last Hv*128
+ *   new_tail[b, j] = ext[b, len_b + j], j = 0 .. K-2   (the last K-1 inputs up to the row's length)
+ * mixed [B, L, Cm] and tail [B, K-1, Cm] (NULL = zeros) in dtype; w [Cm, K] float32 (the
+ * depthwise filter, one row per channel; the last tap multiplies the current token);
+ * lengths [B] int32 or NULL; q, k, v in dtype, the layouts gdr_prefill reads; new_tail
+ * [B, K-1, Cm] in dtype or NULL (not wanted). new_tail may be tail itself (in-place tail
+ * update); no other output may overlap an input. 1 <= K <= 8. Computed in float32. */
+gdr_status gdr_conv_silu(int32_t B, int32_t L, int32_t Hk, int32_t Hv, int32_t K, gdr_dtype dtype, const void* mixed,
+                         const void* tail, const float* w, const int32_t* lengths, void* q, void* k, void* v,
+                         void* new_tail, void* stream);
+
+/* Gated RMSNorm over 128-wide rows (model.py, _gated_rms):
+ *   out[r, :] = w * x[r, :] / sqrt(mean(x[r, :]^2) + eps) * silu(z[r, :])
+ * x, z, out [rows, 128] in dtype (rows = B * L * Hv for the delta rule's o and the gate z);
+ * w [128] float32; eps finite, >= 0. out may be x itself (in place); computed in float32. */
+gdr_status gdr_gated_rmsnorm(int64_t rows, gdr_dtype dtype, const void* x, const void* z, const float* w, float eps,
+                             void* out, void* stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdr_last_error(void);
 
@@ -122,7 +161,10 @@ enum {
   GDR_KERNEL_TRANSITION = 2,  /* bf16 long sequences: per-segment state maps */
   GDR_KERNEL_COMBINE = 3,     /* bf16 long sequences: chains the segment maps */
   GDR_KERNEL_DECODE = 4,      /* gdr_decode */
-  GDR_KERNEL_COUNT = 5
+  GDR_KERNEL_GATES = 5,       /* gdr_gates */
+  GDR_KERNEL_CONV = 6,        /* gdr_conv_silu */
+  GDR_KERNEL_NORM = 7,        /* gdr_gated_rmsnorm */
+  GDR_KERNEL_COUNT = 8
 };
 gdr_status gdr_timing_enable(int on);
 gdr_status gdr_timing_read(double* total_ms, int64_t* launches, int n_kernels);

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_function():
 
 def test_kernel_names():
     assert [gdr.kernel_name(i) for i in range(2)] == ["gdr_prep", "gdr_scan"]
-    assert gdr.kernel_name(5) == ""
+    assert [gdr.kernel_name(i) for i in range(len(gdr.KERNELS))] == list(gdr.KERNELS)
+    assert gdr.kernel_name(len(gdr.KERNELS)) == "" and gdr.kernel_name(-1) == ""
 
 
 BASE = 1 << 32   # fake, 256-byte aligned device addresses, far apart
@@ -221,3 +222,53 @@ def test_decode_empty_problems_need_no_pointers():
     for B, L in ((0, 5), (3, 0)):
         d = gdr.make_desc(B, L, 1, 2)
         assert lib.gdr_decode(ctypes.byref(d), *[None] * 10, None) == OK
+
+
+# ---------------------------------------------------------------- layer steps
+def test_gates_host_validation():
+    lib = gdr.library()
+    P = [BASE + i * (1 << 20) for i in range(7)]
+    ok = lambda *ptrs: lib.gdr_gates(2, 5, 4, 1, *ptrs, None)
+    assert lib.gdr_gates(0, 5, 4, 1, *[None] * 7, None) == OK          # empty: no pointers needed
+    assert lib.gdr_gates(2, 5, 0, 1, *[None] * 7, None) == EINVAL and "Hv" in gdr.last_error()
+    assert lib.gdr_gates(2, 5, 4, 7, *P, None) == EINVAL and "dtype" in gdr.last_error()
+    assert ok(None, *P[1:]) == EINVAL and "non-NULL" in gdr.last_error()
+    assert ok(P[0] + 1, *P[1:]) == EINVAL and "aligned" in gdr.last_error()
+    bad = list(P)
+    bad[5] = P[0] + 4                                                   # beta over b
+    assert ok(*bad) == EINVAL and "overlaps" in gdr.last_error()
+
+
+def test_conv_silu_host_validation():
+    lib = gdr.library()
+    P = [BASE + i * (1 << 24) for i in range(8)]   # mixed tail w lengths q k v new_tail
+    call = lambda K, ptrs, B=2, L=10, dt=1: lib.gdr_conv_silu(B, L, 1, 2, K, dt, *ptrs, None)
+    assert call(0, P) == EUNSUP and "K" in gdr.last_error()
+    assert call(9, P) == EUNSUP
+    assert call(4, P, B=0) == OK and call(4, [None] * 8, B=0) == OK
+    assert call(4, [None] * 8, L=0) == OK                               # nothing to compute or carry
+    assert call(4, [None] * 7 + [P[7]], L=0) == EINVAL and "w" in gdr.last_error()   # a tail to carry needs w
+    bad = list(P)
+    bad[4] = P[0] + 64                                                  # q over mixed
+    assert call(4, bad) == EINVAL and "overlaps" in gdr.last_error()
+    bad = list(P)
+    bad[7] = P[1] + 16                                                  # new_tail partly over tail (not in place)
+    assert call(4, bad) == EINVAL and "overlaps" in gdr.last_error()
+    bad = list(P)
+    bad[0] = P[0] + 8
+    assert call(4, bad) == EINVAL and "aligned" in gdr.last_error()
+    assert lib.gdr_conv_silu(2, 64 * 65536, 1, 2, 4, 1, *P, None) == EUNSUP
+
+
+def test_gated_rmsnorm_host_validation():
+    lib = gdr.library()
+    f = ctypes.c_float
+    P = [BASE + i * (1 << 24) for i in range(4)]   # x z w out
+    call = lambda rows, ptrs, eps=1e-6, dt=1: lib.gdr_gated_rmsnorm(rows, dt, ptrs[0], ptrs[1], ptrs[2], f(eps), ptrs[3], None)
+    assert call(0, [None] * 4) == OK
+    assert call(-1, P) == EINVAL
+    assert call(8, P, eps=-1.0) == EINVAL and "eps" in gdr.last_error()
+    assert call(8, P, eps=float("nan")) == EINVAL
+    assert call(8, [P[0], P[1], P[2], P[1]]) == EINVAL and "overlaps" in gdr.last_error()   # out over z
+    assert call(8, [P[0] + 8, P[1], P[2], P[3]]) == EINVAL and "aligned" in gdr.last_error()
+    assert call(8, [None, P[1], P[2], P[3]]) == EINVAL and "non-NULL" in gdr.last_error()

@@ -29,7 +29,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Inputs", "draw", "config", "CONFIGS", "ConfigSpec"]
+__all__ = ["Inputs", "draw", "config", "CONFIGS", "ConfigSpec", "LayerInputs", "draw_layer"]
 
 REGIMES = ("R1", "R2", "R3", "R4", "LONG")
 
@@ -161,3 +161,50 @@ CONFIGS = {
 
 def config(i: int) -> Inputs:
     return CONFIGS[i].draw()
+
+
+@dataclass
+class LayerInputs:
+    """Inputs of the layer steps around the delta rule (CPU tensors, contiguous).
+
+    Gate prologue: b_raw, a_raw [B, L, Hv] (dtype) ~ N(0, 1); A_log [Hv] = log U(1, 16);
+    dt_bias [Hv] ~ -2 + 0.5 N(0, 1) (float32).
+    Conv: mixed [B, L, (2 Hk + Hv) D] (dtype) ~ N(0, 1); tail [B, K-1, Cm] (dtype) ~ N(0, 1);
+    conv_w [Cm, K] ~ U(-1, 1) / sqrt(K) (float32).
+    Norm: x, z [B, L, Hv, D] (dtype) ~ N(0, 1); norm_w [D] ~ 1 + 0.1 N(0, 1) (float32).
+    lengths [B] int32 or None.
+    """
+
+    b_raw: torch.Tensor
+    a_raw: torch.Tensor
+    A_log: torch.Tensor
+    dt_bias: torch.Tensor
+    mixed: torch.Tensor
+    tail: torch.Tensor
+    conv_w: torch.Tensor
+    x: torch.Tensor
+    z: torch.Tensor
+    norm_w: torch.Tensor
+    lengths: torch.Tensor | None
+
+
+def draw_layer(B: int, L: int, Hk: int, Hv: int, K: int, seed: int, dtype: torch.dtype = torch.float32,
+               lengths=None, D: int = 128) -> LayerInputs:
+    """Seeded draws (float32, then cast) in the order b, a, A_log, dt_bias, mixed, tail, conv_w, x, z,
+    norm_w. ``lengths``: None or a list of B ints."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    Cm = (2 * Hk + Hv) * D
+    b_raw = torch.randn(B, L, Hv, generator=gen)
+    a_raw = torch.randn(B, L, Hv, generator=gen)
+    A_log = torch.log(1.0 + 15.0 * torch.rand(Hv, generator=gen))
+    dt_bias = -2.0 + 0.5 * torch.randn(Hv, generator=gen)
+    mixed = torch.randn(B, L, Cm, generator=gen)
+    tail = torch.randn(B, K - 1, Cm, generator=gen)
+    conv_w = (2.0 * torch.rand(Cm, K, generator=gen) - 1.0) / math.sqrt(K)
+    x = torch.randn(B, L, Hv, D, generator=gen)
+    z = torch.randn(B, L, Hv, D, generator=gen)
+    norm_w = 1.0 + 0.1 * torch.randn(D, generator=gen)
+    lens = None if lengths is None else torch.as_tensor(list(lengths), dtype=torch.int32)
+    c = lambda t: t.to(dtype).contiguous()
+    return LayerInputs(b_raw=c(b_raw), a_raw=c(a_raw), A_log=A_log, dt_bias=dt_bias, mixed=c(mixed), tail=c(tail),
+                       conv_w=conv_w.contiguous(), x=c(x), z=c(z), norm_w=norm_w, lengths=lens)
