@@ -8,6 +8,7 @@ the workspace are resident in HBM before the timed region. Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --decode          # one fork decode step instead (gdr_decode, 64 rows x 1 token)
   python bench.py --layer           # the layer steps around it (gates, conv + SiLU, gated RMSNorm)
+  python bench.py --fused           # the prefill with the gate prologue and gated RMSNorm fused in
   python bench.py --copy-probe      # a plain device copy of known size, for HBM counter scaling
 """
 from __future__ import annotations
@@ -44,7 +45,7 @@ def algorithmic(B, L, Hk, Hv, esz, n_s0, want_state):
     return units, nbytes, flops
 
 
-def kernel_bytes(name, B, L, Hk, Hv, esz, P):
+def kernel_bytes(name, B, L, Hk, Hv, esz, P, fused=False):
     """Bytes a kernel of the path must read and write through its own interface, one launch.
 
     Intermediates count where they cross HBM: the per-chunk record (T diag(beta) and decayed
@@ -59,6 +60,8 @@ def kernel_bytes(name, B, L, Hk, Hv, esz, P):
     gb = 2 * B * L * Hv * 4
     recs = B * Hv * NC * rec
     frac = (P - 1) / P if P > 1 else 0.0                 # share of chunks in the first P-1 segments
+    if fused:   # raw bf16 gate projections read by the prep, the gate z by the output pass
+        gb = 2 * B * L * Hv * 2
     if name == "gdr_prep":
         return 2 * qk + gb + recs
     if name == "gdr_transition":
@@ -66,7 +69,8 @@ def kernel_bytes(name, B, L, Hk, Hv, esz, P):
     if name == "gdr_combine":
         return B * Hv * (P - 1) * (slot * 3 // 2) + B * Hv * P * slot // 2
     if name == "gdr_scan":
-        return 2 * qk + 2 * vo + recs + B * Hv * D * D * 4 + (B * Hv * P * slot // 2 if P > 1 else 0)
+        return (2 * qk + 2 * vo + recs + B * Hv * D * D * 4 + (B * Hv * P * slot // 2 if P > 1 else 0)
+                + (vo if fused else 0))
     raise KeyError(name)
 
 
@@ -242,6 +246,7 @@ def main():
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--rows", type=int, default=64)
     ap.add_argument("--layer", action="store_true")
+    ap.add_argument("--fused", action="store_true")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -269,11 +274,18 @@ def main():
     q, k, v, g, beta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
     o = torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
     s_final = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
-    desc = gdr.make_desc(B, L, Hk, Hv, 0, True, False)
+    desc = gdr.make_desc(B, L, Hk, Hv, 0, True, a.fused)
     ws = torch.empty(gdr.workspace_size(desc), device=dev, dtype=torch.uint8)
+    fused = {}
+    if a.fused:   # raw bf16 gate projections in place of g and beta, and the gate z of the norm
+        from workloads import draw_layer
+        y = draw_layer(B, L, 1, Hv, 1, 5252, torch.bfloat16, D=Dv)
+        fused = {"gates": tuple(t.to(dev) for t in (y.b_raw, y.a_raw, y.A_log, y.dt_bias)),
+                 "norm": (y.x.to(dev), y.norm_w.to(dev), 1e-6)}
+        g = beta = None
 
     def step():
-        gdr.prefill(q, k, v, g, beta, out=o, s_final=s_final, workspace=ws)
+        gdr.prefill(q, k, v, g, beta, out=o, s_final=s_final, workspace=ws, **fused)
 
     for _ in range(a.warmup):
         step()
@@ -292,11 +304,13 @@ def main():
     ms = start.elapsed_time(stop) / a.steps
 
     units, nbytes, flops = algorithmic(B, L, Hk, Hv, 2, 0, True)
+    if a.fused:   # raw bf16 projections instead of fp32 g, beta; plus the gate z
+        nbytes += -2 * B * L * Hv * 4 + 2 * B * L * Hv * 2 + B * L * Hv * Dv * 2
     P = seg_plan(B, Hv, (L + CHUNK - 1) // CHUNK)
     per_kernel = {n: (t / max(c, 1), c) for n, (t, c) in kern.items() if c > 0}
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
     k_ms = per_kernel[dominant][0]
-    k_bytes = kernel_bytes(dominant, B, L, Hk, Hv, 2, P)
+    k_bytes = kernel_bytes(dominant, B, L, Hk, Hv, 2, P, fused=a.fused)
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     traffic = None
     prof = os.path.join(ROOT, "profiles", "traffic_l16384_bf16.json")
@@ -306,7 +320,7 @@ def main():
         if tr.get("source_hash") == source_hash():   # counters of these very kernels only
             traffic = tr.get("kernels", {}).get(dominant, {}).get("hbm_bytes")
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not a.fused else METRIC + ", gate prologue and gated RMSNorm fused",
         "value": units / (ms * 1e-3),
         "unit": "tokens·heads/s",
         "n_gpus": 1,
@@ -318,8 +332,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) q/k/v, beta~U(0.2,0.9), g~-U(0,0.5))",
-        "config": {"workload": "long prefill B=1 L=16384 Hk=16 Hv=32 Dk=Dv=128 bf16 q/k/v fp32 g/beta/state, "
-                               "zero initial state, final state returned",
+        "config": {"workload": ("long prefill B=1 L=16384 Hk=16 Hv=32 Dk=Dv=128 bf16 q/k/v fp32 g/beta/state, "
+                                "zero initial state, final state returned") if not a.fused else
+                               ("long prefill B=1 L=16384 Hk=16 Hv=32 Dk=Dv=128 bf16 q/k/v, gate prologue from raw "
+                                "bf16 projections and gated RMSNorm fused, fp32 state, final state returned"),
                    "B": B, "L": L, "Hk": Hk, "Hv": Hv, "D": Dk, "global_batch": B, "seq_len": L,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -332,7 +348,7 @@ def main():
                  "source_hash": source_hash()},
         "cpu_baseline": None,
     }
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and not a.fused:
         line["cpu_baseline"] = cpu_baseline(x, a.cpu_heads)
     print(json.dumps(line), flush=True)
 

@@ -59,6 +59,8 @@ def library() -> ctypes.CDLL:
     lib.gdr_prefill_check.restype = i32
     lib.gdr_prefill.argtypes = [ctypes.POINTER(Desc)] + [vp] * 11 + [sz, vp]
     lib.gdr_prefill.restype = i32
+    lib.gdr_prefill_ex.argtypes = [ctypes.POINTER(Desc)] + [vp] * 8 + [ctypes.POINTER(Fusion)] + [vp] * 3 + [sz, vp]
+    lib.gdr_prefill_ex.restype = i32
     lib.gdr_decode.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10 + [vp]
     lib.gdr_decode.restype = i32
     i64, f32 = ctypes.c_int64, ctypes.c_float
@@ -151,8 +153,11 @@ def _lengths_from_valid(valid, B, L, device):
     return lengths.to(device)
 
 
-def _inputs(q, k, v, g, beta, valid, s0, s0_row):
-    """Validate the torch arguments shared by prefill and decode; returns what the call needs."""
+def _inputs(q, k, v, g, beta, valid, s0, s0_row, gates=None):
+    """Validate the torch arguments shared by prefill and decode; returns what the call needs.
+
+    With ``gates`` = (b_raw, a_raw, A_log, dt_bias) given, g and beta must be None and the raw
+    projections set the beta dtype."""
     import torch
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4:
         raise ValueError("q, k must be [B, L, Hk, D] and v [B, L, Hv, Dv]")
@@ -163,13 +168,30 @@ def _inputs(q, k, v, g, beta, valid, s0, s0_row):
         raise ValueError("tensors must be on the GPU")
     if q.dtype not in (torch.float32, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype, float32 or bfloat16")
-    if tuple(v.shape[:2]) != (B, L) or g.shape != (B, L, Hv) or beta.shape != (B, L, Hv):
-        raise ValueError("v [B, L, Hv, Dv], g and beta [B, L, Hv] expected")
-    if g.dtype != torch.float32:
-        raise ValueError("g must be float32")
-    if beta.dtype not in (torch.float32, q.dtype):
-        raise ValueError("beta must be float32 or q's dtype")
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("s0", s0)):
+    if tuple(v.shape[:2]) != (B, L):
+        raise ValueError("v [B, L, Hv, Dv] expected")
+    if gates is not None:
+        if g is not None or beta is not None:
+            raise ValueError("g and beta must be None when the gate prologue is fused")
+        b_raw, a_raw, A_log, dt_bias = gates
+        if b_raw.shape != (B, L, Hv) or a_raw.shape != (B, L, Hv) or a_raw.dtype != b_raw.dtype:
+            raise ValueError("b_raw and a_raw must be [B, L, Hv] of one dtype")
+        if b_raw.dtype not in (torch.float32, q.dtype):
+            raise ValueError("b_raw must be float32 or q's dtype")
+        if A_log.shape != (Hv,) or dt_bias.shape != (Hv,) or A_log.dtype != torch.float32 or dt_bias.dtype != torch.float32:
+            raise ValueError(f"A_log and dt_bias must be float32 [{Hv}]")
+        beta_dtype = b_raw.dtype
+        extra = (("b_raw", b_raw), ("a_raw", a_raw), ("A_log", A_log), ("dt_bias", dt_bias))
+    else:
+        if g is None or beta is None or g.shape != (B, L, Hv) or beta.shape != (B, L, Hv):
+            raise ValueError("g and beta [B, L, Hv] expected")
+        if g.dtype != torch.float32:
+            raise ValueError("g must be float32")
+        if beta.dtype not in (torch.float32, q.dtype):
+            raise ValueError("beta must be float32 or q's dtype")
+        beta_dtype = beta.dtype
+        extra = ()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("s0", s0)) + extra:
         if t is not None and (t.device != dev or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous tensor on {dev}")
     lengths = _lengths_from_valid(valid, B, L, dev)
@@ -188,19 +210,42 @@ def _inputs(q, k, v, g, beta, valid, s0, s0_row):
                 raise ValueError(f"s0_row entries must lie in [0, {n_s0})")
             s0_row = s0_row.to(dev)
         s0_row = s0_row.contiguous()
-    desc = make_desc(B, L, Hk, Hv, n_s0, q.dtype == torch.bfloat16, beta.dtype == torch.bfloat16, Dk, Dv)
+    desc = make_desc(B, L, Hk, Hv, n_s0, q.dtype == torch.bfloat16, beta_dtype == torch.bfloat16, Dk, Dv)
     return desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev
 
 
-def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=True, out=None,
-            s_final=None, workspace=None):
+class Fusion(ctypes.Structure):
+    _fields_ = [("b_raw", ctypes.c_void_p), ("a_raw", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("z", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
+
+
+def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, norm=None, want_state=True,
+            out=None, s_final=None, workspace=None):
     """Run the chunked gated delta rule on torch's current stream; see the module docstring.
 
     out / s_final / workspace may be given to reuse buffers (s_final may be s0 itself, for an
     in-place continuation, when s0_row is None).
+
+    Fused work (gdr_prefill_ex): ``gates`` = (b_raw, a_raw, A_log, dt_bias) forms beta and g from
+    the raw projections inside the kernels (pass g = beta = None); ``norm`` = (z, norm_w, eps)
+    returns the gated RMSNorm w o / rms(o) silu(z) of the output instead of o.
     """
     import torch
-    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row)
+    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row, gates)
+    fu = None
+    if gates is not None or norm is not None:
+        fu = Fusion()
+        if gates is not None:
+            fu.b_raw, fu.a_raw, fu.A_log, fu.dt_bias = (t.data_ptr() for t in gates)
+        if norm is not None:
+            z, nw, eps = norm
+            if z.shape != v.shape or z.dtype != v.dtype or nw.shape != (Dv,) or nw.dtype != torch.float32:
+                raise ValueError("norm: z must match v's shape and dtype and norm_w be float32 [128]")
+            for name, t in (("z", z), ("norm_w", nw)):
+                if t.device != dev or not t.is_contiguous():
+                    raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+            fu.z, fu.norm_w, fu.norm_eps = z.data_ptr(), nw.data_ptr(), float(eps)
     need = workspace_size(desc)
     o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
     if want_state and s_final is None:
@@ -211,9 +256,9 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=Tr
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
-        st = library().gdr_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(lengths), _ptr(s0), _ptr(s0_row), _ptr(o), _ptr(s_final),
-                                   _ptr(workspace), need, stream)
+        st = library().gdr_prefill_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(lengths), _ptr(s0), _ptr(s0_row), None if fu is None else ctypes.byref(fu),
+                                      _ptr(o), _ptr(s_final), _ptr(workspace), need, stream)
     _raise(st)
     return o, s_final
 

@@ -72,17 +72,33 @@ gdr_status check_desc(const gdr_desc* d) {
 
 gdr_status check_all(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
                      const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
-                     const void* o, const float* s_final, const void* ws, size_t ws_bytes, bool need_ws = true) {
+                     const void* o, const float* s_final, const void* ws, size_t ws_bytes, bool need_ws = true,
+                     const gdr_fusion* fu = nullptr) {
   gdr_status st = check_desc(d);
   if (st != GDR_OK) return st;
   const size_t B = d->B, L = d->L, Hk = d->Hk, Hv = d->Hv, Dd = gdr::kHeadDim;
   const size_t esz = dtype_size(d->qkv_dtype), bsz = dtype_size(d->beta_dtype);
   const bool any_tokens = B * L > 0;
+  const bool fused_gates = fu && (fu->b_raw || fu->a_raw || fu->A_log || fu->dt_bias);
+  const bool fused_norm = fu && (fu->z || fu->norm_w);
+  if (fused_gates) {
+    if (!fu->b_raw || !fu->a_raw || !fu->A_log || !fu->dt_bias)
+      return fail(GDR_EINVAL, "fusion: b_raw, a_raw, A_log and dt_bias go together");
+    if (g || beta) return fail(GDR_EINVAL, "fusion: g and beta must be NULL when the gate prologue is fused");
+    if (!aligned(fu->b_raw, bsz) || !aligned(fu->a_raw, bsz) || !aligned(fu->A_log, 4) || !aligned(fu->dt_bias, 4))
+      return fail(GDR_EINVAL, "fusion: b_raw, a_raw, A_log and dt_bias must be element-aligned");
+  }
+  if (fused_norm) {
+    if (!fu->z || !fu->norm_w) return fail(GDR_EINVAL, "fusion: z and norm_w go together");
+    if (!aligned(fu->z, 16) || !aligned(fu->norm_w, 16)) return fail(GDR_EINVAL, "fusion: z and norm_w must be 16-byte aligned");
+    if (!(fu->norm_eps >= 0.f) || fu->norm_eps > 1e30f) return fail(GDR_EINVAL, "fusion: norm_eps must be finite and >= 0");
+  }
   if (any_tokens) {
-    if (!q || !k || !v || !g || !beta || !o) return fail(GDR_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+    if (!q || !k || !v || !o || (!fused_gates && (!g || !beta)))
+      return fail(GDR_EINVAL, "q, k, v, g, beta and o must be non-NULL");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
       return fail(GDR_EINVAL, "q, k, v and o must be 16-byte aligned");
-    if (!aligned(g, 4) || !aligned(beta, bsz)) return fail(GDR_EINVAL, "g and beta must be element-aligned");
+    if (!fused_gates && (!aligned(g, 4) || !aligned(beta, bsz))) return fail(GDR_EINVAL, "g and beta must be element-aligned");
   }
   if (s0_row && !s0) return fail(GDR_EINVAL, "s0_row given without s0");
   if (s0) {
@@ -106,9 +122,15 @@ gdr_status check_all(const gdr_desc* d, const void* q, const void* k, const void
   const size_t state_bytes = Hv * Dd * Dd * sizeof(float);
   const Range inputs[] = {
       range("q", q, B * L * Hk * Dd * esz),   range("k", k, B * L * Hk * Dd * esz),
-      range("v", v, B * L * Hv * Dd * esz),   range("g", g, B * L * Hv * sizeof(float)),
-      range("beta", beta, B * L * Hv * bsz),  range("lengths", lengths, lengths ? B * 4 : 0),
+      range("v", v, B * L * Hv * Dd * esz),   range("g", g, g ? B * L * Hv * sizeof(float) : 0),
+      range("beta", beta, beta ? B * L * Hv * bsz : 0),  range("lengths", lengths, lengths ? B * 4 : 0),
       range("s0", s0, s0 ? size_t(d->n_s0) * state_bytes : 0), range("s0_row", s0_row, s0_row ? B * 4 : 0),
+      range("b_raw", fused_gates ? fu->b_raw : nullptr, B * L * Hv * bsz),
+      range("a_raw", fused_gates ? fu->a_raw : nullptr, B * L * Hv * bsz),
+      range("A_log", fused_gates ? fu->A_log : nullptr, Hv * 4),
+      range("dt_bias", fused_gates ? fu->dt_bias : nullptr, Hv * 4),
+      range("z", fused_norm ? fu->z : nullptr, B * L * Hv * Dd * esz),
+      range("norm_w", fused_norm ? fu->norm_w : nullptr, Dd * 4),
   };
   const Range outs[] = {
       range("o", o, B * L * Hv * Dd * esz),
@@ -205,8 +227,16 @@ gdr_status gdr_prefill_check(const gdr_desc* d, const void* q, const void* k, co
 gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
                        const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row, void* o,
                        float* s_final, void* ws, size_t ws_bytes, void* stream) {
-  gdr_status st = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, ws, ws_bytes);
+  return gdr_prefill_ex(d, q, k, v, g, beta, lengths, s0, s0_row, nullptr, o, s_final, ws, ws_bytes, stream);
+}
+
+gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                          const gdr_fusion* fu, void* o, float* s_final, void* ws, size_t ws_bytes, void* stream) {
+  gdr_status st = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, ws, ws_bytes, true, fu);
   if (st != GDR_OK) return st;
+  const bool fused_gates = fu && fu->b_raw;
+  const bool fused_norm = fu && fu->z;
   if (d->B == 0) return GDR_OK;
   if (d->L == 0 && !s_final) return GDR_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -215,6 +245,12 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
 
   if (NC > 0) {
     gdr::PrepParams pp{q, k, g, beta, lengths, ws, d->B, d->L, d->Hk, d->Hv, NC};
+    if (fused_gates) {
+      pp.b_raw = fu->b_raw;
+      pp.a_raw = fu->a_raw;
+      pp.A_log = fu->A_log;
+      pp.dt_bias = fu->dt_bias;
+    }
     hipError_t e = timed(GDR_KERNEL_PREP, s, [&] { return gdr::launch_prep(pp, bf16, d->beta_dtype == GDR_BF16, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "prep launch: %s", hipGetErrorString(e));
   }
@@ -224,6 +260,11 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
                           : nullptr;
   gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final, NC > 0 ? ws : nullptr, seg,
                      d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0, plan.P, plan.Ls};
+  if (fused_norm && bf16) {   // applied in the output pass's registers
+    sp.z = fu->z;
+    sp.norm_w = fu->norm_w;
+    sp.eps = fu->norm_eps;
+  }
   if (plan.P > 1) {
     hipError_t e = timed(GDR_KERNEL_TRANSITION, s, [&] { return gdr::launch_transition(sp, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "transition launch: %s", hipGetErrorString(e));
@@ -232,6 +273,11 @@ gdr_status gdr_prefill(const gdr_desc* d, const void* q, const void* k, const vo
   }
   hipError_t e = timed(GDR_KERNEL_SCAN, s, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));
+  if (fused_norm && !bf16 && d->L > 0) {   // float32: normalise o in place
+    gdr::NormParams np{o, fu->z, fu->norm_w, fu->norm_eps, o, int64_t(d->B) * d->L * d->Hv};
+    e = timed(GDR_KERNEL_NORM, s, [&] { return gdr::launch_gated_rmsnorm(np, 0, s); });
+    if (e != hipSuccess) return fail(GDR_EHIP, "norm launch: %s", hipGetErrorString(e));
+  }
   return GDR_OK;
 }
 

@@ -70,6 +70,12 @@ struct PrepParams {
   const int32_t* lengths;
   void* ws;          // records, see above
   int B, L, Hk, Hv, NC;
+  // fused gate prologue (null b_raw = g and beta as given): beta = sigmoid(b_raw),
+  // g = -exp(A_log) softplus(a_raw + dt_bias); b_raw, a_raw [B, L, Hv] in beta's dtype
+  const void* b_raw;
+  const void* a_raw;
+  const float* A_log;     // [Hv]
+  const float* dt_bias;   // [Hv]
 };
 
 struct ScanParams {
@@ -85,6 +91,10 @@ struct ScanParams {
   float* seg;        // segment states (bf16 with P > 1), see above
   int B, L, Hk, Hv, NC, n_s0;
   int P, Ls;         // segments and chunks per segment
+  // fused gated RMSNorm of o (bf16 output pass; null z = plain o): o <- w o / rms(o) silu(z)
+  const void* z;     // [B, L, Hv, 128], o's dtype
+  const float* norm_w;   // [128]
+  float eps;
 };
 
 struct DecodeParams {

@@ -4,7 +4,9 @@
 // From the chunk's raw q, k, g and beta it forms
 //   rk_t = (|k_t|^2 + 1e-6)^-1/2,  rq_t = (|q_t|^2 + 1e-6)^-1/2 * 128^-1/2   (model page model.py,
 //          function _l2norm, eps inside the rsqrt; q scaled by Dk^-1/2 as in delta_rule_reference)
-//   beta'_t, g'_t with the right-pad guard (model.py, _dn_gates: pads neither write nor decay)
+//   beta'_t, g'_t with the right-pad guard (model.py, _dn_gates: pads neither write nor decay);
+//          with the gate prologue fused, beta = sigmoid(b_raw) and g = -exp(A_log) softplus(a_raw +
+//          dt_bias) are formed here from the raw projections instead of being read
 //   gamma_t = inclusive cumulative sum of g' within the chunk
 //   A[t][i] = beta'_t e^{gamma_t - gamma_i} rk_t rk_i (k_t . k_i)   (i < t)
 //   T = (I + A)^-1, Tb = T diag(beta'),  P[t][i] = rq_t rk_i e^{gamma_t - gamma_i} (q_t . k_i)  (i <= t)
@@ -186,8 +188,15 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
       const int t = t0 + lane;
       const size_t off = ((size_t)b * p.L + t) * p.Hv + h;
       if (t < len) {
-        gv = p.g[off];
-        bv = to_f(reinterpret_cast<const TB*>(p.beta)[off]);
+        if (p.b_raw) {   // fused gate prologue (model.py, _dn_gates)
+          const float x = to_f(reinterpret_cast<const TB*>(p.a_raw)[off]) + p.dt_bias[h];
+          const float sp = fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));   // softplus without overflow
+          gv = -__expf(p.A_log[h]) * sp;
+          bv = __builtin_amdgcn_rcpf(1.0f + __expf(-to_f(reinterpret_cast<const TB*>(p.b_raw)[off])));
+        } else {
+          gv = p.g[off];
+          bv = to_f(reinterpret_cast<const TB*>(p.beta)[off]);
+        }
       }
     }
 #pragma unroll

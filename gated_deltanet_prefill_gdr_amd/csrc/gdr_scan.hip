@@ -93,6 +93,10 @@ __device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+// 1 / (1 + e^-x) with the hardware exp2 and reciprocal
+__device__ __forceinline__ float silu_gate(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
 
 // K^T operand for state tile (key block kb, half s2), k = tokens of token block kb2, from the
 // swizzled K tile. In each 16-lane group the transposing read hands lane m element (m & 3) of
@@ -188,6 +192,13 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   const i32x4 rr = rsrc_words(reinterpret_cast<const unsigned char*>(p.ws) + ((size_t)b * p.Hv + h) * p.NC * kRecB,
                               (uint32_t)p.NC * kRecB);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + vo_base, vo_bytes);
+  // fused gated RMSNorm (outputs only): gate z in o's layout, weights of this lane's columns
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z ? reinterpret_cast<const __bf16*>(p.z) + vo_base : nullptr,
+                                              p.z ? vo_bytes : 0u);
+  f4 nw[NSL];
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl)
+    nw[sl] = (kOut && p.z) ? *reinterpret_cast<const f4*>(p.norm_w + seg_col<kOut>(w, sl) + 4 * G) : f4_splat(0.f);
 
   // This wave's share of chunk c: K (and Q) and V rows R w .. R w + R - 1 (R = 64 / NW, loads
   // of four rows each) and the record blocks w, w + NW, ... (outputs: blocks 0..12; transitions:
@@ -253,13 +264,68 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     }
   }
 
+  // Output tiles of a chunk and, with the fused gated RMSNorm, its gate values. The norm needs each
+  // token's sum of squares over all 128 columns, i.e. over all waves: every wave leaves its partial
+  // sums in LDS (two buffers, by chunk parity) and normalises and stores chunk c - 1 right after
+  // the barrier that opens chunk c, so the fusion adds no barrier.
+  f4 Ot[4][NSL];
+  i32x2 zv[4][NSL];
+  const bool fuse = kOut && p.z != nullptr;
+  float* part = reinterpret_cast<float*>(lds + 2 * Cfg::kBuf);   // [2][NW][64]
+  auto store_o = [&](int c) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        const bf16x4 ob = {(__bf16)Ot[mt][sl][0], (__bf16)Ot[mt][sl][1], (__bf16)Ot[mt][sl][2], (__bf16)Ot[mt][sl][3]};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, orow + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
+      }
+    }
+  };
+  auto finish_norm = [&](int c) {   // w o / sqrt(mean(o^2) + eps) silu(z) for chunk c, then store
+    const float* pp = part + (c & 1) * NW * C;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float ss = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) ss += pp[ww * C + 16 * mt + n16];
+      const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        const bf16x4 zb = __builtin_bit_cast(bf16x4, zv[mt][sl]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float zf = (float)zb[i];
+          Ot[mt][sl][i] = nw[sl][i] * (Ot[mt][sl][i] * r) * (zf * silu_gate(zf));
+        }
+      }
+    }
+    store_o(c);
+  };
+
   issue(c_begin);
   wait_and_barrier<0>();
+  // The same wait as a builtin the compiler sees: the entering-state loads are then known complete,
+  // so it places no wait for them inside the loop (where it would also stall on the next chunk's
+  // loads into LDS).
+  __builtin_amdgcn_s_waitcnt(0);
 
   for (int c = c_begin; c < c_end; ++c) {
-    // chunk c has landed for every wave, and every wave is done with chunk c - 1's buffer
+    // chunk c has landed for every wave, every wave is done with chunk c - 1's buffer, and (fused
+    // norm) chunk c - 1's partial sums are in LDS. Outstanding vector-memory operations issued
+    // after chunk c's loads: chunk c - 1's four output stores, or (fused norm) its four gate loads.
     wait_and_barrier<Cfg::kStores>();
+    if (fuse && c > c_begin) finish_norm(c - 1);
     if (c + 1 < c_end) issue(c + 1);
+    if (fuse) {   // this chunk's gate values, in flight during the chunk's arithmetic
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl)
+          zv[mt][sl] = __builtin_amdgcn_raw_buffer_load_b64(
+              rz, ((uint32_t)c * C + 16 * mt + n16) * vo_row + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
+    }
 
     const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const unsigned char* Kt = Bf + Cfg::kK;
@@ -341,31 +407,35 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f4 Ot[NSL];
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) Ot[sl] = f4_splat(0.f);
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = f4_splat(0.f);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
 #pragma unroll
-          for (int sl = 0; sl < NSL; ++sl) Ot[sl] = mfma(Sop[sl][kb], qf, Ot[sl]);
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
         }
         const float cc = sc[C + 16 * mt + n16];
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) Ot[sl] *= cc;
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= cc;
 #pragma unroll
         for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
           const bf16x8 pf = lds16(Rc + 1024 * (kFragBlocks + frag_block(mt, kb2)) + 16 * lane);
 #pragma unroll
-          for (int sl = 0; sl < NSL; ++sl) Ot[sl] = mfma(Dop[sl][kb2], pf, Ot[sl]);
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
-        const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
+        if (fuse) {   // this wave's sum of squares of the token's columns: its four lanes, into LDS
+          float ss = 0.f;
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) {
-          const bf16x4 ob = {(__bf16)Ot[sl][0], (__bf16)Ot[sl][1], (__bf16)Ot[sl][2], (__bf16)Ot[sl][3]};
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, orow + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
+          for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss += Ot[mt][sl][i] * Ot[mt][sl][i];
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          if (G == 0) part[(c & 1) * NW * C + w * C + 16 * mt + n16] = ss;
         }
       }
+      if (!fuse) store_o(c);
     }
     // S <- e^{gamma_63} S + K^T diag(d) Delta
     const float egc = sc[3 * C];
@@ -382,6 +452,10 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] = mfma(kt, Ddop[sl][kb2], S[sl][kb][s2]);
         }
       }
+  }
+  if (fuse && c_end > c_begin) {   // the last chunk's norm: its partial sums, then store
+    lds_barrier();
+    finish_norm(c_end - 1);
   }
   __builtin_amdgcn_s_waitcnt(0);   // no load into LDS may still be in flight when the workgroup ends
 
@@ -410,7 +484,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
 // Outputs: one workgroup per (row, segment, value head), heads fastest.
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<true>::kBuf];
+  // two chunk buffers, then the per-wave row sums of the fused norm (two chunks)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<true>::kBuf + 2 * SegCfg<true>::NW * C * 4];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % p.P, b = lam / (p.Hv * p.P);
   seg_body<true>(p, lds, b, h, j);

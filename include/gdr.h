@@ -98,6 +98,35 @@ gdr_status gdr_prefill(const gdr_desc* desc, const void* q, const void* k, const
                        const int32_t* s0_row, void* o, float* s_final, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* Work fused into gdr_prefill_ex (model page, model.py, _linear_layer: the gate prologue feeds the
+ * delta rule and the gated RMSNorm follows it). Either part may be left out (NULL pointers).
+ *   Gate prologue: b_raw, a_raw [B, L, Hv] in desc->beta_dtype (the raw projections) and A_log,
+ *     dt_bias [Hv] float32, all four or none. When given, the call's g and beta must be NULL:
+ *     beta = sigmoid(b_raw) and g = -exp(A_log) softplus(a_raw + dt_bias) (gdr_gates) are formed
+ *     inside the per-chunk kernel, in float32, and never written to memory.
+ *   Gated RMSNorm: z [B, L, Hv, 128] in qkv_dtype, 16-byte aligned, and norm_w [128] float32,
+ *     16-byte aligned, both or neither; norm_eps finite, >= 0. When given, o holds
+ *     norm_w * o / sqrt(mean(o^2) + norm_eps) * silu(z) per (token, head) (gdr_gated_rmsnorm)
+ *     instead of the raw output. For bf16 it is applied in registers before o is stored; for
+ *     float32 a second kernel normalises o in place after the scan. */
+typedef struct {
+  const void* b_raw;
+  const void* a_raw;
+  const float* A_log;
+  const float* dt_bias;
+  const void* z;
+  const float* norm_w;
+  float norm_eps;
+} gdr_fusion;
+
+/* gdr_prefill with optional fused prologue / epilogue work (fusion may be NULL: then it is
+ * gdr_prefill). Same arguments, layouts, workspace and errors as gdr_prefill; g and beta must be
+ * NULL when the gate prologue is fused, and non-NULL otherwise (when there are tokens). */
+gdr_status gdr_prefill_ex(const gdr_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                          const gdr_fusion* fusion, void* o, float* s_final, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* The same computation, token by token, for short sequences: decode steps and fork
  * continuations over many rows (the fork model's fork_delta_rule with h0, h0_idx and an in-place
  * store, model.py, _fork_linear_layer). Arguments, layouts, pad guard, s0_row gather, in-place

@@ -272,3 +272,56 @@ def test_gated_rmsnorm_host_validation():
     assert call(8, [P[0], P[1], P[2], P[1]]) == EINVAL and "overlaps" in gdr.last_error()   # out over z
     assert call(8, [P[0] + 8, P[1], P[2], P[3]]) == EINVAL and "aligned" in gdr.last_error()
     assert call(8, [None, P[1], P[2], P[3]]) == EINVAL and "non-NULL" in gdr.last_error()
+
+
+# ---------------------------------------------------------------- gdr_prefill_ex (fused gates / norm)
+def prefill_ex(c, fu, g_beta=True):
+    lib = gdr.library()
+    ptrs = [x or None for x in c.ptrs()]
+    if not g_beta:
+        ptrs[3] = ptrs[4] = None
+    return lib.gdr_prefill_ex(ctypes.byref(c.desc), *ptrs[:8], ctypes.byref(fu), ptrs[8], ptrs[9], ptrs[10],
+                              c.ws_bytes, None)
+
+
+def fusion(c, gates=True, norm=True):
+    fu = gdr.Fusion()
+    base = c.p["ws"] + (1 << 30)
+    if gates:
+        fu.b_raw, fu.a_raw, fu.A_log, fu.dt_bias = base, base + (1 << 24), base + (2 << 24), base + (3 << 24)
+    if norm:
+        fu.z, fu.norm_w, fu.norm_eps = base + (4 << 24), base + (5 << 24), 1e-6
+    return fu
+
+
+@pytest.mark.parametrize("mutate,g_beta,msg", [
+    (lambda f: None, True, "must be NULL"),                           # g, beta given with fused gates
+    (lambda f: setattr(f, "A_log", None), False, "go together"),
+    (lambda f: setattr(f, "norm_w", None), False, "go together"),
+    (lambda f: setattr(f, "norm_eps", -1.0), False, "norm_eps"),
+    (lambda f: setattr(f, "norm_eps", float("inf")), False, "norm_eps"),
+    (lambda f: setattr(f, "norm_w", f.norm_w + 4), False, "aligned"),
+    (lambda f: setattr(f, "b_raw", f.b_raw + 1), False, "aligned"),
+])
+def test_prefill_ex_rejects_bad_fusion(mutate, g_beta, msg):
+    c = Call()
+    fu = fusion(c)
+    mutate(fu)
+    assert prefill_ex(c, fu, g_beta) == EINVAL
+    assert msg in gdr.last_error()
+
+
+def test_prefill_ex_output_must_not_overlap_fused_inputs():
+    c = Call()
+    fu = fusion(c)
+    fu.z = c.p["o"] + 256
+    assert prefill_ex(c, fu, g_beta=False) == EINVAL and "overlaps z" in gdr.last_error()
+    fu = fusion(c)
+    fu.b_raw = c.p["s_final"]
+    assert prefill_ex(c, fu, g_beta=False) == EINVAL and "overlaps b_raw" in gdr.last_error()
+
+
+def test_prefill_ex_without_fused_gates_still_needs_g_and_beta():
+    c = Call()
+    fu = fusion(c, gates=False)
+    assert prefill_ex(c, fu, g_beta=False) == EINVAL and "non-NULL" in gdr.last_error()
