@@ -1,7 +1,7 @@
 """Benchmark of the chunked gated delta rule prefill on one MI355X.
 
-One step = one gdr_prefill call (both kernels: per-chunk prep, then the sequential state scan)
-over the long-prefill workload: B = 1, 16 key / 32 value heads, Dk = Dv = 128, L = 16384,
+One step = one gdr_prefill call (all its kernels: the per-chunk prep, the segment transitions and
+their combine, the output scan) over the long-prefill workload: B = 1, 16 key / 32 value heads, Dk = Dv = 128, L = 16384,
 bf16 q/k/v, fp32 g/beta/state, zero initial state, final state returned. Inputs, outputs and
 the workspace are resident in HBM before the timed region. Prints one JSON line.
 
@@ -119,6 +119,30 @@ def copy_probe(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "reps": reps}))
 
 
+def run_timed(step, steps):
+    """Time `steps` calls of step(): first with nothing but two events around the loop (the step
+    time), then again with the library's per-kernel HIP events on (kernel averages; those events
+    sit between the kernels, so they are kept out of the step time)."""
+    import torch
+    import gated_deltanet_prefill_gdr_amd as gdr
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    gdr.timing_enable(True)
+    gdr.timing_read()                      # drop anything recorded before
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = gdr.timing_read()
+    gdr.timing_enable(False)
+    return ms, kern
+
+
 def bench_decode(a):
     """One decode step of the fork workload: every row continues its own state by one token, in
     place (s_final is s0). Bound by the state read and write; the token rows are tiny."""
@@ -138,17 +162,7 @@ def bench_decode(a):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    gdr.timing_enable(True)
-    gdr.timing_read()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(a.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern = gdr.timing_read()
-    gdr.timing_enable(False)
-    ms = start.elapsed_time(stop) / a.steps
+    ms, kern = run_timed(step, a.steps)
     k_ms = kern["gdr_decode"][0] / max(kern["gdr_decode"][1], 1)
     units, nbytes, _ = algorithmic(B, L, Hk, Hv, 2, B, True)
     achieved = nbytes / (k_ms * 1e-3) / 1e9
@@ -204,17 +218,8 @@ def bench_layer(a):
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    gdr.timing_enable(True)
-    gdr.timing_read()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(a.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern = {n: (ms / c, c) for n, (ms, c) in gdr.timing_read().items() if c > 0}
-    gdr.timing_enable(False)
-    ms = start.elapsed_time(stop) / a.steps
+    ms, kern = run_timed(step, a.steps)
+    kern = {n: (t / c, c) for n, (t, c) in kern.items() if c > 0}
     nb = layer_bytes(B, L, Hk, Hv, K, 2)
     per = {n: {"ms": kern[n][0], "bytes": nb[n], "GB/s": nb[n] / (kern[n][0] * 1e-3) / 1e9,
                "frac": nb[n] / (kern[n][0] * 1e-3) / 1e9 / HBM_PEAK_GBS} for n in nb}
@@ -290,18 +295,7 @@ def main():
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    gdr.timing_enable(True)
-    gdr.timing_read()                      # drop anything recorded before the timed region
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(a.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    kern = gdr.timing_read()
-    gdr.timing_enable(False)
-    ms = start.elapsed_time(stop) / a.steps
+    ms, kern = run_timed(step, a.steps)
 
     units, nbytes, flops = algorithmic(B, L, Hk, Hv, 2, 0, True)
     if a.fused:   # raw bf16 projections instead of fp32 g, beta; plus the gate z

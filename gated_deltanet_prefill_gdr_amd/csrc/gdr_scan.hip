@@ -45,7 +45,8 @@ template <bool kOut> struct SegCfg {
   static constexpr int NSL = (kOut ? 8 : 16) / NW;      // 16-column slices per wave
   static constexpr int kK = 0, kV = kBufK, kRec = 2 * kBufK;
   static constexpr int kQ = kRec + kRecB;               // outputs only
-  static constexpr int kBuf = kOut ? kQ + kBufK : kRec + kRecB;
+  static constexpr int kZ = kQ + kBufK;                 // outputs only: the fused norm's gate rows
+  static constexpr int kBuf = kOut ? kZ + kBufK : kRec + kRecB;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
   static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
 };
@@ -58,6 +59,9 @@ template <bool kOut> struct SegCfg {
 __device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 __device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ swz_f(row)); }
 __device__ __forceinline__ int swz_v(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (2 * (row & 7))); }
+// Gate rows of the fused norm: position q ^ (r & 15), so that sixteen consecutive rows read at one
+// 16-byte chunk land on sixteen distinct positions (every bank once).
+__device__ __forceinline__ int swz_z(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (row & 15)); }
 
 
 // 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
@@ -193,8 +197,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
                               (uint32_t)p.NC * kRecB);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + vo_base, vo_bytes);
   // fused gated RMSNorm (outputs only): gate z in o's layout, weights of this lane's columns
-  const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.z ? reinterpret_cast<const __bf16*>(p.z) + vo_base : nullptr,
-                                              p.z ? vo_bytes : 0u);
+  const i32x4 rz = rsrc_words(p.z ? reinterpret_cast<const __bf16*>(p.z) + vo_base : nullptr, p.z ? vo_bytes : 0u);
   f4 nw[NSL];
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl)
@@ -214,6 +217,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       dma16(rk, kq, Bf + Cfg::kK + (R * w + 4 * m) * 256);
       if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
       dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (R * w + 4 * m) * 256);
+      if (kOut && p.z) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
     }
     const uint32_t rec = (uint32_t)c * kRecB + 16 * lane;
     constexpr int nblk = kOut ? 13 : 7;
@@ -268,8 +272,9 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   // token's sum of squares over all 128 columns, i.e. over all waves: every wave leaves its partial
   // sums in LDS (two buffers, by chunk parity) and normalises and stores chunk c - 1 right after
   // the barrier that opens chunk c, so the fusion adds no barrier.
-  f4 Ot[4][NSL];
-  i32x2 zv[4][NSL];
+  // Ot: the chunk's outputs; sz: w silu(z) of the same lanes' elements, formed from the gate rows
+  // staged with the chunk while the chunk computes.
+  f4 Ot[4][NSL], sz[4][NSL];
   const bool fuse = kOut && p.z != nullptr;
   float* part = reinterpret_cast<float*>(lds + 2 * Cfg::kBuf);   // [2][NW][64]
   auto store_o = [&](int c) {
@@ -290,16 +295,9 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       float ss = 0.f;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) ss += pp[ww * C + 16 * mt + n16];
-      const float r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+      const float r = __builtin_amdgcn_rsqf(ss * (1.0f / D) + p.eps);
 #pragma unroll
-      for (int sl = 0; sl < NSL; ++sl) {
-        const bf16x4 zb = __builtin_bit_cast(bf16x4, zv[mt][sl]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float zf = (float)zb[i];
-          Ot[mt][sl][i] = nw[sl][i] * (Ot[mt][sl][i] * r) * (zf * silu_gate(zf));
-        }
-      }
+      for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= sz[mt][sl] * r;
     }
     store_o(c);
   };
@@ -313,19 +311,15 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
   for (int c = c_begin; c < c_end; ++c) {
     // chunk c has landed for every wave, every wave is done with chunk c - 1's buffer, and (fused
-    // norm) chunk c - 1's partial sums are in LDS. Outstanding vector-memory operations issued
-    // after chunk c's loads: chunk c - 1's four output stores, or (fused norm) its four gate loads.
-    wait_and_barrier<Cfg::kStores>();
+    // norm) chunk c - 1's gate rows and partial sums are in LDS. Vector-memory operations issued
+    // after chunk c's loads: chunk c - 1's output stores; none with the fused norm (its stores
+    // come first in the iteration).
+    if (fuse)
+      wait_and_barrier<0>();
+    else
+      wait_and_barrier<Cfg::kStores>();
     if (fuse && c > c_begin) finish_norm(c - 1);
     if (c + 1 < c_end) issue(c + 1);
-    if (fuse) {   // this chunk's gate values, in flight during the chunk's arithmetic
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int sl = 0; sl < NSL; ++sl)
-          zv[mt][sl] = __builtin_amdgcn_raw_buffer_load_b64(
-              rz, ((uint32_t)c * C + 16 * mt + n16) * vo_row + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
-    }
 
     const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const unsigned char* Kt = Bf + Cfg::kK;
@@ -424,7 +418,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
-        if (fuse) {   // this wave's sum of squares of the token's columns: its four lanes, into LDS
+        if (fuse) {
+          // this wave's sum of squares of the token's columns (its four lane groups), into LDS
           float ss = 0.f;
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl)
@@ -433,6 +428,18 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           ss += __shfl_xor(ss, 16);
           ss += __shfl_xor(ss, 32);
           if (G == 0) part[(c & 1) * NW * C + w * C + 16 * mt + n16] = ss;
+          // w silu(z) of this lane's elements, from the gate rows staged with the chunk
+          const unsigned char* Zb = Bf + Cfg::kZ;
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) {
+            const int zrow = 16 * mt + n16, zcol = seg_col<kOut>(w, sl) + 4 * G;
+            const bf16x4 zb = *reinterpret_cast<const bf16x4*>(Zb + swz_z(zrow, zcol >> 3) + 2 * (zcol & 7));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float zf = (float)zb[i];
+              sz[mt][sl][i] = nw[sl][i] * zf * silu_gate(zf);
+            }
+          }
         }
       }
       if (!fuse) store_o(c);
@@ -519,28 +526,40 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   f4 S[2];
   const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
 #pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)   // all loads first: the stores below may alias s0 as far as the
+#pragma unroll                      // compiler knows, which would otherwise serialise them
+    for (int i = 0; i < 4; ++i) S[s2][i] = s0 ? s0[(32 * w + 16 * s2 + 4 * G + i) * D + col] : 0.f;
+#pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 32 * w + 16 * s2 + 4 * G + i;
-      S[s2][i] = s0 ? s0[row * D + col] : 0.f;
-      slots[row * 2 * D + col] = S[s2][i];
-    }
-  for (int jj = 0; jj + 1 < p.P; ++jj) {
+    for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+  // Step jj reads M_jj (this wave's 32 rows, all 128 keys) and the slice of B_jj; neither depends on
+  // the chained state, so step jj + 1's are loaded while step jj computes.
+  f4 Mr[2][4][2], Br[2];
+  auto load_step = [&](int jj) {
     const float* M = slots + jj * kSlotFloats + D;   // M_jj, row pitch 2D
+    const float* Bn = slots + (jj + 1) * kSlotFloats;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float* mrow = M + (32 * w + 16 * s2 + n16) * 2 * D + 32 * kb + 4 * G;
+        Mr[s2][kb][0] = *reinterpret_cast<const f4*>(mrow);
+        Mr[s2][kb][1] = *reinterpret_cast<const f4*>(mrow + 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Br[s2][i] = Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
+    }
+  };
+  if (p.P > 1) load_step(0);
+  for (int jj = 0; jj + 1 < p.P; ++jj) {
     float* Bn = slots + (jj + 1) * kSlotFloats;       // B_jj, replaced by the state entering jj + 1
-    f4 Bv[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Bv[s2][i] = Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
     bf16x8 mh[2][4], ml[2][4];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float* mrow = M + (32 * w + 16 * s2 + n16) * 2 * D + 32 * kb + 4 * G;
-        const f4 m0 = *reinterpret_cast<const f4*>(mrow), m1 = *reinterpret_cast<const f4*>(mrow + 16);
+        const f4 m0 = Mr[s2][kb][0], m1 = Mr[s2][kb][1];
         mh[s2][kb] = pack8(m0, m1);
         f4 r0, r1;
 #pragma unroll
@@ -550,6 +569,8 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
         }
         ml[s2][kb] = pack8(r0, r1);
       }
+    const f4 Bv[2] = {Br[0], Br[1]};
+    if (jj + 2 < p.P) load_step(jj + 1);
     {
       const bf16x8 hi = pack8(S[0], S[1]);
       f4 r0, r1;
@@ -561,7 +582,7 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
       sx[jj & 1][0][w][lane] = hi;
       sx[jj & 1][1][w][lane] = pack8(r0, r1);
     }
-    __syncthreads();
+    lds_barrier();   // the state exchange is in LDS; the loads of the next step stay in flight
     f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
