@@ -3,7 +3,8 @@
 One step = one gdr_prefill call (all its kernels: the per-chunk prep, the segment transitions and
 their combine, the output scan) over the long-prefill workload: B = 1, 16 key / 32 value heads, Dk = Dv = 128, L = 16384,
 bf16 q/k/v, fp32 g/beta/state, zero initial state, final state returned. Inputs, outputs and
-the workspace are resident in HBM before the timed region. Prints one JSON line.
+the workspace are resident in HBM before the timed region. Before the W warm-up steps the step
+runs untimed for 0.3 s so that the GPU's clocks have settled. Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --decode          # one fork decode step instead (gdr_decode, 64 rows x 1 token)
@@ -119,6 +120,19 @@ def copy_probe(nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "reps": reps}))
 
 
+def settle(step, seconds=0.3):
+    """Run the step untimed until `seconds` have passed: the GPU's clocks ramp up over the first
+    tens of milliseconds of load, and the few warm-up steps alone (a few ms) do not get there.
+    Measured on the long prefill: 317-325 us per step right after 10 warm-up steps, 282 us once
+    the clocks have settled; the step's work is the same."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+
+
 def run_timed(step, steps):
     """Time `steps` calls of step(): first with nothing but two events around the loop (the step
     time), then again with the library's per-kernel HIP events on (kernel averages; those events
@@ -159,6 +173,7 @@ def bench_decode(a):
     def step():
         gdr.decode(q, k, v, g, beta, s0=s0, out=o, s_final=s0)
 
+    settle(step)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -215,6 +230,7 @@ def bench_layer(a):
         gdr.conv_silu(t["mixed"], t["conv_w"], Hk, Hv, t["tail"], out=(q, k, v), new_tail=new_tail)
         gdr.gated_rmsnorm(t["x"], t["z"], t["norm_w"], 1e-6, out=y)
 
+    settle(step)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -292,6 +308,7 @@ def main():
     def step():
         gdr.prefill(q, k, v, g, beta, out=o, s_final=s_final, workspace=ws, **fused)
 
+    settle(step)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()

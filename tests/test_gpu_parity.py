@@ -9,8 +9,9 @@ import numpy as np
 import pytest
 import torch
 
+import gated_deltanet_prefill_gdr_amd as gdr
 from workloads import CONFIGS, draw
-from gpu_helpers import TOL, compare, run_gpu, run_oracle, rel_err
+from gpu_helpers import TOL, compare, run_gpu, run_oracle, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -221,3 +222,34 @@ def test_kernel_timing_records_both_kernels():
         gdr.timing_enable(False)
     assert t["gdr_prep"][1] == 2 and t["gdr_scan"][1] == 2
     assert t["gdr_prep"][0] > 0 and t["gdr_scan"][0] > 0
+
+
+def test_graph_capture_replays_equal_eager():
+    # the library launches only kernels (no allocation, no memset), so a call can be captured in a
+    # HIP graph; every replay, with eager work and synchronisations in between, equals the eager call
+    x = draw(1, 1000, 2, 4, 128, "R1", 1201, torch.bfloat16, s0_rows=1)
+    d = to_dev(x)
+    B, L, Hk, Hv, D, Dv = x.shape
+    o = torch.empty(B, L, Hv, Dv, device="cuda", dtype=torch.bfloat16)
+    sf = torch.empty(B, Hv, D, Dv, device="cuda")
+    desc = gdr.make_desc(B, L, Hk, Hv, 1, True, False)
+    ws = torch.empty(gdr.workspace_size(desc), device="cuda", dtype=torch.uint8)
+    step = lambda: gdr.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=d["s0"], out=o, s_final=sf, workspace=ws)
+    step()
+    torch.cuda.synchronize()
+    o_ref, s_ref = o.clone(), sf.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(3):
+        o.zero_()
+        sf.fill_(7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(sf, s_ref), f"replay {i}"
