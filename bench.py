@@ -49,12 +49,13 @@ def algorithmic(B, L, Hk, Hv, esz, n_s0, want_state):
 def kernel_bytes(name, B, L, Hk, Hv, esz, P, fused=False):
     """Bytes a kernel of the path must read and write through its own interface, one launch.
 
-    Intermediates count where they cross HBM: the per-chunk record (T diag(beta) and decayed
-    scores in q's dtype, 4 x 64 fp32 scalars) and the segment slots (128 x 256 fp32 each).
+    Intermediates count where they cross HBM: the per-chunk record (T diag(beta) in q's dtype,
+    for float32 also the decayed scores, then 8 x 64 fp32 scalars) and the segment slots
+    (128 x 256 fp32 each).
     """
     NC = (L + CHUNK - 1) // CHUNK
-    rec = 2 * 6 * 512 * esz + 4 * CHUNK * 4
-    rec_tb = 6 * 512 * esz + 4 * CHUNK * 4          # the part the transitions read
+    rec = (1 if esz == 2 else 2) * 6 * 512 * esz + 8 * CHUNK * 4
+    rec_tb = 6 * 512 * esz + 8 * CHUNK * 4          # the part the transitions read
     slot = D * 2 * D * 4
     qk = B * L * Hk * D * esz
     vo = B * L * Hv * D * esz

@@ -15,17 +15,21 @@ constexpr int kHeadDim = 128;   // Dk = Dv
 // Workspace: one record per (row b, value head h, chunk c), record index (b*Hv + h)*NC + c.
 // A record holds, in the element type of q/k/v,
 //   Tb = T diag(beta')            (T = (I + A)^-1 of the chunk; zero above the diagonal)
-//   P  = (q_hat k_hat^T) (.) E    (decayed causal scores, diagonal included)
+//   P  = (q_hat k_hat^T) (.) E    (decayed causal scores, diagonal included; float32 records
+//                                  only: the bf16 output pass forms P itself from Q and K)
 // each as 6 blocks in MFMA operand order, one block per (token tile w, token block kb) that
 // the lower triangle reaches: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1). A block is 64 lanes x 8
 // elements; lane (m = lane % 16, G = lane / 16) holds row 16w + m, columns
-// 32kb + {4G..4G+3, 16+4G..16+4G+3}. Then 4 x 64 floats: a_t = e^{gamma_t} rk_t,
-// c_t = e^{gamma_t} rq_t, d_t = rk_t e^{gamma_63 - gamma_t}, then e^{gamma_63} at [3][0].
+// 32kb + {4G..4G+3, 16+4G..16+4G+3}. Then the scalar block, 8 x 64 floats: a_t = e^{gamma_t} rk_t,
+// c_t = e^{gamma_t} rq_t, d_t = rk_t e^{gamma_63 - gamma_t}, e^{gamma_63} at [3][0], gamma_t log2(e),
+// rk_t, rq_t, then zeros.
 constexpr int kFragBlocks = 6;
 constexpr int kBlockElems = 64 * 8;
+constexpr int kScalarBytes = 8 * kChunk * 4;
+constexpr int kScA = 0, kScC = 1, kScD = 2, kScEgC = 3, kScGam2 = 4, kScRk = 5, kScRq = 6;   // rows of 64
 
 inline size_t record_bytes(size_t elem) {
-  return 2 * size_t(kFragBlocks) * kBlockElems * elem + 4 * kChunk * sizeof(float);
+  return (elem == 2 ? 1 : 2) * size_t(kFragBlocks) * kBlockElems * elem + kScalarBytes;
 }
 
 // Segments of the bf16 scan. The chunks of each (row, value head) are split into P runs of

@@ -68,13 +68,15 @@ __device__ __forceinline__ void store_acc(float* tile, int n16, int G, const f4&
 __device__ __forceinline__ const float* blk(const float* m, int I, int J) { return m + 16 * I * kFP + 16 * J; }
 __device__ __forceinline__ float* blk(float* m, int I, int J) { return m + 16 * I * kFP + 16 * J; }
 
-// Phase 2 of wave W: the Gram tiles, P into the record (and the scalars for wave 0). Kept a
-// template on W so that every tile choice is fixed at compile time.
+// Phase 2 of wave W: the Gram tiles, and (float32 records) P into the record. Kept a template on W
+// so that every tile choice is fixed at compile time. bf16 records carry no P: the output pass
+// forms it from the Q and K tiles it stages anyway, so only K K^T is formed here.
 template <int W, typename T, int PK>
 __device__ __forceinline__ void gram_phase(const T* ks, const T* qs, const float* gam2, const float* rk,
                                            const float* rq, int n16, int G, int lane, unsigned char* pbase,
                                            f4 (&gk)[4]) {
-  constexpr int Ik = 3 - W, Iq = W;
+  constexpr bool kP = sizeof(T) == 4;
+  constexpr int Ik = 3 - W, Iq = kP ? W : -1;
   f4 gq[4];
 #pragma unroll
   for (int J = 0; J < 4; ++J) {
@@ -84,7 +86,7 @@ __device__ __forceinline__ void gram_phase(const T* ks, const T* qs, const float
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) {
     const Frag<T> ak = lds_frag(ks, PK, 16 * Ik + n16, 32 * kb, G);
-    const Frag<T> bq = lds_frag(qs, PK, 16 * Iq + n16, 32 * kb, G);
+    const Frag<T> bq = lds_frag(qs, PK, 16 * (kP ? Iq : 0) + n16, 32 * kb, G);
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
       if (J > Ik && J > Iq) continue;
@@ -93,6 +95,7 @@ __device__ __forceinline__ void gram_phase(const T* ks, const T* qs, const float
       if (J <= Iq) mma(gq[J], kj, bq);   // (K Q^T)[16 J + 4G + e][16 Iq + n16] = P^T
     }
   }
+  if constexpr (!kP) return;
   // P[t][i], t = 16 Iq + n16, i = 16 J + 4G + e; each lane writes its eight slots of block (Iq, kb)
   const int t = 16 * Iq + n16;
   const float gt = gam2[t], rqt = rq[t];
@@ -164,7 +167,8 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
   int len = p.lengths ? p.lengths[b] : p.L;
   len = len < 0 ? 0 : (len > p.L ? p.L : len);
   constexpr int kMatBytes = kFragBlocks * kBlockElems * (int)sizeof(T);   // Tb (or P) part of a record
-  constexpr int kRecBytes = 2 * kMatBytes + 4 * C * (int)sizeof(float);
+  constexpr int kNumMat = sizeof(T) == 4 ? 2 : 1;                         // Tb, and P for float32
+  constexpr int kRecBytes = kNumMat * kMatBytes + kScalarBytes;
   unsigned char* rec = reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + h) * p.NC + c) * kRecBytes;
   constexpr float kLog2e = 1.4426950408889634f;
 
@@ -252,11 +256,15 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
       const float g2 = sm.gam[lane], g2C = sm.gam[C - 1];
       const float eg = __builtin_amdgcn_exp2f(g2);
       const float rkl = sm.rk[lane], rql = sm.rq[lane];
-      float* sc = reinterpret_cast<float*>(rec + 2 * kMatBytes);
-      sc[lane] = eg * rkl;
-      sc[C + lane] = eg * rql;
-      sc[2 * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
-      sc[3 * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
+      float* sc = reinterpret_cast<float*>(rec + kNumMat * kMatBytes);
+      sc[kScA * C + lane] = eg * rkl;
+      sc[kScC * C + lane] = eg * rql;
+      sc[kScD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
+      sc[kScEgC * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
+      sc[kScGam2 * C + lane] = g2;   // what the output pass needs to form P
+      sc[kScRk * C + lane] = rkl;
+      sc[kScRq * C + lane] = rql;
+      sc[7 * C + lane] = 0.f;
     }
   }
   lds_barrier();   // the staging area becomes A and T

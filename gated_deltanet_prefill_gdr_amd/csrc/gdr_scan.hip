@@ -27,8 +27,9 @@ constexpr int kSlices16 = D / 16;   // 16-column slices of a head
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // ====================================================================== bf16 segment scan
-constexpr int kRecB = 2 * kFragBlocks * kBlockElems * 2 + 4 * C * 4;   // bf16 record bytes (13312)
-constexpr int kScOff = 2 * kFragBlocks * kBlockElems * 2;              // scalars within the record
+constexpr int kScOff = kFragBlocks * kBlockElems * 2;                  // scalars within a bf16 record
+constexpr int kRecB = kScOff + kScalarBytes;                           // bf16 record bytes (8192)
+constexpr int kRecBlocks = kRecB / 1024;                               // 1 KiB loads per record
 constexpr int kBufK = C * D * 2;                                       // one 64x128 bf16 tile
 
 // LDS staging of one chunk (every wave reads every part of it): K, V (and Q) tiles of 64 rows x
@@ -47,6 +48,11 @@ template <bool kOut> struct SegCfg {
   static constexpr int kQ = kRec + kRecB;               // outputs only
   static constexpr int kZ = kQ + kBufK;                 // outputs only: the fused norm's gate rows
   static constexpr int kBuf = kOut ? kZ + kBufK : kRec + kRecB;
+  // outputs only, after the two buffers: P of the current chunk (formed by the waves; one copy,
+  // as it is formed and used between the same two barriers), then the fused norm's row sums
+  static constexpr int kP = 2 * kBuf;
+  static constexpr int kPart = kP + kFragBlocks * 1024;
+  static constexpr int kLds = kOut ? kPart + 2 * NW * C * 4 : 2 * kBuf;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
   static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
 };
@@ -203,9 +209,9 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   for (int sl = 0; sl < NSL; ++sl)
     nw[sl] = (kOut && p.z) ? *reinterpret_cast<const f4*>(p.norm_w + seg_col<kOut>(w, sl) + 4 * G) : f4_splat(0.f);
 
-  // This wave's share of chunk c: K (and Q) and V rows R w .. R w + R - 1 (R = 64 / NW, loads
-  // of four rows each) and the record blocks w, w + NW, ... (outputs: blocks 0..12; transitions:
-  // the Tb blocks 0..5 and the scalar block 12).
+  // This wave's share of chunk c: K (and Q, and the fused norm's gate rows) and V rows
+  // R w .. R w + R - 1 (R = 64 / NW, loads of four rows each) and the 1 KiB record blocks w,
+  // w + NW, ... (the Tb blocks 0..5 and the scalar blocks 6, 7).
   constexpr int R = C / NW;
   auto issue = [&](int c) {
     unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
@@ -220,14 +226,10 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       if (kOut && p.z) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
     }
     const uint32_t rec = (uint32_t)c * kRecB + 16 * lane;
-    constexpr int nblk = kOut ? 13 : 7;
 #pragma unroll
-    for (int i0 = 0; i0 < nblk; i0 += NW) {
+    for (int i0 = 0; i0 < kRecBlocks; i0 += NW) {
       const int i = i0 + w;
-      if (i < nblk) {   // wave-uniform
-        const int blk = (kOut || i < 6) ? i : 12;
-        dma16(rr, rec + 1024 * blk, Bf + Cfg::kRec + 1024 * blk);
-      }
+      if (i < kRecBlocks) dma16(rr, rec + 1024 * i, Bf + Cfg::kRec + 1024 * i);   // wave-uniform
     }
   };
 
@@ -276,7 +278,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   // staged with the chunk while the chunk computes.
   f4 Ot[4][NSL], sz[4][NSL];
   const bool fuse = kOut && p.z != nullptr;
-  float* part = reinterpret_cast<float*>(lds + 2 * Cfg::kBuf);   // [2][NW][64]
+  float* part = reinterpret_cast<float*>(lds + Cfg::kPart);   // [2][NW][64]
   auto store_o = [&](int c) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -326,6 +328,38 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     const unsigned char* Vt = Bf + Cfg::kV;
     const unsigned char* Rc = Bf + Cfg::kRec;
     const float* sc = reinterpret_cast<const float*>(Rc + kScOff);
+
+    // P of this chunk (outputs): waves 0..5 each form one operand block (token tile mt, key block
+    // kb2) from the staged tiles as the tile pair K Q^T (whose accumulator layout is the operand
+    // layout of P), scaled by rq_t rk_i 2^{min(gamma2_t - gamma2_i, 0)} on i <= t and zero above
+    // the diagonal; read after the barrier that precedes the output products.
+    if constexpr (kOut) {
+      if (w < kFragBlocks) {   // wave-uniform
+        const unsigned char* Qt = Bf + Cfg::kQ;
+        const int mt = block_tile(w), kb2 = block_kb(w);
+        f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
+        }
+        const int t = 16 * mt + n16;
+        const float gt = sc[kScGam2 * C + t], rqt = sc[kScRq * C + t];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int i0 = 32 * kb2 + 16 * s2 + 4 * G;
+          const f4 gi = *reinterpret_cast<const f4*>(sc + kScGam2 * C + i0);
+          const f4 ri = *reinterpret_cast<const f4*>(sc + kScRk * C + i0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = rqt * ri[e] * __builtin_amdgcn_exp2f(fminf(gt - gi[e], 0.f)) * pt[s2][e];
+            pt[s2][e] = (i0 + e <= t) ? x : 0.f;
+          }
+        }
+        *reinterpret_cast<bf16x8*>(lds + Cfg::kP + 1024 * w + 16 * lane) = pack8(pt[0], pt[1]);
+      }
+    }
 
     bf16x8 Sop[NSL][4];
 #pragma unroll
@@ -392,6 +426,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // O^T = diag(c) (S^T Q^T) + Delta^T P^T: the accumulator lane (token n16, G) holds the four
     // consecutive columns 4G .. 4G + 3 of one token, stored as one 8-byte write.
     if constexpr (kOut) {
+      lds_barrier();   // P is complete
       const unsigned char* Qt = Bf + Cfg::kQ;
       bf16x8 Dop[NSL][2];
 #pragma unroll
@@ -414,7 +449,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
         for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= cc;
 #pragma unroll
         for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
-          const bf16x8 pf = lds16(Rc + 1024 * (kFragBlocks + frag_block(mt, kb2)) + 16 * lane);
+          const bf16x8 pf = lds16(lds + Cfg::kP + 1024 * frag_block(mt, kb2) + 16 * lane);
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
@@ -491,8 +526,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
 // Outputs: one workgroup per (row, segment, value head), heads fastest.
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
-  // two chunk buffers, then the per-wave row sums of the fused norm (two chunks)
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<true>::kBuf + 2 * SegCfg<true>::NW * C * 4];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % p.P, b = lam / (p.Hv * p.P);
   seg_body<true>(p, lds, b, h, j);
@@ -500,7 +534,7 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
 
 // Transitions: one workgroup per (row, segment < P - 1, value head).
 __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(ScanParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * SegCfg<false>::kBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<false>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
   seg_body<false>(p, lds, b, h, j);
@@ -604,7 +638,7 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
 }
 
 // ====================================================================== fp32 scan
-constexpr int kRecF = 2 * kFragBlocks * kBlockElems * 4 + 4 * C * 4;   // fp32 record bytes (25600)
+constexpr int kRecF = 2 * kFragBlocks * kBlockElems * 4 + kScalarBytes;   // fp32 record bytes (26624)
 constexpr int kPK32 = D + 4, kPT32 = C + 4;
 
 struct ScanSmemF {

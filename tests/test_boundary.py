@@ -83,10 +83,11 @@ def test_valid_calls_pass_host_check():
 
 def test_workspace_size():
     # one record per (row, value head, chunk): the 6 lower-triangle operand blocks (64 lanes x 8)
-    # of the chunk's T diag(beta) and of its decayed causal scores, in q's dtype, plus 4 x 64 floats
-    rec_bf16 = 2 * 6 * 512 * 2 + 4 * 64 * 4
-    rec_f32 = 2 * 6 * 512 * 4 + 4 * 64 * 4
-    assert rec_bf16 == 13312 and rec_f32 == 25600
+    # of the chunk's T diag(beta) (and, for float32, of its decayed causal scores), in q's dtype,
+    # plus 8 x 64 floats of per-token scalars
+    rec_bf16 = 6 * 512 * 2 + 8 * 64 * 4
+    rec_f32 = 2 * 6 * 512 * 4 + 8 * 64 * 4
+    assert rec_bf16 == 8192 and rec_f32 == 26624
     # bf16 sequences are cut into P segments scanned in parallel (P = ceil(256 / (B Hv)) capped
     # by the chunk count, then trimmed so no segment is empty), each with a 128 x 256 fp32 slot
     slot = 128 * 256 * 4
