@@ -128,7 +128,7 @@ def settle(step, seconds=0.3):
     the clocks have settled; the step's work is the same."""
     import torch
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
+    while seconds > 0 and time.perf_counter() - t0 < seconds:
         for _ in range(20):
             step()
         torch.cuda.synchronize()
@@ -174,7 +174,7 @@ def bench_decode(a):
     def step():
         gdr.decode(q, k, v, g, beta, s0=s0, out=o, s_final=s0)
 
-    settle(step)
+    settle(step, a.settle)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -231,7 +231,7 @@ def bench_layer(a):
         gdr.conv_silu(t["mixed"], t["conv_w"], Hk, Hv, t["tail"], out=(q, k, v), new_tail=new_tail)
         gdr.gated_rmsnorm(t["x"], t["z"], t["norm_w"], 1e-6, out=y)
 
-    settle(step)
+    settle(step, a.settle)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -269,6 +269,8 @@ def main():
     ap.add_argument("--rows", type=int, default=64)
     ap.add_argument("--layer", action="store_true")
     ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up (0 for counter runs)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -309,7 +311,7 @@ def main():
     def step():
         gdr.prefill(q, k, v, g, beta, out=o, s_final=s_final, workspace=ws, **fused)
 
-    settle(step)
+    settle(step, a.settle)
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
