@@ -170,9 +170,16 @@ def bench_decode(a):
     torch.cuda.set_device(dev)
     q, k, v, g, beta, s0 = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta, x.s0))
     o = torch.empty(B, L, Hv, D, device=dev, dtype=v.dtype)
+    fused = {}
+    if a.fused:   # raw gate projections in place of g and beta, and the gated RMSNorm of o
+        from workloads import draw_layer
+        y = draw_layer(B, L, 1, Hv, 1, 4343, torch.bfloat16, D=D)
+        fused = {"gates": tuple(t.to(dev) for t in (y.b_raw, y.a_raw, y.A_log, y.dt_bias)),
+                 "norm": (y.x.to(dev), y.norm_w.to(dev), 1e-6)}
+        g = beta = None
 
     def step():
-        gdr.decode(q, k, v, g, beta, s0=s0, out=o, s_final=s0)
+        gdr.decode(q, k, v, g, beta, s0=s0, out=o, s_final=s0, **fused)
 
     settle(step, a.settle)
     for _ in range(a.warmup):
@@ -183,7 +190,8 @@ def bench_decode(a):
     units, nbytes, _ = algorithmic(B, L, Hk, Hv, 2, B, True)
     achieved = nbytes / (k_ms * 1e-3) / 1e9
     line = {
-        "metric": "gated-delta fork decode step tokens·heads/s (64 rows x 1 token, H=32, D=128)",
+        "metric": "gated-delta fork decode step tokens·heads/s (64 rows x 1 token, H=32, D=128)"
+                  + (", gate prologue and gated RMSNorm fused" if a.fused else ""),
         "value": units / (ms * 1e-3), "unit": "tokens·heads/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",

@@ -62,6 +62,8 @@ def library() -> ctypes.CDLL:
     lib.gdr_prefill_ex.argtypes = [ctypes.POINTER(Desc)] + [vp] * 8 + [ctypes.POINTER(Fusion)] + [vp] * 3 + [sz, vp]
     lib.gdr_prefill_ex.restype = i32
     lib.gdr_decode.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10 + [vp]
+    lib.gdr_decode_ex.argtypes = [ctypes.POINTER(Desc)] + [vp] * 8 + [ctypes.POINTER(Fusion)] + [vp] * 2 + [vp]
+    lib.gdr_decode_ex.restype = i32
     lib.gdr_decode.restype = i32
     i64, f32 = ctypes.c_int64, ctypes.c_float
     lib.gdr_gates.argtypes = [i32, i32, i32, i32] + [vp] * 7 + [vp]
@@ -220,6 +222,26 @@ class Fusion(ctypes.Structure):
                 ("norm_eps", ctypes.c_float)]
 
 
+def _fusion(gates, norm, v, dev):
+    """The gdr_fusion struct for gates = (b_raw, a_raw, A_log, dt_bias) and norm = (z, norm_w, eps),
+    or None when neither is given (the gate tensors are checked by _inputs)."""
+    import torch
+    if gates is None and norm is None:
+        return None
+    fu = Fusion()
+    if gates is not None:
+        fu.b_raw, fu.a_raw, fu.A_log, fu.dt_bias = (t.data_ptr() for t in gates)
+    if norm is not None:
+        z, nw, eps = norm
+        if z.shape != v.shape or z.dtype != v.dtype or nw.shape != (v.shape[3],) or nw.dtype != torch.float32:
+            raise ValueError("norm: z must match v's shape and dtype and norm_w be float32 [128]")
+        for name, t in (("z", z), ("norm_w", nw)):
+            if t.device != dev or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+        fu.z, fu.norm_w, fu.norm_eps = z.data_ptr(), nw.data_ptr(), float(eps)
+    return fu
+
+
 def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, norm=None, want_state=True,
             out=None, s_final=None, workspace=None):
     """Run the chunked gated delta rule on torch's current stream; see the module docstring.
@@ -233,19 +255,7 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, n
     """
     import torch
     desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row, gates)
-    fu = None
-    if gates is not None or norm is not None:
-        fu = Fusion()
-        if gates is not None:
-            fu.b_raw, fu.a_raw, fu.A_log, fu.dt_bias = (t.data_ptr() for t in gates)
-        if norm is not None:
-            z, nw, eps = norm
-            if z.shape != v.shape or z.dtype != v.dtype or nw.shape != (Dv,) or nw.dtype != torch.float32:
-                raise ValueError("norm: z must match v's shape and dtype and norm_w be float32 [128]")
-            for name, t in (("z", z), ("norm_w", nw)):
-                if t.device != dev or not t.is_contiguous():
-                    raise ValueError(f"{name} must be a contiguous tensor on {dev}")
-            fu.z, fu.norm_w, fu.norm_eps = z.data_ptr(), nw.data_ptr(), float(eps)
+    fu = _fusion(gates, norm, v, dev)
     need = workspace_size(desc)
     o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
     if want_state and s_final is None:
@@ -263,11 +273,13 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, n
     return o, s_final
 
 
-def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=True, out=None, s_final=None):
-    """The same recurrence token by token (gdr_decode): for short sequences over many rows, with
-    the same arguments and results as prefill and no workspace."""
+def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, norm=None, want_state=True, out=None,
+           s_final=None):
+    """The same recurrence token by token (gdr_decode_ex): for short sequences over many rows, with
+    the same arguments (fused gates / norm included) and results as prefill and no workspace."""
     import torch
-    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row)
+    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row, gates)
+    fu = _fusion(gates, norm, v, dev)
     o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
     if want_state and s_final is None:
         s_final = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
@@ -275,8 +287,9 @@ def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, want_state=Tru
         s_final = None
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
-        st = library().gdr_decode(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                  _ptr(lengths), _ptr(s0), _ptr(s0_row), _ptr(o), _ptr(s_final), stream)
+        st = library().gdr_decode_ex(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(lengths), _ptr(s0), _ptr(s0_row), None if fu is None else ctypes.byref(fu),
+                                     _ptr(o), _ptr(s_final), stream)
     _raise(st)
     return o, s_final
 

@@ -284,15 +284,32 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
 gdr_status gdr_decode(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
                       const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row, void* o,
                       float* s_final, void* stream) {
-  // same validation as gdr_prefill, with no workspace
+  return gdr_decode_ex(d, q, k, v, g, beta, lengths, s0, s0_row, nullptr, o, s_final, stream);
+}
+
+gdr_status gdr_decode_ex(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                         const gdr_fusion* fu, void* o, float* s_final, void* stream) {
+  // same validation as gdr_prefill_ex, with no workspace
   gdr_status st = check_desc(d);
   if (st != GDR_OK) return st;
-  st = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, nullptr, 0, /*need_ws=*/false);
+  st = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, nullptr, 0, /*need_ws=*/false, fu);
   if (st != GDR_OK) return st;
   if (d->B == 0) return GDR_OK;
   if (d->L == 0 && !s_final) return GDR_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   gdr::DecodeParams dp{q, k, v, g, beta, lengths, s0, s0_row, o, s_final, d->B, d->L, d->Hk, d->Hv, s0 ? d->n_s0 : 0};
+  if (fu && fu->b_raw) {
+    dp.b_raw = fu->b_raw;
+    dp.a_raw = fu->a_raw;
+    dp.A_log = fu->A_log;
+    dp.dt_bias = fu->dt_bias;
+  }
+  if (fu && fu->z) {
+    dp.z = fu->z;
+    dp.norm_w = fu->norm_w;
+    dp.eps = fu->norm_eps;
+  }
   hipError_t e = timed(GDR_KERNEL_DECODE, s, [&] {
     return gdr::launch_decode(dp, d->qkv_dtype == GDR_BF16, d->beta_dtype == GDR_BF16, s);
   });

@@ -9,6 +9,10 @@
 // right-pad guard of _dn_gates (beta' = beta [t < len], g' = g [t < len]). The state is read once
 // from s0 (row s0_row[b], the fork model's h0 / h0_idx) and written once to s_final, so the cost
 // is the state traffic plus the token rows: the path is bound by HBM.
+// Optional fused work (the fork layer's order, model.py, _fork_linear_layer): beta, g formed from
+// the raw projections per token (_dn_gates), and the gated RMSNorm of each token's output with its
+// gate z (_gated_rms), so that a decode step reads the raw projections and writes the normalised
+// output.
 #include "gdr_device.h"
 
 namespace gdr {
@@ -17,7 +21,7 @@ template <typename T, typename TB>
 __global__ __launch_bounds__(256) void gdr_decode_kernel(DecodeParams p) {
   __shared__ float qs[D], ks[D];
   __shared__ float part[2][2][D];   // [kv or o][key half][column] partial sums
-  __shared__ float scal[4];         // r_k, r_q of the current token
+  __shared__ float scal[4];         // r_k, r_q of the current token; the norm's two partial sums
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = tid & (D - 1), half = tid >> 7;
   const int h = blockIdx.x % p.Hv, b = blockIdx.x / p.Hv;
@@ -53,8 +57,17 @@ __global__ __launch_bounds__(256) void gdr_decode_kernel(DecodeParams p) {
       qs[tid] = to_f(qg[(tok * p.Hk + kh) * D + tid]);
     }
     const float vn = to_f(vg[(tok * p.Hv + h) * D + n]);
-    const float gv = valid ? p.g[tok * p.Hv + h] : 0.f;
-    const float bv = valid ? to_f(betag[tok * p.Hv + h]) : 0.f;
+    float gv = 0.f, bv = 0.f;
+    if (valid) {
+      if (p.b_raw) {   // fused gate prologue (model.py, _dn_gates)
+        const float x = to_f(reinterpret_cast<const TB*>(p.a_raw)[tok * p.Hv + h]) + p.dt_bias[h];
+        gv = -__expf(p.A_log[h]) * (fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))));
+        bv = __builtin_amdgcn_rcpf(1.0f + __expf(-to_f(reinterpret_cast<const TB*>(p.b_raw)[tok * p.Hv + h])));
+      } else {
+        gv = p.g[tok * p.Hv + h];
+        bv = to_f(betag[tok * p.Hv + h]);
+      }
+    }
     __syncthreads();
     if (wave < 2) {
       const float* x = wave == 0 ? ks : qs;
@@ -84,7 +97,20 @@ __global__ __launch_bounds__(256) void gdr_decode_kernel(DecodeParams p) {
     }
     part[1][half][n] = ov * rq;
     __syncthreads();
-    if (half == 0) og[(tok * p.Hv + h) * D + n] = from_f<T>(part[1][0][n] + part[1][1][n]);
+    float on = part[1][0][n] + part[1][1][n];
+    if (p.z) {   // fused gated RMSNorm: the sum of squares over the 128 outputs (waves 0, 1)
+      if (half == 0) {
+        float s2 = on * on;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) s2 += __shfl_xor(s2, off);
+        if (lane == 0) scal[2 + wave] = s2;
+      }
+      __syncthreads();
+      const float r = 1.0f / sqrtf((scal[2] + scal[3]) * (1.0f / D) + p.eps);
+      const float zf = to_f(reinterpret_cast<const T*>(p.z)[(tok * p.Hv + h) * D + n]);
+      on = p.norm_w[n] * (on * r) * (zf * __builtin_amdgcn_rcpf(1.0f + __expf(-zf)));
+    }
+    if (half == 0) og[(tok * p.Hv + h) * D + n] = from_f<T>(on);
     // the next token's staging waits for every thread's reads of this one
     __syncthreads();
   }

@@ -113,6 +113,15 @@ struct DecodeParams {
   void* o;
   float* s_final;
   int B, L, Hk, Hv, n_s0;
+  // fused gate prologue (null b_raw = g and beta as given), as in PrepParams
+  const void* b_raw;
+  const void* a_raw;
+  const float* A_log;
+  const float* dt_bias;
+  // fused gated RMSNorm of o (null z = plain o), as in ScanParams
+  const void* z;
+  const float* norm_w;
+  float eps;
 };
 
 // Layer steps around the delta rule (gdr_layer.hip).

@@ -177,6 +177,14 @@ gdr_status gdr_conv_silu(int32_t B, int32_t L, int32_t Hk, int32_t Hv, int32_t K
 gdr_status gdr_gated_rmsnorm(int64_t rows, gdr_dtype dtype, const void* x, const void* z, const float* w, float eps,
                              void* out, void* stream);
 
+/* gdr_decode with the same optional fused work as gdr_prefill_ex (fusion may be NULL: then it is
+ * gdr_decode): a decode step of the fork model's layer (model.py, _fork_linear_layer) that reads the
+ * raw gate projections and writes the normalised output. Arguments and errors as gdr_prefill_ex,
+ * without the workspace. */
+gdr_status gdr_decode_ex(const gdr_desc* desc, const void* q, const void* k, const void* v, const float* g,
+                         const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                         const gdr_fusion* fusion, void* o, float* s_final, void* stream);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdr_last_error(void);
 

@@ -326,3 +326,16 @@ def test_prefill_ex_without_fused_gates_still_needs_g_and_beta():
     c = Call()
     fu = fusion(c, gates=False)
     assert prefill_ex(c, fu, g_beta=False) == EINVAL and "non-NULL" in gdr.last_error()
+
+
+def test_decode_ex_validates_fusion_like_prefill_ex():
+    c = Call()
+    fu = fusion(c)
+    lib = gdr.library()
+    ptrs = [x or None for x in c.ptrs()]
+    st = lib.gdr_decode_ex(ctypes.byref(c.desc), *ptrs[:8], ctypes.byref(fu), ptrs[8], ptrs[9], None)
+    assert st == EINVAL and "must be NULL" in gdr.last_error()      # g, beta given with fused gates
+    fu.norm_eps = -1.0
+    ptrs[3] = ptrs[4] = None
+    st = lib.gdr_decode_ex(ctypes.byref(c.desc), *ptrs[:8], ctypes.byref(fu), ptrs[8], ptrs[9], None)
+    assert st == EINVAL and "norm_eps" in gdr.last_error()

@@ -140,3 +140,49 @@ def test_fused_equals_unfused_composition_float32():
     comp = gdr.gated_rmsnorm(o_plain, y.x.cuda(), y.norm_w.cuda(), 1e-6)
     torch.cuda.synchronize()
     assert torch.equal(o, comp)
+
+
+# ---------------------------------------------------------------- gdr_decode_ex
+def run_decode(x, y, gates, norm, eps=1e-6):
+    d = lambda t: None if t is None else t.cuda()
+    kw = {}
+    if gates:
+        kw["gates"] = (d(y.b_raw), d(y.a_raw), d(y.A_log), d(y.dt_bias))
+    if norm:
+        kw["norm"] = (d(y.x).to(x.v.dtype), d(y.norm_w), eps)
+    o, s = gdr.decode(d(x.q), d(x.k), d(x.v), None if gates else d(x.g), None if gates else d(x.beta),
+                      valid=d(x.lengths), s0=d(x.s0), s0_row=d(x.s0_row), **kw)
+    torch.cuda.synchronize()
+    return o, s
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("L", [1, 5, 64])
+def test_fused_decode_vs_oracle(dtype, L):
+    x, y = layer_inputs(3, L, 2, 4, dtype, 1160 + L, lengths=[L, max(L - 2, 0), 0], s0_rows=3)
+    o, s = run_decode(x, y, True, True)
+    o_ref, s_ref = oracle(x, y, True, True)
+    rows = check(o, s, o_ref, s_ref, dtype, f"fused decode L={L} {dtype}")
+    assert rows <= ROW_TOL[dtype]
+
+
+def test_fused_decode_fork_rows():
+    # a decode step of 64 fork rows that all continue one shared state row, both fusions
+    x = draw(64, 1, 16, 32, 128, "R1", 1170, torch.bfloat16, s0_rows=1, s0_row=[0] * 64)
+    y = draw_layer(64, 1, 1, 32, 1, 1171, torch.bfloat16, D=128)
+    o, s = run_decode(x, y, True, True)
+    rows = [0, 17, 63]
+    lens = None
+    beta, g = dn_gates(f64(y.b_raw)[rows], f64(y.a_raw)[rows], f64(y.A_log), f64(y.dt_bias), lens)
+    o_ref, s_ref = gated_delta_rule(f64(x.q)[rows], f64(x.k)[rows], f64(x.v)[rows], g, beta,
+                                    s0=f64(x.s0), s0_row=np.zeros(len(rows), dtype=np.int64))
+    o_ref = gated_rmsnorm(o_ref, f64(y.x)[rows], f64(y.norm_w), 1e-6)
+    check(o[rows], s[rows], o_ref, s_ref, torch.bfloat16, "fused decode fork rows")
+
+
+def test_fused_decode_equals_fused_prefill():
+    # the two entry points compute the same thing; in float32 they agree to accumulated rounding
+    x, y = layer_inputs(2, 70, 1, 2, torch.float32, 1180, lengths=[70, 33], s0_rows=2)
+    o1, s1 = run_decode(x, y, True, True)
+    o2, s2 = run(x, y, True, True)
+    assert rel_err(f64(o1), f64(o2)) <= 1e-5 and rel_err(f64(s1), f64(s2)) <= 1e-5
