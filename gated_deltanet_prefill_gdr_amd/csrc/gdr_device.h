@@ -144,6 +144,38 @@ __device__ __forceinline__ int block_kb(int blk) { return blk < 2 ? 0 : (blk - 2
 // Column (within the 64-token chunk) of slot j of lane group G in token block kb.
 __device__ __forceinline__ int slot_col(int kb, int G, int j) { return 32 * kb + (j < 4 ? 4 * G + j : 12 + 4 * G + j); }
 
+// ---- 64 x 128 bf16 tiles staged in LDS by DMA (256-byte rows, no padding)
+// The 16-byte chunk q of row r sits at position q ^ f(r), f swapping the two 2-bit fields of
+// r mod 16. Sixteen consecutive rows of one chunk (the row operands) and four consecutive rows of
+// four consecutive chunks (the transposing reads) then both land on 16 distinct positions, i.e.
+// on all 64 banks once.
+__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ swz_f(row)); }
+
+// 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
+// range: zeros). Written as inline assembly so that the compiler neither waits for these loads
+// at every barrier nor moves LDS accesses across them; the kernel counts them itself (vmcnt).
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t off, const unsigned char* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  // M0 is not otherwise used by these kernels; one wait state separates its write from the load.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(r)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f4& lo, const f4& hi) {
+  bf16x8 f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = (__bf16)lo[i];
+    f[4 + i] = (__bf16)hi[i];
+  }
+  return f;
+}
+__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
 // Workgroup barrier for waves that exchange data through LDS only: waits for this wave's LDS
 // accesses, not for its global loads and stores (which a plain __syncthreads would also drain),
 // and keeps the compiler from moving memory accesses across it.

@@ -1,7 +1,6 @@
 // Per-chunk transform of the chunked gated delta rule (gfx950).
 //
-// One workgroup (4 waves) per (row b, value head h, chunk c), with key head kh = h / (Hv / Hk).
-// From the chunk's raw q, k, g and beta it forms
+// From a chunk's raw k, g and beta (and q for float32) it forms
 //   rk_t = (|k_t|^2 + 1e-6)^-1/2,  rq_t = (|q_t|^2 + 1e-6)^-1/2 * 128^-1/2   (model page model.py,
 //          function _l2norm, eps inside the rsqrt; q scaled by Dk^-1/2 as in delta_rule_reference)
 //   beta'_t, g'_t with the right-pad guard (model.py, _dn_gates: pads neither write nor decay);
@@ -10,23 +9,34 @@
 //   gamma_t = inclusive cumulative sum of g' within the chunk
 //   A[t][i] = beta'_t e^{gamma_t - gamma_i} rk_t rk_i (k_t . k_i)   (i < t)
 //   T = (I + A)^-1, Tb = T diag(beta'),  P[t][i] = rq_t rk_i e^{gamma_t - gamma_i} (q_t . k_i)  (i <= t)
-// and writes the chunk record: Tb and P as MFMA operand blocks (lower triangle only), then the
-// per-token scalars a = e^gamma rk, c = e^gamma rq, d = rk e^{gamma_63 - gamma} and e^{gamma_63}.
+// and writes the chunk record: Tb (and for float32 P) as MFMA operand blocks (lower triangle
+// only), then the per-token scalars a = e^gamma rk, d = rk e^{gamma_63 - gamma}, e^{gamma_63},
+// gamma log2 e and rk (float32 also c = e^gamma rq and rq).
 // Exponents are only taken of non-positive differences on the kept triangle ("direct" decay
 // from in-chunk differences), so nothing over- or underflows however strong the decay.
 //
+// bf16 (gdr_prep_keyhead): persistent workgroups, each walking work items (row b, key head kh,
+// chunk c) with the next item's K rows and gates loaded into registers while the current item
+// computes. The Gram K K^T is formed once per item and shared by the Hv / Hk value heads of the
+// key head, each of which then gets its own A, inverse and record. q is not read: the output
+// pass forms the q norms from the Q tile it stages anyway.
+//
+// float32 (gdr_prep): one workgroup (4 waves) per (row b, value head h, chunk c).
+//
 // Phases (one barrier each; the waves exchange data through LDS only, so the barriers do not
 // wait for the global stores of the record):
-//   1. stage q, k rows in LDS, row norms, gates and gamma;
+//   1. stage k (and q) rows in LDS, row norms, gates and gamma;
 //   2. Gram tiles on MFMA, balanced over the waves: wave w forms the K K^T tiles of row 3 - w and
-//      the K Q^T tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator layout is
-//      exactly the operand layout of P, so P goes from registers straight to the record;
+//      (float32) the K Q^T tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator
+//      layout is exactly the operand layout of P, so P goes from registers straight to the record;
 //   3. A (fp32) into LDS over the staging area;
 //   4. T of the four 16x16 diagonal blocks by forward substitution, one lane per column, all in
 //      registers (wave 0);
 //   5. off-diagonal blocks by the 2x2 block rule T_BA = -T_BB A_BA T_AA, first within each
 //      32-row half (T_10, T_32), then across the halves, on fp32 MFMA;
 //   6. Tb = T diag(beta') gathered into operand order.
+#include <algorithm>
+
 #include "gdr_device.h"
 
 namespace gdr {
@@ -143,6 +153,112 @@ __device__ __forceinline__ void a_phase(float* A, const float* gam2, const float
       const int row = 16 * I + 4 * G + e;
       const float x = br[e] * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * rr[e] * rc * gk[J][e];
       A[row * kFP + col] = row > col ? x : 0.f;
+    }
+  }
+}
+
+// Phases 3-6 for one value head: A from the Gram tiles gk of this wave (row 3 - wave), the
+// blocked inverse in Amat / Tmat (64 x kFP floats each), and Tb into the record at rec. Four
+// barriers; on return every wave may still be reading Tmat (phase 6), so Amat may be rewritten
+// at once but Tmat only after a barrier.
+template <typename T>
+__device__ __forceinline__ void inverse_to_record(float* Amat, float* Tmat, const float* gam, const float* rk,
+                                                  const float* bet, const f4 (&gk)[4], int wave, int n16, int G,
+                                                  int lane, unsigned char* rec) {
+  // ---- 3. A, strictly lower, fp32
+  switch (wave) {
+    case 0: a_phase<0>(Amat, gam, rk, bet, n16, G, gk); break;
+    case 1: a_phase<1>(Amat, gam, rk, bet, n16, G, gk); break;
+    case 2: a_phase<2>(Amat, gam, rk, bet, n16, G, gk); break;
+    default: a_phase<3>(Amat, gam, rk, bet, n16, G, gk); break;
+  }
+  lds_barrier();
+
+  // ---- 4. diagonal blocks: lane 16 w' + j solves column j of block w' (wave 0), column k of the
+  //         block read from LDS at step k (one address per block, broadcast over its 16 lanes)
+  if (wave == 0) {
+    const int o = 16 * G, j = n16;
+    const float* ablk = Amat + o * kFP + o;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+    for (int k = 0; k < 15; ++k) {
+#pragma unroll
+      for (int i = k + 1; i < 16; ++i) x[i] -= ablk[i * kFP + k] * x[k];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Tmat[(o + i) * kFP + o + j] = x[i];
+  }
+  lds_barrier();
+
+  // ---- 5. off-diagonal blocks. Within each 32-row half: T_10 = -T_11 A_10 T_00 (wave 0),
+  //         T_32 = -T_33 A_32 T_22 (wave 1); waves 2, 3 meanwhile form A_20 T_00, A_30 T_00.
+  //         Across the halves (T_IJ for I in {2,3}, J in {0,1}), with Z = A_[23][01] T_[01][01]:
+  //         T_2J = -T_22 Z_2J, T_3J = -(T_32 Z_2J + T_33 Z_3J); wave 2: T_20, wave 3: T_30,
+  //         wave 0: T_21, wave 1: T_31.
+  const float* Am = Amat;
+  float* Tm = Tmat;
+  f4 pre0 = f4_splat(0.f), pre1 = f4_splat(0.f);
+  if (wave < 2) {
+    const int I = 2 * wave + 1, J = 2 * wave;   // (1, 0) or (3, 2)
+    f4 x = f4_splat(0.f);
+    mma_lds_acc(x, blk(Am, I, J), n16, G, tile_acc(blk(Tm, J, J), n16, G));
+    f4 y = f4_splat(0.f);
+    mma_lds_acc(y, blk(Tm, I, I), n16, G, x);
+    store_acc(blk(Tm, I, J), n16, G, -y);
+  } else {
+    const f4 t00 = tile_acc(blk(Tm, 0, 0), n16, G);
+    mma_lds_acc(pre0, blk(Am, 2, 0), n16, G, t00);            // A_20 T_00
+    if (wave == 3) mma_lds_acc(pre1, blk(Am, 3, 0), n16, G, t00);   // A_30 T_00
+  }
+  lds_barrier();
+  {
+    const int J = (wave >= 2) ? 0 : 1;
+    const bool row3 = (wave & 1) != 0;   // waves 1, 3 produce row 3
+    const f4 tj1 = tile_acc(blk(Tm, 1, J), n16, G);   // T_10 (J = 0) or T_11 (J = 1)
+    f4 z2 = pre0;                                      // Z_2J = A_20 T_0J + A_21 T_1J (T_01 = 0)
+    mma_lds_acc(z2, blk(Am, 2, 1), n16, G, tj1);
+    f4 out = f4_splat(0.f);
+    if (!row3) {
+      mma_lds_acc(out, blk(Tm, 2, 2), n16, G, z2);
+      store_acc(blk(Tm, 2, J), n16, G, -out);
+    } else {
+      f4 z3 = pre1;                                    // Z_3J = A_30 T_0J + A_31 T_1J
+      mma_lds_acc(z3, blk(Am, 3, 1), n16, G, tj1);
+      mma_lds_acc(out, blk(Tm, 3, 2), n16, G, z2);
+      mma_lds_acc(out, blk(Tm, 3, 3), n16, G, z3);
+      store_acc(blk(Tm, 3, J), n16, G, -out);
+    }
+  }
+  lds_barrier();
+
+  // ---- 6. Tb = T diag(beta') in operand order (zero above the diagonal): wave w writes blocks
+  //         w and w + 4; lane (m, g) of block (tile I, kb) holds row 16 I + m, columns
+  //         32 kb + 4g + {0..3} and 32 kb + 16 + 4g + {0..3}
+#pragma unroll
+  for (int i2 = 0; i2 < 2; ++i2) {
+    const int bk = wave + 4 * i2;
+    if (bk < kFragBlocks) {
+      const int row = 16 * block_tile(bk) + n16, c0 = 32 * block_kb(bk) + 4 * G;
+      const f4 t_lo = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0]);
+      const f4 t_hi = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0 + 16]);
+      const f4 b_lo = *reinterpret_cast<const f4*>(&bet[c0]);
+      const f4 b_hi = *reinterpret_cast<const f4*>(&bet[c0 + 16]);
+      f4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = (c0 + e <= row) ? t_lo[e] * b_lo[e] : 0.f;
+        hi[e] = (c0 + 16 + e <= row) ? t_hi[e] * b_hi[e] : 0.f;
+      }
+      const Frag<T> f = acc_frag<T>(lo, hi, f4_splat(1.f), f4_splat(1.f));
+      unsigned char* dst = rec + (size_t)bk * kBlockElems * sizeof(T) + (size_t)lane * 8 * sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x8*>(dst) = f.v;
+      } else {
+        *reinterpret_cast<f4*>(dst) = f4{f.v[0], f.v[1], f.v[2], f.v[3]};
+        *reinterpret_cast<f4*>(dst + 16) = f4{f.v[4], f.v[5], f.v[6], f.v[7]};
+      }
     }
   }
 }
@@ -269,117 +385,217 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
   }
   lds_barrier();   // the staging area becomes A and T
 
-  // ---- 3. A, strictly lower, fp32
-  switch (wave) {
-    case 0: a_phase<0>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
-    case 1: a_phase<1>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
-    case 2: a_phase<2>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
-    default: a_phase<3>(sm.u.m.a, sm.gam, sm.rk, sm.bet, n16, G, gk); break;
-  }
-  lds_barrier();
+  inverse_to_record<T>(sm.u.m.a, sm.u.m.t, sm.gam, sm.rk, sm.bet, gk, wave, n16, G, lane, rec);
+}
 
-  // ---- 4. diagonal blocks: lane 16 w' + j solves column j of block w' (wave 0); the block's
-  //         rows are read into registers first (16-byte reads, broadcast over the block's lanes)
-  if (wave == 0) {
-    const int o = 16 * G, j = n16;
-    f4 arow[16][4];
-#pragma unroll
-    for (int i = 1; i < 16; ++i)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        if (4 * s4 < i) arow[i][s4] = *reinterpret_cast<const f4*>(&sm.u.m.a[(o + i) * kFP + o + 4 * s4]);
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-    for (int k = 0; k < 15; ++k) {
-#pragma unroll
-      for (int i = k + 1; i < 16; ++i) x[i] -= arow[i][k >> 2][k & 3] * x[k];
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.u.m.t[(o + i) * kFP + o + j] = x[i];
-  }
-  lds_barrier();
+// ====================================================================== bf16: per key head, persistent
+// LDS of the key-head prep: the K tile (swizzled 256-byte rows, written by DMA), and A and T.
+struct PrepKhSmem {
+  unsigned char k[C * 256];
+  float a[C * kFP], t[C * kFP];
+  float rk[C];
+  float gam[4][C], bet[4][C];   // gates of up to four value heads (one batch of the key head's)
+};
 
-  // ---- 5. off-diagonal blocks. Within each 32-row half: T_10 = -T_11 A_10 T_00 (wave 0),
-  //         T_32 = -T_33 A_32 T_22 (wave 1); waves 2, 3 meanwhile form A_20 T_00, A_30 T_00.
-  //         Across the halves (T_IJ for I in {2,3}, J in {0,1}), with Z = A_[23][01] T_[01][01]:
-  //         T_2J = -T_22 Z_2J, T_3J = -(T_32 Z_2J + T_33 Z_3J); wave 2: T_20, wave 3: T_30,
-  //         wave 0: T_21, wave 1: T_31.
-  const float* Am = sm.u.m.a;
-  float* Tm = sm.u.m.t;
-  f4 pre0 = f4_splat(0.f), pre1 = f4_splat(0.f);
-  if (wave < 2) {
-    const int I = 2 * wave + 1, J = 2 * wave;   // (1, 0) or (3, 2)
-    f4 x = f4_splat(0.f);
-    mma_lds_acc(x, blk(Am, I, J), n16, G, tile_acc(blk(Tm, J, J), n16, G));
-    f4 y = f4_splat(0.f);
-    mma_lds_acc(y, blk(Tm, I, I), n16, G, x);
-    store_acc(blk(Tm, I, J), n16, G, -y);
+// Gates of value head hr of an item's key head at this lane's token, in two steps so that the loads
+// of the next item stay in flight while the current one computes: gates_issue loads the raw words
+// (range-checked: tokens past L read zeros, and nothing waits on them), gates_finish applies the
+// right-pad guard and, with the fused gate prologue, forms beta = sigmoid(b_raw) and
+// g = -exp(A_log) softplus(a_raw + dt_bias) (model.py, _dn_gates).
+struct GateRaw {
+  uint32_t x0, x1;   // g or a_raw, beta or b_raw (raw bits)
+  int len, h, t;
+};
+template <typename TB>
+__device__ __forceinline__ GateRaw gates_issue(const PrepParams& p, int b, int kh, int c, int hr, int lane) {
+  GateRaw gr;
+  gr.h = kh * (p.Hv / p.Hk) + hr;
+  gr.t = c * C + lane;
+  gr.len = p.lengths ? p.lengths[b] : p.L;
+  const size_t row0 = (size_t)b * p.L * p.Hv;
+  const uint32_t n = (uint32_t)p.L * p.Hv;   // elements of one batch row
+  const uint32_t e = (uint32_t)gr.t * p.Hv + gr.h;
+  const void* p0 = p.b_raw ? p.a_raw : static_cast<const void*>(p.g);
+  const void* p1 = p.b_raw ? p.b_raw : p.beta;
+  const bool w0 = p.b_raw != nullptr && sizeof(TB) == 2;   // element width 2 for raw projections in bf16
+  if (w0) {
+    gr.x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(make_rsrc(static_cast<const TB*>(p0) + row0, 2 * n), 2 * e, 0, 0);
   } else {
-    const f4 t00 = tile_acc(blk(Tm, 0, 0), n16, G);
-    mma_lds_acc(pre0, blk(Am, 2, 0), n16, G, t00);            // A_20 T_00
-    if (wave == 3) mma_lds_acc(pre1, blk(Am, 3, 0), n16, G, t00);   // A_30 T_00
+    gr.x0 = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(static_cast<const float*>(p0) + row0, 4 * n), 4 * e, 0, 0);
   }
-  lds_barrier();
-  {
-    const int J = (wave >= 2) ? 0 : 1;
-    const bool row3 = (wave & 1) != 0;   // waves 1, 3 produce row 3
-    const f4 tj1 = tile_acc(blk(Tm, 1, J), n16, G);   // T_10 (J = 0) or T_11 (J = 1)
-    f4 z2 = pre0;                                      // Z_2J = A_20 T_0J + A_21 T_1J (T_01 = 0)
-    mma_lds_acc(z2, blk(Am, 2, 1), n16, G, tj1);
-    f4 out = f4_splat(0.f);
-    if (!row3) {
-      mma_lds_acc(out, blk(Tm, 2, 2), n16, G, z2);
-      store_acc(blk(Tm, 2, J), n16, G, -out);
-    } else {
-      f4 z3 = pre1;                                    // Z_3J = A_30 T_0J + A_31 T_1J
-      mma_lds_acc(z3, blk(Am, 3, 1), n16, G, tj1);
-      mma_lds_acc(out, blk(Tm, 3, 2), n16, G, z2);
-      mma_lds_acc(out, blk(Tm, 3, 3), n16, G, z3);
-      store_acc(blk(Tm, 3, J), n16, G, -out);
-    }
+  if constexpr (sizeof(TB) == 2)
+    gr.x1 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(make_rsrc(static_cast<const TB*>(p1) + row0, 2 * n), 2 * e, 0, 0);
+  else
+    gr.x1 = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(static_cast<const float*>(p1) + row0, 4 * n), 4 * e, 0, 0);
+  return gr;
+}
+template <typename TB>
+__device__ __forceinline__ void gates_finish(const PrepParams& p, const GateRaw& gr, float& gv, float& bv) {
+  const int len = gr.len < 0 ? 0 : (gr.len > p.L ? p.L : gr.len);
+  auto as_f = [](uint32_t x, bool half) {
+    return half ? __builtin_bit_cast(float, x << 16) : __builtin_bit_cast(float, x);   // bf16 -> fp32 is a shift
+  };
+  const bool half1 = sizeof(TB) == 2;
+  const bool half0 = p.b_raw != nullptr && half1;
+  const float x0 = as_f(gr.x0, half0), x1 = as_f(gr.x1, half1);
+  if (p.b_raw) {
+    const float x = x0 + p.dt_bias[gr.h];
+    const float sp = fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));   // softplus without overflow
+    gv = -__expf(p.A_log[gr.h]) * sp;
+    bv = __builtin_amdgcn_rcpf(1.0f + __expf(-x1));
+  } else {
+    gv = x0;
+    bv = x1;
   }
-  lds_barrier();
+  if (gr.t >= len) gv = bv = 0.f;
+}
 
-  // ---- 6. Tb = T diag(beta') in operand order (zero above the diagonal): wave w writes blocks
-  //         w and w + 4; lane (m, g) of block (tile I, kb) holds row 16 I + m, columns
-  //         32 kb + 4g + {0..3} and 32 kb + 16 + 4g + {0..3}
+// Inclusive cumulative sum of the gates over the wave's 64 lanes (tokens), in base 2, into LDS.
+__device__ __forceinline__ void store_gates(float* gam, float* bet, float gv, float bv, int lane) {
+  float x = gv;
 #pragma unroll
-  for (int i2 = 0; i2 < 2; ++i2) {
-    const int bk = wave + 4 * i2;
-    if (bk < kFragBlocks) {
-      const int row = 16 * block_tile(bk) + n16, c0 = 32 * block_kb(bk) + 4 * G;
-      const f4 t_lo = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0]);
-      const f4 t_hi = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0 + 16]);
-      const f4 b_lo = *reinterpret_cast<const f4*>(&sm.bet[c0]);
-      const f4 b_hi = *reinterpret_cast<const f4*>(&sm.bet[c0 + 16]);
-      f4 lo, hi;
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  gam[lane] = x * 1.4426950408889634f;   // e^{u - v} = 2^{(u - v) log2 e}
+  bet[lane] = bv;
+}
+
+// Gram tiles K K^T of row Ik = 3 - W from the swizzled K tile: gk[J][e] = (K K^T)[16 Ik + 4G + e][16 J + n16].
+// Both operands are 16-byte row reads (key 32 kb + 8G + e in slot e of lane group G).
+template <int W>
+__device__ __forceinline__ void gram_kk(const unsigned char* kt, int n16, int G, f4 (&gk)[4]) {
+  constexpr int Ik = 3 - W;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = (c0 + e <= row) ? t_lo[e] * b_lo[e] : 0.f;
-        hi[e] = (c0 + 16 + e <= row) ? t_hi[e] * b_hi[e] : 0.f;
-      }
-      const Frag<T> f = acc_frag<T>(lo, hi, f4_splat(1.f), f4_splat(1.f));
-      unsigned char* dst = rec + (size_t)bk * kBlockElems * sizeof(T) + (size_t)lane * 8 * sizeof(T);
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x8*>(dst) = f.v;
-      } else {
-        *reinterpret_cast<f4*>(dst) = f4{f.v[0], f.v[1], f.v[2], f.v[3]};
-        *reinterpret_cast<f4*>(dst + 16) = f4{f.v[4], f.v[5], f.v[6], f.v[7]};
-      }
-    }
+  for (int J = 0; J < 4; ++J) gk[J] = f4_splat(0.f);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bf16x8 a = lds16(kt + swz(16 * Ik + n16, 4 * kb + G));
+#pragma unroll
+    for (int J = 0; J <= Ik; ++J) gk[J] = mfma(a, lds16(kt + swz(16 * J + n16, 4 * kb + G)), gk[J]);
   }
 }
 
+// Work item it = ((b NC) + c) Hk + kh: items of one chunk and neighbouring key heads read
+// neighbouring 256-byte pieces of the same k rows. The next item's K tile is copied HBM -> LDS
+// (the waves' DMA, issued once the current Gram is formed) while the current item's inverses run.
+template <typename TB>
+__global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int items) {
+  __shared__ __attribute__((aligned(16))) PrepKhSmem sm;
+  constexpr int kRecBytes = kFragBlocks * kBlockElems * 2 + kScalarBytes;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, G = lane >> 4;
+  const int r = p.Hv / p.Hk;
+  const uint32_t row_bytes = (uint32_t)p.Hk * D * 2;
+
+  // This wave's quarter of item it's K tile: rows 16 wave .. 16 wave + 15, four DMA loads of four rows.
+  auto issue_k = [&](int it) {
+    const int kh = it % p.Hk, c = (it / p.Hk) % p.NC, b = it / (p.Hk * p.NC);
+    const i32x4 rk = rsrc_words(reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.L * p.Hk * D,
+                                (uint32_t)p.L * row_bytes);   // rows past L read as zeros
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int row = 16 * wave + 4 * m + (lane >> 4), pos = lane & 15;
+      dma16(rk, (uint32_t)(c * C + row) * row_bytes + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(row)),
+            sm.k + (16 * wave + 4 * m) * 256);
+    }
+  };
+
+  int it = blockIdx.x;
+  GateRaw graw{};   // raw gates of value head `wave` of item it (first batch of four), in flight
+  if (it < items) {
+    issue_k(it);
+    if (wave < r) graw = gates_issue<TB>(p, it / (p.Hk * p.NC), it % p.Hk, (it / p.Hk) % p.NC, wave, lane);
+  }
+  for (; it < items; it += gridDim.x) {
+    const int kh = it % p.Hk, c = (it / p.Hk) % p.NC, b = it / (p.Hk * p.NC);
+    // this wave's part of the K tile (and its gates) have landed; every wave is done with the
+    // previous item's A, T and gates
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+
+    // ---- 1-2. gates of the first (up to) four value heads; Gram tiles of row 3 - wave; rk from
+    //           the Gram diagonal, rk_t = (|k_t|^2 + 1e-6)^-1/2 (model.py, _l2norm)
+    if (wave < r) {
+      float gv, bv;
+      gates_finish<TB>(p, graw, gv, bv);
+      store_gates(sm.gam[wave], sm.bet[wave], gv, bv, lane);
+    }
+    f4 gk[4];
+    switch (wave) {
+      case 0: gram_kk<0>(sm.k, n16, G, gk); break;
+      case 1: gram_kk<1>(sm.k, n16, G, gk); break;
+      case 2: gram_kk<2>(sm.k, n16, G, gk); break;
+      default: gram_kk<3>(sm.k, n16, G, gk); break;
+    }
+    {
+      const int Ik = 3 - wave, e = n16 & 3;   // diagonal element (16 Ik + n16, 16 Ik + n16): lane group n16 / 4
+      const f4 dg = gk[Ik];
+      const float ss = e == 0 ? dg[0] : e == 1 ? dg[1] : e == 2 ? dg[2] : dg[3];
+      if ((n16 >> 2) == G) sm.rk[16 * Ik + n16] = 1.0f / sqrtf(ss + 1e-6f);
+    }
+    lds_barrier();   // the K tile is free, gates and rk are in LDS
+
+    // the next item's K tile and gates, while this item's inverses run
+    const int nx = it + gridDim.x;
+    if (nx < items) {
+      issue_k(nx);
+      if (wave < r) graw = gates_issue<TB>(p, nx / (p.Hk * p.NC), nx % p.Hk, (nx / p.Hk) % p.NC, wave, lane);
+    }
+
+    // ---- 3-6 for each value head of the key head
+    for (int hb = 0; 4 * hb < r; ++hb) {
+      if (hb > 0) {   // more than four value heads per key head: the next batch's gates, read now
+        float g2 = 0.f, b2 = 0.f;
+        if (4 * hb + wave < r) gates_finish<TB>(p, gates_issue<TB>(p, b, kh, c, 4 * hb + wave, lane), g2, b2);
+        lds_barrier();   // the previous batch's gates are no longer read
+        if (4 * hb + wave < r) store_gates(sm.gam[wave], sm.bet[wave], g2, b2, lane);
+        lds_barrier();
+      }
+      for (int j = 0; j < 4 && 4 * hb + j < r; ++j) {
+        const int h = kh * r + 4 * hb + j;
+        unsigned char* rec = reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + h) * p.NC + c) * kRecBytes;
+        if (wave == 3) {   // scalars (rows c and rq are not used by bf16 records)
+          const float g2 = sm.gam[j][lane], g2C = sm.gam[j][C - 1], rkl = sm.rk[lane];
+          float* sc = reinterpret_cast<float*>(rec + kFragBlocks * kBlockElems * 2);
+          sc[kScA * C + lane] = __builtin_amdgcn_exp2f(g2) * rkl;
+          sc[kScD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
+          sc[kScEgC * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
+          sc[kScGam2 * C + lane] = g2;
+          sc[kScRk * C + lane] = rkl;
+        }
+        inverse_to_record<__bf16>(sm.a, sm.t, sm.gam[j], sm.rk, sm.bet[j], gk, wave, n16, G, lane, rec);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA into LDS may be in flight at the end
+}
+
+// Workgroups of the persistent prep: three per compute unit of the current device (what fits).
+static int prep_workgroups() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  int* slot = dev < 64 ? &cache[dev] : nullptr;
+  if (slot && *slot > 0) return *slot;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (slot) *slot = 3 * cus;
+  return 3 * cus;
+}
+
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s) {
-  const dim3 grid(p.B * p.Hv * p.NC);
   if (qkv_bf16) {
+    const int64_t items = int64_t(p.B) * p.Hk * p.NC;   // <= B Hv NC < 2^31 (checked by the caller)
+    const dim3 grid((unsigned)std::min<int64_t>(items, prep_workgroups()));
     if (beta_bf16)
-      hipLaunchKernelGGL((gdr_prep<__bf16, __bf16>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gdr_prep_keyhead<__bf16>), grid, dim3(256), 0, s, p, (int)items);
     else
-      hipLaunchKernelGGL((gdr_prep<__bf16, float>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gdr_prep_keyhead<float>), grid, dim3(256), 0, s, p, (int)items);
   } else {
+    const dim3 grid(p.B * p.Hv * p.NC);
     hipLaunchKernelGGL((gdr_prep<float, float>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();

@@ -49,36 +49,23 @@ template <bool kOut> struct SegCfg {
   static constexpr int kZ = kQ + kBufK;                 // outputs only: the fused norm's gate rows
   static constexpr int kBuf = kOut ? kZ + kBufK : kRec + kRecB;
   // outputs only, after the two buffers: P of the current chunk (formed by the waves; one copy,
-  // as it is formed and used between the same two barriers), then the fused norm's row sums
+  // as it is formed and used between the same two barriers), the fused norm's row sums, and the
+  // partial sums of squares of the chunk's q rows (formed and used between the same two barriers)
   static constexpr int kP = 2 * kBuf;
   static constexpr int kPart = kP + kFragBlocks * 1024;
-  static constexpr int kLds = kOut ? kPart + 2 * NW * C * 4 : 2 * kBuf;
+  static constexpr int kRq = kPart + 2 * NW * C * 4;    // outputs only: q sums of squares, 4 per token
+  static constexpr int kLds = kOut ? kRq + 4 * C * 4 : 2 * kBuf;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
   static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
 };
 
-// K and Q tiles: the 16-byte chunk q of row r sits at position q ^ f(r), f swapping the two
-// 2-bit fields of r mod 16. Sixteen consecutive rows of one chunk (the row operands) and four
-// consecutive rows of four consecutive chunks (the transposing reads) then both land on 16
-// distinct positions, i.e. on all 64 banks once. V tiles: position q ^ 2(r & 7), which keeps the
-// two chunks of eight consecutive rows read together apart.
-__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
-__device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ swz_f(row)); }
+// K and Q tiles use the row swizzle swz of the device header. V tiles: position q ^ 2(r & 7), which
+// keeps the two chunks of eight consecutive rows read together apart.
 __device__ __forceinline__ int swz_v(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (2 * (row & 7))); }
 // Gate rows of the fused norm: position q ^ (r & 15), so that sixteen consecutive rows read at one
 // 16-byte chunk land on sixteen distinct positions (every bank once).
 __device__ __forceinline__ int swz_z(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ (row & 15)); }
 
-
-// 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
-// range: zeros). Written as inline assembly so that the compiler neither waits for these loads
-// at every barrier nor moves LDS accesses across them; the kernel counts them itself (vmcnt).
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t off, const unsigned char* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  // M0 is not otherwise used by these kernels; one wait state separates its write from the load.
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(r)
-               : "memory", "m0");
-}
 
 // Wait until at most N vector-memory operations of this wave are outstanding and all of its
 // LDS accesses are done, then meet the other waves. Memory clobbers keep every LDS access on
@@ -90,19 +77,6 @@ template <int N> __device__ __forceinline__ void wait_and_barrier() {
   else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ bf16x8 pack8(const f4& lo, const f4& hi) {
-  bf16x8 f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[i] = (__bf16)lo[i];
-    f[4 + i] = (__bf16)hi[i];
-  }
-  return f;
-}
-__device__ __forceinline__ f4 mfma(const bf16x8& a, const bf16x8& b, const f4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x8 lds16(const unsigned char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 // 1 / (1 + e^-x) with the hardware exp2 and reciprocal
 __device__ __forceinline__ float silu_gate(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
@@ -329,23 +303,34 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     const unsigned char* Rc = Bf + Cfg::kRec;
     const float* sc = reinterpret_cast<const float*>(Rc + kScOff);
 
-    // P of this chunk (outputs): waves 0..5 each form one operand block (token tile mt, key block
+    // P' of this chunk (outputs): waves 0..5 each form one operand block (token tile mt, key block
     // kb2) from the staged tiles as the tile pair K Q^T (whose accumulator layout is the operand
-    // layout of P), scaled by rq_t rk_i 2^{min(gamma2_t - gamma2_i, 0)} on i <= t and zero above
-    // the diagonal; read after the barrier that precedes the output products.
+    // layout of P'), scaled by rk_i 2^{min(gamma2_t - gamma2_i, 0)} on i <= t and zero above the
+    // diagonal; read after the barrier that precedes the output products. The q norm of token t,
+    // rq_t = (|q_t|^2 + 1e-6)^-1/2 128^-1/2 (model page model.py, _l2norm), is a factor of both
+    // output terms of row t (O = diag(rq) (diag(e^gamma) Q S + P' Delta)), so it is applied to the
+    // finished row. Its sum of squares comes from the same Q reads: in the waves with kb2 = 0 (one
+    // per token tile) each lane adds its 32 of the token's 128 values and leaves the partial sum
+    // in LDS, four per token, summed by the output step.
+    float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // [64 tokens][4 partial sums]
     if constexpr (kOut) {
       if (w < kFragBlocks) {   // wave-uniform
         const unsigned char* Qt = Bf + Cfg::kQ;
         const int mt = block_tile(w), kb2 = block_kb(w);
         f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)};
+        float qss = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
+          if (kb2 == 0)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qss += (float)qf[e] * (float)qf[e];
         }
+        if (kb2 == 0) rqs[4 * (16 * mt + n16) + G] = qss;
         const int t = 16 * mt + n16;
-        const float gt = sc[kScGam2 * C + t], rqt = sc[kScRq * C + t];
+        const float gt = sc[kScGam2 * C + t];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int i0 = 32 * kb2 + 16 * s2 + 4 * G;
@@ -353,7 +338,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           const f4 ri = *reinterpret_cast<const f4*>(sc + kScRk * C + i0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x = rqt * ri[e] * __builtin_amdgcn_exp2f(fminf(gt - gi[e], 0.f)) * pt[s2][e];
+            const float x = ri[e] * __builtin_amdgcn_exp2f(fminf(gt - gi[e], 0.f)) * pt[s2][e];
             pt[s2][e] = (i0 + e <= t) ? x : 0.f;
           }
         }
@@ -444,15 +429,19 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
         }
-        const float cc = sc[C + 16 * mt + n16];
+        const float eg = __builtin_amdgcn_exp2f(sc[kScGam2 * C + 16 * mt + n16]);   // e^gamma_t
 #pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= cc;
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= eg;
 #pragma unroll
         for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
           const bf16x8 pf = lds16(lds + Cfg::kP + 1024 * frag_block(mt, kb2) + 16 * lane);
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
+        const f4 qp = *reinterpret_cast<const f4*>(rqs + 4 * (16 * mt + n16));
+        const float rq = __builtin_amdgcn_rsqf(((qp[0] + qp[1]) + (qp[2] + qp[3])) + 1e-6f) * 0.08838834764831845f;
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rq;
         if (fuse) {
           // this wave's sum of squares of the token's columns (its four lane groups), into LDS
           float ss = 0.f;
