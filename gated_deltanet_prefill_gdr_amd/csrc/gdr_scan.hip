@@ -50,11 +50,11 @@ template <bool kOut> struct SegCfg {
   static constexpr int kBuf = kOut ? kZ + kBufK : kRec + kRecB;
   // outputs only, after the two buffers: P of the current chunk (formed by the waves; one copy,
   // as it is formed and used between the same two barriers), the fused norm's row sums, and the
-  // partial sums of squares of the chunk's q rows (formed and used between the same two barriers)
+  // squared norms of the chunk's q rows (formed and used between the same two barriers)
   static constexpr int kP = 2 * kBuf;
   static constexpr int kPart = kP + kFragBlocks * 1024;
-  static constexpr int kRq = kPart + 2 * NW * C * 4;    // outputs only: q sums of squares, 4 per token
-  static constexpr int kLds = kOut ? kRq + 4 * C * 4 : 2 * kBuf;
+  static constexpr int kRq = kPart + 2 * NW * C * 4;    // outputs only: |q_t|^2 of the chunk's tokens
+  static constexpr int kLds = kOut ? kRq + C * 4 : 2 * kBuf;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
   static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
 };
@@ -309,26 +309,25 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // diagonal; read after the barrier that precedes the output products. The q norm of token t,
     // rq_t = (|q_t|^2 + 1e-6)^-1/2 128^-1/2 (model page model.py, _l2norm), is a factor of both
     // output terms of row t (O = diag(rq) (diag(e^gamma) Q S + P' Delta)), so it is applied to the
-    // finished row. Its sum of squares comes from the same Q reads: in the waves with kb2 = 0 (one
-    // per token tile) each lane adds its 32 of the token's 128 values and leaves the partial sum
-    // in LDS, four per token, summed by the output step.
-    float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // [64 tokens][4 partial sums]
+    // finished row. Its sum of squares comes from the same Q reads: the waves with kb2 = 0 (one per
+    // token tile) also form the tile's Q Q^T on MFMA and leave its diagonal in LDS.
+    float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // |q_t|^2, t = 0..63
     if constexpr (kOut) {
       if (w < kFragBlocks) {   // wave-uniform
         const unsigned char* Qt = Bf + Cfg::kQ;
         const int mt = block_tile(w), kb2 = block_kb(w);
-        f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)};
-        float qss = 0.f;
+        f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)}, qq = f4_splat(0.f);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
-          if (kb2 == 0)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qss += (float)qf[e] * (float)qf[e];
+          if (kb2 == 0) qq = mfma(qf, qf, qq);   // Q Q^T of the token tile: its diagonal is |q_t|^2
         }
-        if (kb2 == 0) rqs[4 * (16 * mt + n16) + G] = qss;
+        if (kb2 == 0 && (n16 >> 2) == G) {   // lane (n16, G) holds rows 4G .. 4G + 3 of column n16
+          const int e = n16 & 3;
+          rqs[16 * mt + n16] = e == 0 ? qq[0] : e == 1 ? qq[1] : e == 2 ? qq[2] : qq[3];
+        }
         const int t = 16 * mt + n16;
         const float gt = sc[kScGam2 * C + t];
 #pragma unroll
@@ -438,8 +437,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
-        const f4 qp = *reinterpret_cast<const f4*>(rqs + 4 * (16 * mt + n16));
-        const float rq = __builtin_amdgcn_rsqf(((qp[0] + qp[1]) + (qp[2] + qp[3])) + 1e-6f) * 0.08838834764831845f;
+        const float rq = __builtin_amdgcn_rsqf(rqs[16 * mt + n16] + 1e-6f) * 0.08838834764831845f;   // * 128^-1/2
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rq;
         if (fuse) {
@@ -557,73 +555,90 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
   // Step jj reads M_jj (this wave's 32 rows, all 128 keys) and the slice of B_jj; neither depends on
-  // the chained state, so step jj + 1's are loaded while step jj computes.
-  f4 Mr[2][4][2], Br[2];
-  auto load_step = [&](int jj) {
-    const float* M = slots + jj * kSlotFloats + D;   // M_jj, row pitch 2D
-    const float* Bn = slots + (jj + 1) * kSlotFloats;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float* mrow = M + (32 * w + 16 * s2 + n16) * 2 * D + 32 * kb + 4 * G;
-        Mr[s2][kb][0] = *reinterpret_cast<const f4*>(mrow);
-        Mr[s2][kb][1] = *reinterpret_cast<const f4*>(mrow + 16);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Br[s2][i] = Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
-    }
-  };
-  if (p.P > 1) load_step(0);
-  for (int jj = 0; jj + 1 < p.P; ++jj) {
-    float* Bn = slots + (jj + 1) * kSlotFloats;       // B_jj, replaced by the state entering jj + 1
-    bf16x8 mh[2][4], ml[2][4];
+  // the chained state, so they are loaded kPf steps ahead (a ring of register sets, the loop
+  // unrolled by kPf). With no initial state S_1 = B_0, which is already in its slot: the chain
+  // starts at step 1.
+  constexpr int kPf = 2;
+  f4 Mr[kPf][2][4][2], Br[kPf][2];
+  const int steps = p.P - 1, first = p.s0 ? 0 : 1;
+#define GDR_COMBINE_LOAD(u, jj)                                                          \
+  do {                                                                                   \
+    const float* M = slots + (size_t)(jj) * kSlotFloats + D; /* M_jj, row pitch 2D */    \
+    const float* Bn = slots + (size_t)((jj) + 1) * kSlotFloats;                          \
+    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                                   \
+      _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                                 \
+        const float* mrow = M + (32 * w + 16 * s2 + n16) * 2 * D + 32 * kb + 4 * G;      \
+        Mr[u][s2][kb][0] = *reinterpret_cast<const f4*>(mrow);                           \
+        Mr[u][s2][kb][1] = *reinterpret_cast<const f4*>(mrow + 16);                      \
+      }                                                                                  \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
+        Br[u][s2][i] = Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];                 \
+    }                                                                                    \
+  } while (0)
+  if (!p.s0 && steps > 0) {   // S_1 = B_0
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f4 m0 = Mr[s2][kb][0], m1 = Mr[s2][kb][1];
-        mh[s2][kb] = pack8(m0, m1);
+      for (int i = 0; i < 4; ++i) S[s2][i] = slots[kSlotFloats + (32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
+  }
+#pragma unroll
+  for (int u = 0; u < kPf; ++u)
+    if (first + u < steps) GDR_COMBINE_LOAD(u, first + u);
+  for (int j0 = first; j0 < steps; j0 += kPf) {
+#pragma unroll
+    for (int u = 0; u < kPf; ++u) {
+      const int jj = j0 + u;
+      if (jj >= steps) break;   // uniform
+      float* Bn = slots + (size_t)(jj + 1) * kSlotFloats;   // B_jj, replaced by the state entering jj + 1
+      bf16x8 mh[2][4], ml[2][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const f4 m0 = Mr[u][s2][kb][0], m1 = Mr[u][s2][kb][1];
+          mh[s2][kb] = pack8(m0, m1);
+          f4 r0, r1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r0[i] = m0[i] - (float)mh[s2][kb][i];
+            r1[i] = m1[i] - (float)mh[s2][kb][4 + i];
+          }
+          ml[s2][kb] = pack8(r0, r1);
+        }
+      const f4 Bv[2] = {Br[u][0], Br[u][1]};
+      if (jj + kPf < steps) GDR_COMBINE_LOAD(u, jj + kPf);
+      {
+        const bf16x8 hi = pack8(S[0], S[1]);
         f4 r0, r1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          r0[i] = m0[i] - (float)mh[s2][kb][i];
-          r1[i] = m1[i] - (float)mh[s2][kb][4 + i];
+          r0[i] = S[0][i] - (float)hi[i];
+          r1[i] = S[1][i] - (float)hi[4 + i];
         }
-        ml[s2][kb] = pack8(r0, r1);
+        sx[jj & 1][0][w][lane] = hi;
+        sx[jj & 1][1][w][lane] = pack8(r0, r1);
       }
-    const f4 Bv[2] = {Br[0], Br[1]};
-    if (jj + 2 < p.P) load_step(jj + 1);
-    {
-      const bf16x8 hi = pack8(S[0], S[1]);
-      f4 r0, r1;
+      lds_barrier();   // the state exchange is in LDS; the loads of later steps stay in flight
+      f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r0[i] = S[0][i] - (float)hi[i];
-        r1[i] = S[1][i] - (float)hi[4 + i];
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 sh = sx[jj & 1][0][kb][lane], sl = sx[jj & 1][1][kb][lane];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          acc[s2] = mfma(mh[s2][kb], sh, acc[s2]);
+          acc[s2] = mfma(mh[s2][kb], sl, acc[s2]);
+          acc[s2] = mfma(ml[s2][kb], sh, acc[s2]);
+        }
       }
-      sx[jj & 1][0][w][lane] = hi;
-      sx[jj & 1][1][w][lane] = pack8(r0, r1);
-    }
-    lds_barrier();   // the state exchange is in LDS; the loads of the next step stay in flight
-    f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const bf16x8 sh = sx[jj & 1][0][kb][lane], sl = sx[jj & 1][1][kb][lane];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        acc[s2] = mfma(mh[s2][kb], sh, acc[s2]);
-        acc[s2] = mfma(mh[s2][kb], sl, acc[s2]);
-        acc[s2] = mfma(ml[s2][kb], sh, acc[s2]);
+        S[s2] = acc[s2] + Bv[s2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
       }
     }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      S[s2] = acc[s2] + Bv[s2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
-    }
   }
+#undef GDR_COMBINE_LOAD
 }
 
 // ====================================================================== fp32 scan
