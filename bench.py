@@ -10,6 +10,7 @@ runs untimed for 0.3 s so that the GPU's clocks have settled. Prints one JSON li
   python bench.py --decode          # one fork decode step instead (gdr_decode, 64 rows x 1 token)
   python bench.py --layer           # the layer steps around it (gates, conv + SiLU, gated RMSNorm)
   python bench.py --fused           # the prefill with the gate prologue and gated RMSNorm fused in
+  python bench.py --all-configs     # every named workload: median call time, throughput, rooflines
   python bench.py --copy-probe      # a plain device copy of known size, for HBM counter scaling
 """
 from __future__ import annotations
@@ -26,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "gated-delta prefill tokens·heads/s and % MFMA roofline at L=16384, H=32, D=128"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3    # fp32 matrix
 CHUNK, D = 64, 128
 
 
@@ -73,6 +75,8 @@ def kernel_bytes(name, B, L, Hk, Hv, esz, P, fused=False):
     if name == "gdr_scan":
         return (2 * qk + 2 * vo + recs + B * Hv * D * D * 4 + (B * Hv * P * slot // 2 if P > 1 else 0)
                 + (vo if fused else 0))
+    if name == "gdr_gated_rmsnorm":   # o and z read, o written
+        return 3 * vo
     raise KeyError(name)
 
 
@@ -265,6 +269,56 @@ def bench_layer(a):
     print(json.dumps(line), flush=True)
 
 
+def bench_all_configs(a):
+    """Every named workload (configs 1..5): median call time over 50 calls after 10 warm-up calls
+    (HIP events around each call, inputs resident), throughput, TFLOP/s, algorithmic GB/s and
+    both roofline fractions. One JSON line per config; a report, not the step metric."""
+    import statistics
+    import torch
+    import gated_deltanet_prefill_gdr_amd as gdr
+    from workloads import CONFIGS
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    for i in sorted(CONFIGS):
+        x = CONFIGS[i].draw()
+        B, L, Hk, Hv, Dk, Dv = x.shape
+        esz = 2 if x.q.dtype == torch.bfloat16 else 4
+        t = {n: (None if v is None else v.to(dev)) for n, v in
+             (("q", x.q), ("k", x.k), ("v", x.v), ("g", x.g), ("beta", x.beta), ("lengths", x.lengths),
+              ("s0", x.s0), ("s0_row", x.s0_row))}
+        o = torch.empty(B, L, Hv, Dv, device=dev, dtype=x.v.dtype)
+        sf = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
+        n_s0 = 0 if x.s0 is None else x.s0.shape[0]
+        desc = gdr.make_desc(B, L, Hk, Hv, n_s0, esz == 2, False)
+        ws = torch.empty(max(gdr.workspace_size(desc), 1), device=dev, dtype=torch.uint8)
+
+        def step():
+            gdr.prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], valid=t["lengths"], s0=t["s0"],
+                        s0_row=t["s0_row"], out=o, s_final=sf, workspace=ws)
+
+        settle(step, a.settle)
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for e0, e1 in ev:
+            e0.record()
+            step()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+        units, nbytes, flops = algorithmic(B, L, Hk, Hv, esz, n_s0, True)
+        nbytes += 4 * B if x.lengths is not None else 0
+        valid_units = units if x.lengths is None else int(x.lengths.sum()) * Hv
+        peak = MFMA_BF16_PEAK_TFLOPS if esz == 2 else MFMA_FP32_PEAK_TFLOPS
+        line = {"config": i, "workload": CONFIGS[i].name, "dtype": "bf16" if esz == 2 else "f32",
+                "us": ms * 1e3, "tokens_heads_per_s": units / (ms * 1e-3),
+                "valid_tokens_heads_per_s": valid_units / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
+                "alg_GBs": nbytes / (ms * 1e-3) / 1e9, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak,
+                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": nbytes, "alg_flops": flops}
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +331,7 @@ def main():
     ap.add_argument("--rows", type=int, default=64)
     ap.add_argument("--layer", action="store_true")
     ap.add_argument("--fused", action="store_true")
+    ap.add_argument("--all-configs", action="store_true", help="time every named workload (a report)")
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up (0 for counter runs)")
     a = ap.parse_args()
@@ -294,6 +349,9 @@ def main():
         return
     if a.layer:
         bench_layer(a)
+        return
+    if a.all_configs:
+        bench_all_configs(a)
         return
     import gated_deltanet_prefill_gdr_amd as gdr
     from workloads import CONFIGS
@@ -333,7 +391,10 @@ def main():
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
     k_ms = per_kernel[dominant][0]
     k_bytes = kernel_bytes(dominant, B, L, Hk, Hv, 2, P, fused=a.fused)
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    # roofline of the dominant kernel: the path's algorithmic bytes per unit (one token x one value
+    # head) times the units one launch processes (every kernel of the path processes all of them),
+    # over that kernel's average launch time
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
     traffic = None
     prof = os.path.join(ROOT, "profiles", "traffic_l16384_bf16.json")
     if os.path.exists(prof):
@@ -362,11 +423,13 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
-                     "kernel_bytes": k_bytes, "kernel_ms": k_ms},
+                     "kernel_ms": k_ms, "alg_bytes_per_unit": nbytes / units, "units": units,
+                     "interface_bytes": k_bytes, "interface_GBs": k_bytes / (k_ms * 1e-3) / 1e9},
         "path": {"ms": ms, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                  "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": nbytes, "alg_flops": flops,
-                 "kernel_ms": {n: t for n, (t, c) in per_kernel.items()}, "segments": P,
+                 "kernel_ms": {n: t for n, (t, c) in per_kernel.items()},
+                 "segments": P,
                  "source_hash": source_hash()},
         "cpu_baseline": None,
     }

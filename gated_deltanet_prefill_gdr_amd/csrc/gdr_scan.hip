@@ -303,19 +303,21 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     const unsigned char* Rc = Bf + Cfg::kRec;
     const float* sc = reinterpret_cast<const float*>(Rc + kScOff);
 
-    // P' of this chunk (outputs): waves 0..5 each form one operand block (token tile mt, key block
-    // kb2) from the staged tiles as the tile pair K Q^T (whose accumulator layout is the operand
-    // layout of P'), scaled by rk_i 2^{min(gamma2_t - gamma2_i, 0)} on i <= t and zero above the
-    // diagonal; read after the barrier that precedes the output products. The q norm of token t,
+    // P' of this chunk (outputs): the waves form its six operand blocks (token tile mt, key block
+    // kb2; block i by wave i mod NW) from the staged tiles as the tile pair K Q^T (whose
+    // accumulator layout is the operand layout of P'), scaled by rk_i 2^{min(gamma2_t - gamma2_i, 0)}
+    // on i <= t and zero above the diagonal; read after the barrier that precedes the output
+    // products. The q norm of token t,
     // rq_t = (|q_t|^2 + 1e-6)^-1/2 128^-1/2 (model page model.py, _l2norm), is a factor of both
     // output terms of row t (O = diag(rq) (diag(e^gamma) Q S + P' Delta)), so it is applied to the
     // finished row. Its sum of squares comes from the same Q reads: the waves with kb2 = 0 (one per
     // token tile) also form the tile's Q Q^T on MFMA and leave its diagonal in LDS.
     float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // |q_t|^2, t = 0..63
     if constexpr (kOut) {
-      if (w < kFragBlocks) {   // wave-uniform
-        const unsigned char* Qt = Bf + Cfg::kQ;
-        const int mt = block_tile(w), kb2 = block_kb(w);
+      const unsigned char* Qt = Bf + Cfg::kQ;
+      // eight waves: one block each (waves 0..5); four waves: blocks w and w + 4
+      for (int blk = w; blk < (NW >= kFragBlocks ? w + 1 : kFragBlocks) && blk < kFragBlocks; blk += NW) {
+        const int mt = block_tile(blk), kb2 = block_kb(blk);
         f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)}, qq = f4_splat(0.f);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -341,7 +343,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
             pt[s2][e] = (i0 + e <= t) ? x : 0.f;
           }
         }
-        *reinterpret_cast<bf16x8*>(lds + Cfg::kP + 1024 * w + 16 * lane) = pack8(pt[0], pt[1]);
+        *reinterpret_cast<bf16x8*>(lds + Cfg::kP + 1024 * blk + 16 * lane) = pack8(pt[0], pt[1]);
       }
     }
 
