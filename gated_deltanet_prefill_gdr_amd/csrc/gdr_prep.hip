@@ -503,13 +503,28 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     }
   };
 
+  // Chunks entirely past their row's length get no record: the scan passes neither read nor need
+  // one (there beta' = g' = 0, so the chunk leaves the state unchanged), and the item walk skips
+  // them. Rows whose length is out of range are computed in full (the output pass turns them into
+  // NaN).
+  auto is_pad = [&](int it2) {
+    if (!p.lengths) return false;
+    const int len = p.lengths[it2 / (p.Hk * p.NC)], c2 = (it2 / p.Hk) % p.NC;
+    return len >= 0 && len <= p.L && c2 * C >= len;
+  };
+  auto next_item = [&](int it2) {
+    do it2 += gridDim.x;
+    while (it2 < items && is_pad(it2));
+    return it2;
+  };
   int it = blockIdx.x;
+  if (it < items && is_pad(it)) it = next_item(it);
   GateRaw graw{};   // raw gates of value head `wave` of item it (first batch of four), in flight
   if (it < items) {
     issue_k(it);
     if (wave < r) graw = gates_issue<TB>(p, it / (p.Hk * p.NC), it % p.Hk, (it / p.Hk) % p.NC, wave, lane);
   }
-  for (; it < items; it += gridDim.x) {
+  for (int nx; it < items; it = nx) {
     const int kh = it % p.Hk, c = (it / p.Hk) % p.NC, b = it / (p.Hk * p.NC);
     // this wave's part of the K tile (and its gates) have landed; every wave is done with the
     // previous item's A, T and gates
@@ -539,7 +554,7 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     lds_barrier();   // the K tile is free, gates and rk are in LDS
 
     // the next item's K tile and gates, while this item's inverses run
-    const int nx = it + gridDim.x;
+    nx = next_item(it);
     if (nx < items) {
       issue_k(nx);
       if (wave < r) graw = gates_issue<TB>(p, nx / (p.Hk * p.NC), nx % p.Hk, (nx / p.Hk) % p.NC, wave, lane);

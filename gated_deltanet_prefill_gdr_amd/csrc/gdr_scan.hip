@@ -167,6 +167,11 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     return;
   }
 
+  // Chunks entirely past the row's length (right pads: beta' = g' = 0) leave the state unchanged
+  // and give O = diag(rq) Q S: only their Q tile (and gate rows) is staged and only the output
+  // products run.
+  int len_b = p.lengths ? p.lengths[b] : p.L;
+  len_b = len_b < 0 ? 0 : (len_b > p.L ? p.L : len_b);
   const uint32_t kq_row = (uint32_t)p.Hk * D * 2, vo_row = (uint32_t)p.Hv * D * 2;
   const size_t kq_base = (size_t)b * p.L * p.Hk * D, vo_base = ((size_t)b * p.L * p.Hv + h) * D;
   const uint32_t vo_bytes = p.L > 0 ? (uint32_t)(p.L - 1) * vo_row + D * 2 : 0;
@@ -206,6 +211,20 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       if (i < kRecBlocks) dma16(rr, rec + 1024 * i, Bf + Cfg::kRec + 1024 * i);   // wave-uniform
     }
   };
+  // a chunk past the row's length (outputs only): its Q rows and, with the fused norm, gate rows
+  auto issue_q = [&](int c) {
+    unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
+    const uint32_t t0 = (uint32_t)c * C;
+#pragma unroll
+    for (int m = 0; m < R / 4; ++m) {
+      const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
+      const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
+      if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
+      if (kOut && p.z) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
+    }
+  };
+  // chunks c_begin .. c_mid - 1 hold valid tokens; c_mid .. c_end - 1 are right pads
+  const int c_mid = min(max((len_b + C - 1) / C, c_begin), c_end);
 
   // ---- state entering the segment
   f4 S[NSL][4][2];
@@ -278,14 +297,54 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     store_o(c);
   };
 
-  issue(c_begin);
+  if (c_begin < c_mid)
+    issue(c_begin);
+  else if (c_begin < c_end)
+    issue_q(c_begin);
   wait_and_barrier<0>();
   // The same wait as a builtin the compiler sees: the entering-state loads are then known complete,
   // so it places no wait for them inside the loop (where it would also stall on the next chunk's
   // loads into LDS).
   __builtin_amdgcn_s_waitcnt(0);
 
-  for (int c = c_begin; c < c_end; ++c) {
+  float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // |q_t|^2, t = 0..63 (outputs)
+  auto put_qnorms = [&](int mt, const f4& qq) {   // lane (n16, G) holds rows 4G .. 4G + 3 of column n16
+    if ((n16 >> 2) == G) {
+      const int e = n16 & 3;
+      rqs[16 * mt + n16] = e == 0 ? qq[0] : e == 1 ? qq[1] : e == 2 ? qq[2] : qq[3];
+    }
+  };
+  // Row t of O is finished by the q norm factor rq_t; with the fused norm the wave's partial sum
+  // of squares of the row goes to LDS and w silu(z) of the lane's elements is formed from the
+  // gate rows staged with the chunk.
+  auto finish_rows = [&](int mt, int c, const unsigned char* Bf) {
+    const float rq = __builtin_amdgcn_rsqf(rqs[16 * mt + n16] + 1e-6f) * 0.08838834764831845f;   // * 128^-1/2
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rq;
+    if (fuse) {
+      float ss = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss += Ot[mt][sl][i] * Ot[mt][sl][i];
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      if (G == 0) part[(c & 1) * NW * C + w * C + 16 * mt + n16] = ss;
+      const unsigned char* Zb = Bf + Cfg::kZ;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        const int zrow = 16 * mt + n16, zcol = seg_col<kOut>(w, sl) + 4 * G;
+        const bf16x4 zb = *reinterpret_cast<const bf16x4*>(Zb + swz_z(zrow, zcol >> 3) + 2 * (zcol & 7));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float zf = (float)zb[i];
+          sz[mt][sl][i] = nw[sl][i] * zf * silu_gate(zf);
+        }
+      }
+    }
+  };
+
+  for (int c = c_begin; c < c_mid; ++c) {
     // chunk c has landed for every wave, every wave is done with chunk c - 1's buffer, and (fused
     // norm) chunk c - 1's gate rows and partial sums are in LDS. Vector-memory operations issued
     // after chunk c's loads: chunk c - 1's output stores; none with the fused norm (its stores
@@ -295,7 +354,10 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     else
       wait_and_barrier<Cfg::kStores>();
     if (fuse && c > c_begin) finish_norm(c - 1);
-    if (c + 1 < c_end) issue(c + 1);
+    if (c + 1 < c_mid)
+      issue(c + 1);
+    else if (kOut && c + 1 < c_end)
+      issue_q(c + 1);
 
     const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const unsigned char* Kt = Bf + Cfg::kK;
@@ -312,7 +374,6 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // output terms of row t (O = diag(rq) (diag(e^gamma) Q S + P' Delta)), so it is applied to the
     // finished row. Its sum of squares comes from the same Q reads: the waves with kb2 = 0 (one per
     // token tile) also form the tile's Q Q^T on MFMA and leave its diagonal in LDS.
-    float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // |q_t|^2, t = 0..63
     if constexpr (kOut) {
       const unsigned char* Qt = Bf + Cfg::kQ;
       // eight waves: one block each (waves 0..5); four waves: blocks w and w + 4
@@ -326,10 +387,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
           if (kb2 == 0) qq = mfma(qf, qf, qq);   // Q Q^T of the token tile: its diagonal is |q_t|^2
         }
-        if (kb2 == 0 && (n16 >> 2) == G) {   // lane (n16, G) holds rows 4G .. 4G + 3 of column n16
-          const int e = n16 & 3;
-          rqs[16 * mt + n16] = e == 0 ? qq[0] : e == 1 ? qq[1] : e == 2 ? qq[2] : qq[3];
-        }
+        if (kb2 == 0) put_qnorms(mt, qq);
         const int t = 16 * mt + n16;
         const float gt = sc[kScGam2 * C + t];
 #pragma unroll
@@ -439,32 +497,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
-        const float rq = __builtin_amdgcn_rsqf(rqs[16 * mt + n16] + 1e-6f) * 0.08838834764831845f;   // * 128^-1/2
-#pragma unroll
-        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rq;
-        if (fuse) {
-          // this wave's sum of squares of the token's columns (its four lane groups), into LDS
-          float ss = 0.f;
-#pragma unroll
-          for (int sl = 0; sl < NSL; ++sl)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ss += Ot[mt][sl][i] * Ot[mt][sl][i];
-          ss += __shfl_xor(ss, 16);
-          ss += __shfl_xor(ss, 32);
-          if (G == 0) part[(c & 1) * NW * C + w * C + 16 * mt + n16] = ss;
-          // w silu(z) of this lane's elements, from the gate rows staged with the chunk
-          const unsigned char* Zb = Bf + Cfg::kZ;
-#pragma unroll
-          for (int sl = 0; sl < NSL; ++sl) {
-            const int zrow = 16 * mt + n16, zcol = seg_col<kOut>(w, sl) + 4 * G;
-            const bf16x4 zb = *reinterpret_cast<const bf16x4*>(Zb + swz_z(zrow, zcol >> 3) + 2 * (zcol & 7));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float zf = (float)zb[i];
-              sz[mt][sl][i] = nw[sl][i] * zf * silu_gate(zf);
-            }
-          }
-        }
+        finish_rows(mt, c, Bf);
       }
       if (!fuse) store_o(c);
     }
@@ -483,6 +516,46 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] = mfma(kt, Ddop[sl][kb2], S[sl][kb][s2]);
         }
       }
+  }
+  if constexpr (kOut) {
+    // Right pads (beta' = g' = 0): the state stays as it is and O = diag(rq) Q S, the only products.
+    bf16x8 Sop[NSL][4];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
+    for (int c = c_mid; c < c_end; ++c) {
+      if (fuse)
+        wait_and_barrier<0>();
+      else
+        wait_and_barrier<Cfg::kStores>();
+      if (fuse && c > c_begin) finish_norm(c - 1);
+      if (c + 1 < c_end) issue_q(c + 1);
+      const unsigned char* Qt = lds + (c & 1) * Cfg::kBuf + Cfg::kQ;
+      if (w < 4) {   // q norms of token tile w
+        f4 qq = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * w + n16, 4 * kb + G));
+          qq = mfma(qf, qf, qq);
+        }
+        put_qnorms(w, qq);
+      }
+      lds_barrier();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
+        }
+        finish_rows(mt, c, lds + (c & 1) * Cfg::kBuf);
+      }
+      if (!fuse) store_o(c);
+    }
   }
   if (fuse && c_end > c_begin) {   // the last chunk's norm: its partial sums, then store
     lds_barrier();

@@ -94,6 +94,14 @@ def test_zero_length_rows_keep_state():
     assert torch.equal(s[0].cpu(), x.s0[0]) and torch.equal(s[2].cpu(), x.s0[2])
 
 
+def test_bf16_padded_segments():
+    # many chunks past the row lengths, spread over the segments of the bf16 scan: whole pad
+    # segments (identity transitions), a segment that starts in the pad, and a zero-length row
+    x = draw(3, 700, 2, 4, 128, "R1", 508, torch.bfloat16, lengths=[700, 0, 129], s0_rows=3)
+    o, s = run_gpu(x)
+    check(x, o, s, label="bf16 padded segments")
+
+
 def test_empty_sequence_copies_state():
     x = draw(2, 0, 2, 4, 128, "R1", 503, torch.float32, s0_rows=2)
     o, s = run_gpu(x)
