@@ -490,9 +490,15 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
   const int r = p.Hv / p.Hk;
   const uint32_t row_bytes = (uint32_t)p.Hk * D * 2;
 
+  // Items are numbered key head fastest, then row, then chunk: it = kh + Hk (b + B c). A
+  // workgroup's items (it, it + grid, ...) then cover every chunk position in turn, so that with
+  // ragged rows (whose late chunks are skipped) every workgroup gets a like share of real work.
+  auto item_b = [&](int it2) { return (it2 / p.Hk) % p.B; };
+  auto item_c = [&](int it2) { return it2 / (p.Hk * p.B); };
+
   // This wave's quarter of item it's K tile: rows 16 wave .. 16 wave + 15, four DMA loads of four rows.
   auto issue_k = [&](int it) {
-    const int kh = it % p.Hk, c = (it / p.Hk) % p.NC, b = it / (p.Hk * p.NC);
+    const int kh = it % p.Hk, b = item_b(it), c = item_c(it);
     const i32x4 rk = rsrc_words(reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.L * p.Hk * D,
                                 (uint32_t)p.L * row_bytes);   // rows past L read as zeros
 #pragma unroll
@@ -509,8 +515,8 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
   // NaN).
   auto is_pad = [&](int it2) {
     if (!p.lengths) return false;
-    const int len = p.lengths[it2 / (p.Hk * p.NC)], c2 = (it2 / p.Hk) % p.NC;
-    return len >= 0 && len <= p.L && c2 * C >= len;
+    const int len = p.lengths[item_b(it2)];
+    return len >= 0 && len <= p.L && item_c(it2) * C >= len;
   };
   auto next_item = [&](int it2) {
     do it2 += gridDim.x;
@@ -522,10 +528,10 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
   GateRaw graw{};   // raw gates of value head `wave` of item it (first batch of four), in flight
   if (it < items) {
     issue_k(it);
-    if (wave < r) graw = gates_issue<TB>(p, it / (p.Hk * p.NC), it % p.Hk, (it / p.Hk) % p.NC, wave, lane);
+    if (wave < r) graw = gates_issue<TB>(p, item_b(it), it % p.Hk, item_c(it), wave, lane);
   }
   for (int nx; it < items; it = nx) {
-    const int kh = it % p.Hk, c = (it / p.Hk) % p.NC, b = it / (p.Hk * p.NC);
+    const int kh = it % p.Hk, b = item_b(it), c = item_c(it);
     // this wave's part of the K tile (and its gates) have landed; every wave is done with the
     // previous item's A, T and gates
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -557,7 +563,7 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     nx = next_item(it);
     if (nx < items) {
       issue_k(nx);
-      if (wave < r) graw = gates_issue<TB>(p, nx / (p.Hk * p.NC), nx % p.Hk, (nx / p.Hk) % p.NC, wave, lane);
+      if (wave < r) graw = gates_issue<TB>(p, item_b(nx), nx % p.Hk, item_c(nx), wave, lane);
     }
 
     // ---- 3-6 for each value head of the key head
