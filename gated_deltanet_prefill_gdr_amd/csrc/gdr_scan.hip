@@ -190,25 +190,29 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
   // This wave's share of chunk c: K (and Q, and the fused norm's gate rows) and V rows
   // R w .. R w + R - 1 (R = 64 / NW, loads of four rows each) and the 1 KiB record blocks w,
-  // w + NW, ... (the Tb blocks 0..5 and the scalar blocks 6, 7).
+  // w + NW, ... (the Tb blocks 0..5 and the scalar blocks 6, 7); `parts` selects which of them.
   constexpr int R = C / NW;
-  auto issue = [&](int c) {
+  enum : int { kStK = 1, kStV = 2, kStRec = 4, kStQ = 8, kStAll = 15 };   // kStQ: Q and gate rows
+  auto issue = [&](int c, int parts) {
     unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const uint32_t t0 = (uint32_t)c * C;
 #pragma unroll
     for (int m = 0; m < R / 4; ++m) {
       const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
       const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
-      dma16(rk, kq, Bf + Cfg::kK + (R * w + 4 * m) * 256);
-      if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
-      dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (R * w + 4 * m) * 256);
-      if (kOut && p.z) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
+      if (parts & kStK) dma16(rk, kq, Bf + Cfg::kK + (R * w + 4 * m) * 256);
+      if (kOut && (parts & kStQ)) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
+      if (parts & kStV) dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (R * w + 4 * m) * 256);
+      if (kOut && p.z && (parts & kStQ))
+        dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
     }
-    const uint32_t rec = (uint32_t)c * kRecB + 16 * lane;
+    if (parts & kStRec) {
+      const uint32_t rec = (uint32_t)c * kRecB + 16 * lane;
 #pragma unroll
-    for (int i0 = 0; i0 < kRecBlocks; i0 += NW) {
-      const int i = i0 + w;
-      if (i < kRecBlocks) dma16(rr, rec + 1024 * i, Bf + Cfg::kRec + 1024 * i);   // wave-uniform
+      for (int i0 = 0; i0 < kRecBlocks; i0 += NW) {
+        const int i = i0 + w;
+        if (i < kRecBlocks) dma16(rr, rec + 1024 * i, Bf + Cfg::kRec + 1024 * i);   // wave-uniform
+      }
     }
   };
   // a chunk past the row's length (outputs only): its Q rows and, with the fused norm, gate rows
@@ -298,7 +302,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   };
 
   if (c_begin < c_mid)
-    issue(c_begin);
+    issue(c_begin, kStAll);
   else if (c_begin < c_end)
     issue_q(c_begin);
   wait_and_barrier<0>();
@@ -354,10 +358,15 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     else
       wait_and_barrier<Cfg::kStores>();
     if (fuse && c > c_begin) finish_norm(c - 1);
+    // The next chunk's staging. The output pass spreads it over the iteration: K here, Q after the
+    // P formation, V after X, the record before the P barrier. Issued all at once, these loads
+    // hold up this chunk's first LDS reads and products (about a tenth of the pass at the long
+    // prefill). The transitions, which form no P, issue it all here.
     if (c + 1 < c_mid)
-      issue(c + 1);
+      issue(c + 1, kOut ? kStK : kStAll);
     else if (kOut && c + 1 < c_end)
       issue_q(c + 1);
+    const bool stage_next = kOut && c + 1 < c_mid;
 
     const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const unsigned char* Kt = Bf + Cfg::kK;
@@ -411,6 +420,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
 
+    if (stage_next) issue(c + 1, kStQ);
+
     // X = K S
     f4 X[NSL][4];
 #pragma unroll
@@ -424,6 +435,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
         for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = mfma(kf, Sop[sl][kb], X[sl][mt]);
       }
     }
+    if (stage_next) issue(c + 1, kStV);
     // R = V - diag(a) X  (zero values for the identity columns)
     bf16x8 Rop[NSL][2];
     {
@@ -470,6 +482,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // O^T = diag(c) (S^T Q^T) + Delta^T P^T: the accumulator lane (token n16, G) holds the four
     // consecutive columns 4G .. 4G + 3 of one token, stored as one 8-byte write.
     if constexpr (kOut) {
+      if (stage_next) issue(c + 1, kStRec);
       lds_barrier();   // P is complete
       const unsigned char* Qt = Bf + Cfg::kQ;
       bf16x8 Dop[NSL][2];
