@@ -276,16 +276,17 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   f4 Ot[4][NSL], sz[4][NSL];
   const bool fuse = kOut && p.z != nullptr;
   float* part = reinterpret_cast<float*>(lds + Cfg::kPart);   // [2][NW][64]
+  auto store_tile = [&](int c, int mt) {
+    const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const bf16x4 ob = {(__bf16)Ot[mt][sl][0], (__bf16)Ot[mt][sl][1], (__bf16)Ot[mt][sl][2], (__bf16)Ot[mt][sl][3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, orow + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
+    }
+  };
   auto store_o = [&](int c) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
-#pragma unroll
-      for (int sl = 0; sl < NSL; ++sl) {
-        const bf16x4 ob = {(__bf16)Ot[mt][sl][0], (__bf16)Ot[mt][sl][1], (__bf16)Ot[mt][sl][2], (__bf16)Ot[mt][sl][3]};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, orow + 2 * (seg_col<kOut>(w, sl) + 4 * G), 0, 0);
-      }
-    }
+    for (int mt = 0; mt < 4; ++mt) store_tile(c, mt);
   };
   auto finish_norm = [&](int c) {   // w o / sqrt(mean(o^2) + eps) silu(z) for chunk c, then store
     const float* pp = part + (c & 1) * NW * C;
@@ -511,8 +512,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
         }
         finish_rows(mt, c, Bf);
+        if (!fuse) store_tile(c, mt);   // each token tile as soon as it is done
       }
-      if (!fuse) store_o(c);
     }
     // S <- e^{gamma_63} S + K^T diag(d) Delta
     const float egc = sc[3 * C];
