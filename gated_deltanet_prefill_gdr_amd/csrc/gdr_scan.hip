@@ -645,9 +645,10 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
     for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
   // Step jj reads M_jj (this wave's 32 rows, all 128 keys) and the slice of B_jj; neither depends on
   // the chained state, so they are loaded kPf steps ahead (a ring of register sets, the loop
-  // unrolled by kPf). With no initial state S_1 = B_0, which is already in its slot: the chain
-  // starts at step 1.
-  constexpr int kPf = 2;
+  // unrolled by kPf). One step ahead measured fastest: a deeper ring puts part of it in AGPRs, and
+  // the copies out of them wait for the loads. With no initial state S_1 = B_0, which is already in
+  // its slot: the chain starts at step 1.
+  constexpr int kPf = 1;
   f4 Mr[kPf][2][4][2], Br[kPf][2];
   const int steps = p.P - 1, first = p.s0 ? 0 : 1;
 #define GDR_COMBINE_LOAD(u, jj)                                                          \
