@@ -245,6 +245,10 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
 
   if (NC > 0) {
     gdr::PrepParams pp{q, k, g, beta, lengths, ws, d->B, d->L, d->Hk, d->Hv, NC};
+    if (bf16 && lengths)
+      pp.chunk_list = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
+                                                 gdr::records_bytes(d->B, d->Hv, NC, dtype_size(d->qkv_dtype)) +
+                                                 gdr::seg_bytes(d->B, d->Hv, NC, dtype_size(d->qkv_dtype)));
     if (fused_gates) {
       pp.b_raw = fu->b_raw;
       pp.a_raw = fu->a_raw;

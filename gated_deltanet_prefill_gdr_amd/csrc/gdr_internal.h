@@ -60,10 +60,17 @@ inline size_t records_bytes(int B, int Hv, int NC, size_t elem) {
   return size_t(B) * Hv * NC * record_bytes(elem);
 }
 
-inline size_t workspace_bytes(int B, int Hv, int NC, size_t elem) {
+inline size_t seg_bytes(int B, int Hv, int NC, size_t elem) {
   const SegPlan sp = seg_plan(B, Hv, NC, elem == 2);
-  const size_t seg = sp.P > 1 ? size_t(B) * Hv * sp.P * kSlotFloats * sizeof(float) : 0;
-  return records_bytes(B, Hv, NC, elem) + seg;
+  return sp.P > 1 ? size_t(B) * Hv * sp.P * kSlotFloats * sizeof(float) : 0;
+}
+
+// Chunk list (bf16, after the segment states): the chunks that hold valid tokens when lengths are
+// given, row-major: int32 count U, then U entries b NC + c.
+inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 4 * (1 + size_t(B) * NC) : 0; }
+
+inline size_t workspace_bytes(int B, int Hv, int NC, size_t elem) {
+  return records_bytes(B, Hv, NC, elem) + seg_bytes(B, Hv, NC, elem) + chunk_list_bytes(B, NC, elem);
 }
 
 struct PrepParams {
@@ -80,6 +87,7 @@ struct PrepParams {
   const void* a_raw;
   const float* A_log;     // [Hv]
   const float* dt_bias;   // [Hv]
+  int32_t* chunk_list;     // bf16 with lengths: the chunk list (written by the prep launch), else null
 };
 
 struct ScanParams {

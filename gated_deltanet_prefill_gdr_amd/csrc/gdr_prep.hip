@@ -480,7 +480,38 @@ __device__ __forceinline__ void gram_kk(const unsigned char* kt, int n16, int G,
 // Work item it = ((b NC) + c) Hk + kh: items of one chunk and neighbouring key heads read
 // neighbouring 256-byte pieces of the same k rows. The next item's K tile is copied HBM -> LDS
 // (the waves' DMA, issued once the current Gram is formed) while the current item's inverses run.
-template <typename TB>
+// The chunks of a right-padded batch that hold valid tokens, row-major: list[0] = their count U,
+// list[1 + u] = b NC + c. Rows whose length is out of range count all their chunks (they are
+// computed in full; the output pass turns them into NaN). One workgroup: rows in blocks of 256,
+// each with a workgroup-wide inclusive prefix sum of the rows' chunk counts.
+__global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, int B, int L, int NC, int32_t* list) {
+  __shared__ int sc[256];
+  const int tid = threadIdx.x;
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    const int b = b0 + tid;
+    int nc = 0;
+    if (b < B) {
+      const int len = lengths[b];
+      nc = (len < 0 || len > L) ? NC : (len + C - 1) / C;
+    }
+    sc[tid] = nc;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int y = tid >= d ? sc[tid - d] : 0;
+      __syncthreads();
+      sc[tid] += y;
+      __syncthreads();
+    }
+    const int start = base + sc[tid] - nc;
+    for (int c = 0; c < nc; ++c) list[1 + start + c] = b * NC + c;
+    base += sc[255];
+    __syncthreads();
+  }
+  if (tid == 0) list[0] = base;
+}
+
+template <typename TB, bool kList>
 __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int items) {
   __shared__ __attribute__((aligned(16))) PrepKhSmem sm;
   constexpr int kRecBytes = kFragBlocks * kBlockElems * 2 + kScalarBytes;
@@ -490,15 +521,33 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
   const int r = p.Hv / p.Hk;
   const uint32_t row_bytes = (uint32_t)p.Hk * D * 2;
 
-  // Items are numbered key head fastest, then row, then chunk: it = kh + Hk (b + B c). A
-  // workgroup's items (it, it + grid, ...) then cover every chunk position in turn, so that with
-  // ragged rows (whose late chunks are skipped) every workgroup gets a like share of real work.
-  auto item_b = [&](int it2) { return (it2 / p.Hk) % p.B; };
-  auto item_c = [&](int it2) { return it2 / (p.Hk * p.B); };
+  // Work items. With lengths (kList), the items are the chunks of the chunk list, key head fastest:
+  // it = kh + Hk u, so that every workgroup's items (it, it + grid, ...) are real work in equal
+  // number. Chunks wholly past their row's length are not in the list: they get no record, which
+  // the scan passes neither read nor need (there beta' = g' = 0, so the chunk leaves the state
+  // unchanged). Without lengths, the items are numbered key head fastest, then row, then chunk:
+  // it = kh + Hk (b + B c), so that a workgroup's items pass through every chunk position.
+  struct Item {
+    int b, c, kh;
+  };
+  auto item = [&](int it2) {
+    Item x;
+    x.kh = it2 % p.Hk;
+    if constexpr (kList) {
+      const int e = p.chunk_list[1 + it2 / p.Hk];
+      x.b = e / p.NC;
+      x.c = e - x.b * p.NC;
+    } else {
+      x.b = (it2 / p.Hk) % p.B;
+      x.c = it2 / (p.Hk * p.B);
+    }
+    return x;
+  };
+  if constexpr (kList) items = p.chunk_list[0] * p.Hk;
 
   // This wave's quarter of item it's K tile: rows 16 wave .. 16 wave + 15, four DMA loads of four rows.
-  auto issue_k = [&](int it) {
-    const int kh = it % p.Hk, b = item_b(it), c = item_c(it);
+  auto issue_k = [&](const Item& x) {
+    const int kh = x.kh, b = x.b, c = x.c;
     const i32x4 rk = rsrc_words(reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.L * p.Hk * D,
                                 (uint32_t)p.L * row_bytes);   // rows past L read as zeros
 #pragma unroll
@@ -509,29 +558,16 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     }
   };
 
-  // Chunks entirely past their row's length get no record: the scan passes neither read nor need
-  // one (there beta' = g' = 0, so the chunk leaves the state unchanged), and the item walk skips
-  // them. Rows whose length is out of range are computed in full (the output pass turns them into
-  // NaN).
-  auto is_pad = [&](int it2) {
-    if (!p.lengths) return false;
-    const int len = p.lengths[item_b(it2)];
-    return len >= 0 && len <= p.L && item_c(it2) * C >= len;
-  };
-  auto next_item = [&](int it2) {
-    do it2 += gridDim.x;
-    while (it2 < items && is_pad(it2));
-    return it2;
-  };
   int it = blockIdx.x;
-  if (it < items && is_pad(it)) it = next_item(it);
   GateRaw graw{};   // raw gates of value head `wave` of item it (first batch of four), in flight
+  Item nxt{};       // item it, then the next one
   if (it < items) {
-    issue_k(it);
-    if (wave < r) graw = gates_issue<TB>(p, item_b(it), it % p.Hk, item_c(it), wave, lane);
+    nxt = item(it);
+    issue_k(nxt);
+    if (wave < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, wave, lane);
   }
-  for (int nx; it < items; it = nx) {
-    const int kh = it % p.Hk, b = item_b(it), c = item_c(it);
+  for (; it < items; it += gridDim.x) {
+    const int kh = nxt.kh, b = nxt.b, c = nxt.c;
     // this wave's part of the K tile (and its gates) have landed; every wave is done with the
     // previous item's A, T and gates
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -560,10 +596,10 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     lds_barrier();   // the K tile is free, gates and rk are in LDS
 
     // the next item's K tile and gates, while this item's inverses run
-    nx = next_item(it);
-    if (nx < items) {
-      issue_k(nx);
-      if (wave < r) graw = gates_issue<TB>(p, item_b(nx), nx % p.Hk, item_c(nx), wave, lane);
+    if (it + (int)gridDim.x < items) {
+      nxt = item(it + gridDim.x);
+      issue_k(nxt);
+      if (wave < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, wave, lane);
     }
 
     // ---- 3-6 for each value head of the key head
@@ -609,12 +645,21 @@ static int prep_workgroups() {
 
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s) {
   if (qkv_bf16) {
-    const int64_t items = int64_t(p.B) * p.Hk * p.NC;   // <= B Hv NC < 2^31 (checked by the caller)
+    // items: an upper bound with a chunk list (the kernel reads the count); <= B Hv NC < 2^31
+    // (checked by the caller)
+    const int64_t items = int64_t(p.B) * p.Hk * p.NC;
     const dim3 grid((unsigned)std::min<int64_t>(items, prep_workgroups()));
-    if (beta_bf16)
-      hipLaunchKernelGGL((gdr_prep_keyhead<__bf16>), grid, dim3(256), 0, s, p, (int)items);
-    else
-      hipLaunchKernelGGL((gdr_prep_keyhead<float>), grid, dim3(256), 0, s, p, (int)items);
+    if (p.chunk_list) {
+      hipLaunchKernelGGL(gdr_chunk_list, dim3(1), dim3(256), 0, s, p.lengths, p.B, p.L, p.NC, p.chunk_list);
+      if (beta_bf16)
+        hipLaunchKernelGGL((gdr_prep_keyhead<__bf16, true>), grid, dim3(256), 0, s, p, (int)items);
+      else
+        hipLaunchKernelGGL((gdr_prep_keyhead<float, true>), grid, dim3(256), 0, s, p, (int)items);
+    } else if (beta_bf16) {
+      hipLaunchKernelGGL((gdr_prep_keyhead<__bf16, false>), grid, dim3(256), 0, s, p, (int)items);
+    } else {
+      hipLaunchKernelGGL((gdr_prep_keyhead<float, false>), grid, dim3(256), 0, s, p, (int)items);
+    }
   } else {
     const dim3 grid(p.B * p.Hv * p.NC);
     hipLaunchKernelGGL((gdr_prep<float, float>), grid, dim3(256), 0, s, p);

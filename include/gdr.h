@@ -79,9 +79,10 @@ typedef struct {
 /* Bytes of device workspace gdr_prefill needs for this shape (0 when B*L == 0), or
  * (size_t)-1 when the descriptor itself is invalid (see gdr_last_error). The workspace holds
  * per-chunk intermediates (the chunk's inverse T*diag(beta), the decayed causal q.k scores
- * and per-token scalars) and, for bf16 sequences long enough to be cut into segments that are
- * scanned in parallel, each segment's state map and entering state. Every call writes all of
- * it before reading it. */
+ * and per-token scalars), for bf16 sequences long enough to be cut into segments that are
+ * scanned in parallel each segment's state map and entering state, and (bf16) the list of the
+ * chunks that hold valid tokens when lengths are given. Every call writes what it reads before
+ * reading it. */
 size_t gdr_prefill_workspace_size(const gdr_desc* desc);
 
 /* Host-only validation of a gdr_prefill call (same arguments, no stream). Touches no GPU. */

@@ -91,10 +91,13 @@ def test_workspace_size():
     # bf16 sequences are cut into P segments scanned in parallel (P = ceil(256 / (B Hv)) capped
     # by the chunk count, then trimmed so no segment is empty), each with a 128 x 256 fp32 slot
     slot = 128 * 256 * 4
-    assert gdr.workspace_size(gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)) == 32 * 256 * rec_bf16 + 32 * 8 * slot
-    assert gdr.workspace_size(gdr.make_desc(1, 200, 1, 2, qkv_bf16=True)) == 2 * 4 * rec_bf16 + 2 * 4 * slot
-    assert gdr.workspace_size(gdr.make_desc(1, 640, 2, 100, qkv_bf16=True)) == 100 * 10 * rec_bf16 + 100 * 3 * slot
-    assert gdr.workspace_size(gdr.make_desc(64, 1024, 16, 32, qkv_bf16=True)) == 64 * 32 * 16 * rec_bf16
+    # bf16 also keeps a list of the chunks that hold valid tokens (used when lengths are given):
+    # an int32 count and one int32 per (row, chunk)
+    lst = lambda B, NC: 4 * (1 + B * NC)
+    assert gdr.workspace_size(gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)) == 32 * 256 * rec_bf16 + 32 * 8 * slot + lst(1, 256)
+    assert gdr.workspace_size(gdr.make_desc(1, 200, 1, 2, qkv_bf16=True)) == 2 * 4 * rec_bf16 + 2 * 4 * slot + lst(1, 4)
+    assert gdr.workspace_size(gdr.make_desc(1, 640, 2, 100, qkv_bf16=True)) == 100 * 10 * rec_bf16 + 100 * 3 * slot + lst(1, 10)
+    assert gdr.workspace_size(gdr.make_desc(64, 1024, 16, 32, qkv_bf16=True)) == 64 * 32 * 16 * rec_bf16 + lst(64, 16)
     assert gdr.workspace_size(gdr.make_desc(2, 130, 2, 4)) == 2 * 4 * 3 * rec_f32
     assert gdr.workspace_size(gdr.make_desc(0, 100, 1, 1)) == 0
     assert gdr.workspace_size(gdr.make_desc(3, 0, 1, 1)) == 0
