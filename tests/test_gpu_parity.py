@@ -102,6 +102,15 @@ def test_bf16_padded_segments():
     check(x, o, s, label="bf16 padded segments")
 
 
+def test_bf16_ragged_rows():
+    # sixteen ragged rows, some empty, one full: the chunk list of the prep, the pad loop of the
+    # output pass and the row-to-workgroup mapping together
+    lens = [200, 3, 64, 65, 0, 128, 199, 1, 150, 77, 100, 190, 12, 129, 63, 180]
+    x = draw(16, 200, 1, 2, 128, "R1", 509, torch.bfloat16, lengths=lens, s0_rows=16)
+    o, s = run_gpu(x)
+    check(x, o, s, label="bf16 ragged rows")
+
+
 def test_empty_sequence_copies_state():
     x = draw(2, 0, 2, 4, 128, "R1", 503, torch.float32, s0_rows=2)
     o, s = run_gpu(x)
