@@ -781,48 +781,75 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
       for (int e = 0; e < 4; ++e) S[st][e] = s0 ? s0[(16 * st + 4 * G + e) * D + ncol] : 0.f;
   }
 
-  for (int c = 0; c < p.NC; ++c) {
+  // Chunk staging, one chunk ahead: the global loads of chunk c + 1 are issued into registers right
+  // after chunk c's tiles are in LDS, and land while chunk c computes. Per thread: eight 16-byte
+  // pieces of K and of Q, six of the record's Tb and P operand blocks (12 blocks of 64 lanes x 8),
+  // four of V and (64 threads) one of the scalars.
+  f4 kr[8], qr[8], rr[6], vr[4], sr = f4_splat(0.f);
+  auto load = [&](int c) {
     const int t0 = c * C;
     const unsigned char* rec = wsb + (((size_t)b * p.Hv + h) * p.NC + c) * kRecF;
-    const float* recf = reinterpret_cast<const float*>(rec);
-    __syncthreads();   // the previous chunk is done with LDS
-    for (int idx = tid; idx < C * (D / 4); idx += NT) {
-      const int row = idx / (D / 4), cv = idx % (D / 4), t = t0 + row;
-      f4 kv = f4_splat(0.f), qv = f4_splat(0.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + NT * i, row = idx >> 5, cv = idx & 31, t = t0 + row;
+      kr[i] = qr[i] = f4_splat(0.f);
       if (t < p.L) {
         const size_t off = ((size_t)b * p.L + t) * p.Hk * D + (size_t)kh * D + 4 * cv;
-        kv = *reinterpret_cast<const f4*>(kg + off);
-        qv = *reinterpret_cast<const f4*>(qg + off);
+        kr[i] = *reinterpret_cast<const f4*>(kg + off);
+        qr[i] = *reinterpret_cast<const f4*>(qg + off);
       }
-      *reinterpret_cast<f4*>(&sm.k[row * kPK32 + 4 * cv]) = kv;
-      *reinterpret_cast<f4*>(&sm.q[row * kPK32 + 4 * cv]) = qv;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.kt[(4 * cv + e) * kPT32 + row] = kv[e];
+    for (int i = 0; i < 6; ++i) {   // block q >> 7 (Tb 0..5, P 6..11), lane (q & 127) >> 1, half q & 1
+      const int q = tid + NT * i;
+      rr[i] = *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(rec) + (q >> 7) * kBlockElems + ((q & 127) >> 1) * 8 +
+                                           4 * (q & 1));
     }
-    // Tb and P unpacked from operand blocks to full 64x64 (zeros above the stored blocks)
-    for (int idx = tid; idx < C * C; idx += NT) {
-      const int row = idx / C, col = idx % C;
-      const int w = row / 16, kb = col / 32;
-      float tv = 0.f, pv = 0.f;
-      if (kb <= w / 2) {
-        const int cc = col % 32, g = (cc % 16) / 4, j = (cc / 16) * 4 + cc % 4;
-        const int e = frag_block(w, kb) * kBlockElems + ((row % 16) + 16 * g) * 8 + j;
-        tv = recf[e];
-        pv = recf[kFragBlocks * kBlockElems + e];
-      }
-      sm.tb[row * kPT32 + col] = tv;
-      sm.pm[row * kPT32 + col] = pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, row = idx >> 4, cv = idx & 15, t = t0 + row;
+      vr[i] = t < p.L ? *reinterpret_cast<const f4*>(vg + ((size_t)b * p.L + t) * p.Hv * D + (size_t)h * D + col0 + 4 * cv)
+                      : f4_splat(0.f);
     }
-    for (int idx = tid; idx < C * (16 * NW / 4); idx += NT) {
-      const int row = idx / (16 * NW / 4), cv = idx % (16 * NW / 4), t = t0 + row;
-      f4 vv = f4_splat(0.f);
-      if (t < p.L) vv = *reinterpret_cast<const f4*>(vg + ((size_t)b * p.L + t) * p.Hv * D + (size_t)h * D + col0 + 4 * cv);
-      *reinterpret_cast<f4*>(&sm.v[row * kPT32 + 4 * cv]) = vv;
+    if (tid < C) sr = *reinterpret_cast<const f4*>(rec + 2 * kFragBlocks * kBlockElems * 4 + 16 * tid);
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + NT * i, row = idx >> 5, cv = idx & 31;
+      *reinterpret_cast<f4*>(&sm.k[row * kPK32 + 4 * cv]) = kr[i];
+      *reinterpret_cast<f4*>(&sm.q[row * kPK32 + 4 * cv]) = qr[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.kt[(4 * cv + e) * kPT32 + row] = kr[i][e];
     }
-    for (int idx = tid; idx < C; idx += NT)
-      *reinterpret_cast<f4*>(&sm.sc[4 * idx]) =
-          *reinterpret_cast<const f4*>(rec + 2 * kFragBlocks * kBlockElems * 4 + 16 * idx);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {   // lane (m, g) of block (tile I, kb): row 16 I + m, columns 32 kb + 4g (+16)
+      const int q = tid + NT * i, blk = q >> 7, bk = blk % kFragBlocks, ln = (q & 127) >> 1;
+      const int row = 16 * block_tile(bk) + (ln & 15), col = 32 * block_kb(bk) + 4 * (ln >> 4) + 16 * (q & 1);
+      *reinterpret_cast<f4*>(&(blk < kFragBlocks ? sm.tb : sm.pm)[row * kPT32 + col]) = rr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + NT * i, row = idx >> 4, cv = idx & 15;
+      *reinterpret_cast<f4*>(&sm.v[row * kPT32 + 4 * cv]) = vr[i];
+    }
+    if (tid < C) *reinterpret_cast<f4*>(&sm.sc[4 * tid]) = sr;
+  };
+  // Tb and P are zero above their stored blocks (rows 0..31, columns 32..63); the blocks never
+  // write there
+  for (int idx = tid; idx < 32 * 32; idx += NT) {
+    const int row = idx >> 5, col = 32 + (idx & 31);
+    sm.tb[row * kPT32 + col] = 0.f;
+    sm.pm[row * kPT32 + col] = 0.f;
+  }
+  if (p.NC > 0) load(0);
+
+  for (int c = 0; c < p.NC; ++c) {
+    const int t0 = c * C;
+    __syncthreads();   // the previous chunk is done with LDS
+    store();
     __syncthreads();
+    if (c + 1 < p.NC) load(c + 1);
 
     const float* sa = sm.sc;
     const float* scc = sm.sc + C;
