@@ -111,6 +111,17 @@ def test_bf16_ragged_rows():
     check(x, o, s, label="bf16 ragged rows")
 
 
+def test_bf16_many_ragged_rows():
+    # 300 ragged rows: the prep's chunk list is built over two blocks of 256 rows; rows on both
+    # sides of the block boundary, an empty one and a full one are checked against the oracle
+    rng = np.random.default_rng(510)
+    lens = rng.integers(0, 131, size=300).tolist()
+    lens[255], lens[256], lens[257] = 0, 130, 1
+    x = draw(300, 130, 1, 2, 128, "R1", 510, torch.bfloat16, lengths=lens, s0_rows=300)
+    o, s = run_gpu(x)
+    check(x, o, s, rows=[0, 1, 254, 255, 256, 257, 299], label="bf16 300 ragged rows")
+
+
 def test_empty_sequence_copies_state():
     x = draw(2, 0, 2, 4, 128, "R1", 503, torch.float32, s0_rows=2)
     o, s = run_gpu(x)
