@@ -621,8 +621,33 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
 // (tiles 2w, 2w + 1, plain row order) and the waves exchange the state each step as bf16
 // hi + lo operand pairs, so that with M = Mh + Ml the products Mh Sh + Mh Sl + Ml Sh keep
 // about 16 significant bits more than bf16 alone.
+//
+// Step jj reads this wave's 32 rows of M_jj (all 128 keys) and of the slice of B_jj; neither
+// depends on the chained state, so each wave copies them HBM->LDS by DMA two steps ahead into a
+// ring of two slots of its own (no other wave reads them, so no barrier guards them). In a slot the
+// 16-byte chunk q of M row r sits at position q ^ (r & 15): the sixteen rows that one operand read
+// touches then fall on distinct banks.
+struct CombineSmem {
+  unsigned char m[2][4][32 * 512];   // [slot][wave]: 32 rows of M_jj, 512 bytes each
+  unsigned char bs[2][4][32 * 64];   // [slot][wave]: 32 rows of the B_jj slice, 64 bytes each
+  bf16x8 sx[2][2][4][64];            // [step parity][hi, lo][wave][lane]: the state exchange
+};
+// Vector-memory operations this wave issues after the loads of step jj's slot, when that slot is
+// waited for: the loads of step jj + 1 (kCombineLoads, if any) and the state stores of the steps
+// in between (kCombineStores each).
+constexpr int kCombineLoads = 16 + 2, kCombineStores = 8;
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N == 0 || N == 8 || N == 16 || N == 18 || N == 26 || N == 34, "extend the list of encodings");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if constexpr (N == 26) asm volatile("s_waitcnt vmcnt(26)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(34)" ::: "memory");
+}
+
 __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
-  __shared__ bf16x8 sx[2][2][4][64];   // [step parity][hi, lo][wave][lane]
+  __shared__ __attribute__((aligned(16))) CombineSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, G = lane >> 4;
@@ -632,6 +657,9 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   if (row_is_bad(p, b, srow)) return;   // the output pass writes NaN for this row
   const int col = 16 * slice + n16;
   float* slots = p.seg + ((size_t)b * p.Hv + h) * p.P * kSlotFloats;
+  i32x4 rs = rsrc_words(slots, (uint32_t)(p.P * kSlotFloats * sizeof(float)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rs[i]);   // uniform: keep it in SGPRs
 
   f4 S[2];
   const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
@@ -643,92 +671,104 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
-  // Step jj reads M_jj (this wave's 32 rows, all 128 keys) and the slice of B_jj; neither depends on
-  // the chained state, so they are loaded kPf steps ahead (a ring of register sets, the loop
-  // unrolled by kPf). One step ahead measured fastest: a deeper ring puts part of it in AGPRs, and
-  // the copies out of them wait for the loads. With no initial state S_1 = B_0, which is already in
-  // its slot: the chain starts at step 1.
-  constexpr int kPf = 1;
-  f4 Mr[kPf][2][4][2], Br[kPf][2];
+  // With no initial state S_1 = B_0, which is already in its slot: the chain starts at step 1.
   const int steps = p.P - 1, first = p.s0 ? 0 : 1;
-#define GDR_COMBINE_LOAD(u, jj)                                                          \
-  do {                                                                                   \
-    const float* M = slots + (size_t)(jj) * kSlotFloats + D; /* M_jj, row pitch 2D */    \
-    const float* Bn = slots + (size_t)((jj) + 1) * kSlotFloats;                          \
-    _Pragma("unroll") for (int s2 = 0; s2 < 2; ++s2) {                                   \
-      _Pragma("unroll") for (int kb = 0; kb < 4; ++kb) {                                 \
-        const float* mrow = M + (32 * w + 16 * s2 + n16) * 2 * D + 32 * kb + 4 * G;      \
-        Mr[u][s2][kb][0] = *reinterpret_cast<const f4*>(mrow);                           \
-        Mr[u][s2][kb][1] = *reinterpret_cast<const f4*>(mrow + 16);                      \
-      }                                                                                  \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                      \
-        Br[u][s2][i] = Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];                 \
-    }                                                                                    \
-  } while (0)
-  if (!p.s0 && steps > 0) {   // S_1 = B_0
+  if (!p.s0 && steps > 0) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int i = 0; i < 4; ++i) S[s2][i] = slots[kSlotFloats + (32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
   }
+  // This wave's rows of M_jj (slot jj, columns 128..255; two rows per load) and of the B_jj slice
+  // (slot jj + 1, columns 16 slice ..; sixteen rows per load) into ring slot u.
+  auto issue = [&](int jj, int u) {
+    const uint32_t mbase = (uint32_t)jj * kSlotFloats * 4, bbase = (uint32_t)(jj + 1) * kSlotFloats * 4;
 #pragma unroll
-  for (int u = 0; u < kPf; ++u)
-    if (first + u < steps) GDR_COMBINE_LOAD(u, first + u);
-  for (int j0 = first; j0 < steps; j0 += kPf) {
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + (lane >> 5), pos = lane & 31;
+      dma16(rs, mbase + ((uint32_t)(32 * w + r) * 2 * D + D) * 4 + 16 * (pos ^ (r & 15)), sm.m[u][w] + 2 * i * 512);
+    }
 #pragma unroll
-    for (int u = 0; u < kPf; ++u) {
-      const int jj = j0 + u;
-      if (jj >= steps) break;   // uniform
-      float* Bn = slots + (size_t)(jj + 1) * kSlotFloats;   // B_jj, replaced by the state entering jj + 1
-      bf16x8 mh[2][4], ml[2][4];
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      dma16(rs, bbase + ((uint32_t)(32 * w + r) * 2 * D + 16 * slice + 4 * (lane & 3)) * 4, sm.bs[u][w] + 16 * i * 64);
+    }
+  };
+  // A wait the compiler sees: the state loads above are then known complete, so it places no wait
+  // for them inside the loop (where it would also stall on the slot loads in flight).
+  __builtin_amdgcn_s_waitcnt(0);
+  if (first < steps) issue(first, 0);
+  if (first + 1 < steps) issue(first + 1, 1);
+  for (int jj = first; jj < steps; ++jj) {
+    const int rel = jj - first, u = rel & 1;
+    const bool next = jj + 1 < steps;   // step jj + 1's loads were issued after this step's
+    if (rel == 0) {
+      if (next) wait_vm<kCombineLoads>(); else wait_vm<0>();
+    } else if (rel == 1) {
+      if (next) wait_vm<kCombineLoads + kCombineStores>(); else wait_vm<kCombineStores>();
+    } else {
+      if (next) wait_vm<kCombineLoads + 2 * kCombineStores>(); else wait_vm<2 * kCombineStores>();
+    }
+    bf16x8 mh[2][4], ml[2][4];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const f4 m0 = Mr[u][s2][kb][0], m1 = Mr[u][s2][kb][1];
-          mh[s2][kb] = pack8(m0, m1);
-          f4 r0, r1;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            r0[i] = m0[i] - (float)mh[s2][kb][i];
-            r1[i] = m1[i] - (float)mh[s2][kb][4 + i];
-          }
-          ml[s2][kb] = pack8(r0, r1);
-        }
-      const f4 Bv[2] = {Br[u][0], Br[u][1]};
-      if (jj + kPf < steps) GDR_COMBINE_LOAD(u, jj + kPf);
-      {
-        const bf16x8 hi = pack8(S[0], S[1]);
+      for (int kb = 0; kb < 4; ++kb) {
+        const unsigned char* mrow = sm.m[u][w] + (16 * s2 + n16) * 512;
+        const f4 m0 = *reinterpret_cast<const f4*>(mrow + 16 * ((8 * kb + G) ^ n16));
+        const f4 m1 = *reinterpret_cast<const f4*>(mrow + 16 * ((8 * kb + 4 + G) ^ n16));
+        mh[s2][kb] = pack8(m0, m1);
         f4 r0, r1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          r0[i] = S[0][i] - (float)hi[i];
-          r1[i] = S[1][i] - (float)hi[4 + i];
+          r0[i] = m0[i] - (float)mh[s2][kb][i];
+          r1[i] = m1[i] - (float)mh[s2][kb][4 + i];
         }
-        sx[jj & 1][0][w][lane] = hi;
-        sx[jj & 1][1][w][lane] = pack8(r0, r1);
+        ml[s2][kb] = pack8(r0, r1);
       }
-      lds_barrier();   // the state exchange is in LDS; the loads of later steps stay in flight
-      f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
+    f4 Bv[2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 sh = sx[jj & 1][0][kb][lane], sl = sx[jj & 1][1][kb][lane];
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          acc[s2] = mfma(mh[s2][kb], sh, acc[s2]);
-          acc[s2] = mfma(mh[s2][kb], sl, acc[s2]);
-          acc[s2] = mfma(ml[s2][kb], sh, acc[s2]);
-        }
+      for (int i = 0; i < 4; ++i)
+        Bv[s2][i] = *reinterpret_cast<const float*>(sm.bs[u][w] + (16 * s2 + 4 * G + i) * 64 + 4 * n16);
+    if (jj + 2 < steps) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave is done reading slot u
+      issue(jj + 2, u);
+    }
+    {
+      const bf16x8 hi = pack8(S[0], S[1]);
+      f4 r0, r1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r0[i] = S[0][i] - (float)hi[i];
+        r1[i] = S[1][i] - (float)hi[4 + i];
       }
+      sm.sx[jj & 1][0][w][lane] = hi;
+      sm.sx[jj & 1][1][w][lane] = pack8(r0, r1);
+    }
+    lds_barrier();   // the state exchange is in LDS; the loads of later steps stay in flight
+    f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 sh = sm.sx[jj & 1][0][kb][lane], sl = sm.sx[jj & 1][1][kb][lane];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        S[s2] = acc[s2] + Bv[s2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+        acc[s2] = mfma(mh[s2][kb], sh, acc[s2]);
+        acc[s2] = mfma(mh[s2][kb], sl, acc[s2]);
+        acc[s2] = mfma(ml[s2][kb], sh, acc[s2]);
       }
     }
+    // the state entering segment jj + 1, over B_jj in slot jj + 1: exactly kCombineStores stores
+    float* Bn = slots + (size_t)(jj + 1) * kSlotFloats;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      S[s2] = acc[s2] + Bv[s2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+    }
   }
-#undef GDR_COMBINE_LOAD
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load into LDS may be in flight at the end
 }
 
 // ====================================================================== fp32 scan
