@@ -16,10 +16,11 @@
 // from in-chunk differences), so nothing over- or underflows however strong the decay.
 //
 // bf16 (gdr_prep_keyhead): persistent workgroups, each walking work items (row b, key head kh,
-// chunk c) with the next item's K rows and gates loaded into registers while the current item
-// computes. The Gram K K^T is formed once per item and shared by the Hv / Hk value heads of the
-// key head, each of which then gets its own A, inverse and record. q is not read: the output
-// pass forms the q norms from the Q tile it stages anyway.
+// chunk c) with the next item's K rows (HBM->LDS by DMA) and gates (into registers) in flight
+// while the current item computes. The Gram K K^T is formed once per item and shared by the
+// Hv / Hk value heads of the key head, each of which then gets its own A, inverse and record. q is
+// not read: the output pass forms the q norms from the Q tile it stages anyway. With lengths the
+// items are only the chunks that hold valid tokens (gdr_chunk_list).
 //
 // float32 (gdr_prep): one workgroup (4 waves) per (row b, value head h, chunk c).
 //

@@ -10,13 +10,16 @@
 // bf16: segment-parallel. The map from the state entering a run of chunks to the state leaving
 // it is affine, S -> M S + B, with M independent of the values. The chunks of each (row, head)
 // are cut into P segments; gdr_transition_bf16 runs every segment but the last from the
-// augmented start [identity | 0] (giving M_j and B_j), gdr_combine chains
+// augmented start [0 | identity] (giving B_j and M_j), gdr_combine chains
 // S_{j+1} = M_j S_j + B_j over the segments, and gdr_scan_bf16 runs every segment again from
 // its true entering state, writing outputs (and, for the last one, the final state). With
-// P = 1 only gdr_scan_bf16 runs.
+// P = 1 only gdr_scan_bf16 runs. Chunks wholly past a row's length (right pads: beta' = g' = 0)
+// are the identity map: the transitions skip them and the output pass gives them a short loop of
+// their own (O = diag(rq) Q S).
 //
 // gdr_scan_f32: float32 inputs; one workgroup per (row, value head, 64-column slice), each wave
-// owning 16 columns and walking all chunks on its own (fp32 MFMA, K^T staged in LDS).
+// owning 16 columns and walking all chunks on its own (fp32 MFMA, K^T staged in LDS, each chunk
+// loaded into registers one chunk ahead).
 #include "gdr_device.h"
 
 namespace gdr {
@@ -33,8 +36,8 @@ constexpr int kRecBlocks = kRecB / 1024;                               // 1 KiB 
 constexpr int kBufK = C * D * 2;                                       // one 64x128 bf16 tile
 
 // LDS staging of one chunk (every wave reads every part of it): K, V (and Q) tiles of 64 rows x
-// 256 bytes, swizzled as below, and the record as written by the prep kernel. Two buffers: chunk c + 1 is loaded while chunk c is
-// computed.
+// 256 bytes, swizzled as below, and the record as written by the prep kernel. Two buffers: chunk
+// c + 1 is loaded while chunk c is computed.
 #ifndef GDR_SEG_WAVES_OUT
 #define GDR_SEG_WAVES_OUT 8
 #endif
