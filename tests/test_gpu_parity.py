@@ -79,6 +79,15 @@ def test_no_head_sharing_and_ratio_4():
         check(x, o, s, label=f"Hk={Hk} Hv={Hv}")
 
 
+def test_eight_value_heads_per_key_head():
+    # more than four value heads share a key head: the prep forms their records in two batches
+    # of gates (both dtypes, with ragged rows and initial states)
+    for dtype in (torch.bfloat16, torch.float32):
+        x = draw(2, 150, 1, 8, 128, "R1", 511, dtype, lengths=[150, 70], s0_rows=2)
+        o, s = run_gpu(x)
+        check(x, o, s, label=f"Hk=1 Hv=8 {dtype}")
+
+
 def test_bf16_beta():
     x = draw(1, 200, 2, 4, 128, "R1", 501, torch.bfloat16)
     x.beta = x.beta.to(torch.bfloat16)
