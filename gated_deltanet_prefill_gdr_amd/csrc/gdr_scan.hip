@@ -44,6 +44,9 @@ constexpr int kBufK = C * D * 2;                                       // one 64
 #ifndef GDR_SEG_WAVES_TRANSITION
 #define GDR_SEG_WAVES_TRANSITION 8
 #endif
+// Right-pad chunks of the output pass without the fused norm are taken kPadGroup at a time: their Q
+// tiles fill the Q, K and V regions of one buffer while the next group loads into the other.
+constexpr int kPadGroup = 3;
 template <bool kOut> struct SegCfg {
   static constexpr int NW = kOut ? GDR_SEG_WAVES_OUT : GDR_SEG_WAVES_TRANSITION;   // waves per workgroup
   static constexpr int NSL = (kOut ? 8 : 16) / NW;      // 16-column slices per wave
@@ -57,7 +60,7 @@ template <bool kOut> struct SegCfg {
   static constexpr int kP = 2 * kBuf;
   static constexpr int kPart = kP + kFragBlocks * 1024;
   static constexpr int kRq = kPart + 2 * NW * C * 4;    // outputs only: |q_t|^2 of the chunk's tokens
-  static constexpr int kLds = kOut ? kRq + C * 4 : 2 * kBuf;
+  static constexpr int kLds = kOut ? kRq + kPadGroup * C * 4 : 2 * kBuf;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
   static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
 };
@@ -74,10 +77,11 @@ __device__ __forceinline__ int swz_z(int row, int chunk16) { return row * 256 + 
 // LDS accesses are done, then meet the other waves. Memory clobbers keep every LDS access on
 // its side of the wait and the barrier.
 template <int N> __device__ __forceinline__ void wait_and_barrier() {
-  static_assert(N == 0 || N == 4 || N == 8, "extend the list of encodings");   // stores per chunk
+  static_assert(N == 0 || N == 4 || N == 8 || N == 12, "extend the list of encodings");   // stores
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // 1 / (1 + e^-x) with the hardware exp2 and reciprocal
@@ -230,6 +234,23 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       if (kOut && p.z) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
     }
   };
+  // Q tiles of the pad chunks c0 .. c0 + kPadGroup - 1 (those before c_end) into the Q, K and V
+  // regions of buffer bi (outputs without the fused norm)
+  auto issue_qg = [&](int c0, int bi) {
+    unsigned char* Bf = lds + bi * Cfg::kBuf;
+#pragma unroll
+    for (int i = 0; i < kPadGroup; ++i) {
+      if (c0 + i >= c_end) break;   // uniform
+      const int region = i == 0 ? Cfg::kQ : (i == 1 ? Cfg::kK : Cfg::kV);
+      const uint32_t t0 = (uint32_t)(c0 + i) * C;
+#pragma unroll
+      for (int m = 0; m < R / 4; ++m) {
+        const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
+        const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
+        if constexpr (kOut) dma16(rq, kq, Bf + region + (R * w + 4 * m) * 256);
+      }
+    }
+  };
   // chunks c_begin .. c_mid - 1 hold valid tokens; c_mid .. c_end - 1 are right pads
   const int c_mid = min(max((len_b + C - 1) / C, c_begin), c_end);
 
@@ -277,7 +298,6 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   // Ot: the chunk's outputs; sz: w silu(z) of the same lanes' elements, formed from the gate rows
   // staged with the chunk while the chunk computes.
   f4 Ot[4][NSL], sz[4][NSL];
-  const bool fuse = kOut && p.z != nullptr;
   float* part = reinterpret_cast<float*>(lds + Cfg::kPart);   // [2][NW][64]
   auto store_tile = [&](int c, int mt) {
     const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
@@ -305,10 +325,13 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     store_o(c);
   };
 
+  const bool fuse = kOut && p.z != nullptr;
   if (c_begin < c_mid)
     issue(c_begin, kStAll);
-  else if (c_begin < c_end)
+  else if (c_begin < c_end && fuse)
     issue_q(c_begin);
+  else if (c_begin < c_end)
+    issue_qg(c_begin, c_begin & 1);
   wait_and_barrier<0>();
   // The same wait as a builtin the compiler sees: the entering-state loads are then known complete,
   // so it places no wait for them inside the loop (where it would also stall on the next chunk's
@@ -368,8 +391,10 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // prefill). The transitions, which form no P, issue it all here.
     if (c + 1 < c_mid)
       issue(c + 1, kOut ? kStK : kStAll);
-    else if (kOut && c + 1 < c_end)
+    else if (kOut && c + 1 < c_end && fuse)
       issue_q(c + 1);
+    else if (kOut && c + 1 < c_end)
+      issue_qg(c + 1, (c + 1) & 1);
     const bool stage_next = kOut && c + 1 < c_mid;
 
     const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
@@ -541,12 +566,57 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
-    for (int c = c_mid; c < c_end; ++c) {
-      if (fuse)
-        wait_and_barrier<0>();
-      else
-        wait_and_barrier<Cfg::kStores>();
-      if (fuse && c > c_begin) finish_norm(c - 1);
+    if (!fuse) {
+      // groups of kPadGroup chunks, group g in buffer (c_mid + g) & 1; after a group's loads come
+      // the stores of the chunk or group before it (none when the segment starts in the pads: its
+      // first group was waited for before the main loop)
+      float* rqg = reinterpret_cast<float*>(lds + Cfg::kRq);   // [kPadGroup][64]: |q_t|^2
+      for (int c0 = c_mid, g = 0; c0 < c_end; c0 += kPadGroup, ++g) {
+        const int bi = (c_mid + g) & 1, n = min(kPadGroup, c_end - c0);
+        if (g == 0)
+          wait_and_barrier<Cfg::kStores>();
+        else
+          wait_and_barrier<kPadGroup * Cfg::kStores>();
+        if (c0 + kPadGroup < c_end) issue_qg(c0 + kPadGroup, bi ^ 1);
+        const unsigned char* Bq = lds + bi * Cfg::kBuf;
+        for (int pr = w; pr < 4 * n; pr += NW) {   // q norms of (chunk pr / 4, token tile pr % 4)
+          const int i = pr >> 2, mt = pr & 3;
+          const unsigned char* Qt = Bq + (i == 0 ? Cfg::kQ : (i == 1 ? Cfg::kK : Cfg::kV));
+          f4 qq = f4_splat(0.f);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+            qq = mfma(qf, qf, qq);
+          }
+          if ((n16 >> 2) == G) {
+            const int e = n16 & 3;
+            rqg[64 * i + 16 * mt + n16] = e == 0 ? qq[0] : e == 1 ? qq[1] : e == 2 ? qq[2] : qq[3];
+          }
+        }
+        lds_barrier();
+        for (int i = 0; i < n; ++i) {
+          const unsigned char* Qt = Bq + (i == 0 ? Cfg::kQ : (i == 1 ? Cfg::kK : Cfg::kV));
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = f4_splat(0.f);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+              for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
+            }
+            const float rqv = __builtin_amdgcn_rsqf(rqg[64 * i + 16 * mt + n16] + 1e-6f) * 0.08838834764831845f;
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rqv;
+            store_tile(c0 + i, mt);
+          }
+        }
+      }
+    }
+    for (int c = c_mid; fuse && c < c_end; ++c) {
+      wait_and_barrier<0>();
+      if (c > c_begin) finish_norm(c - 1);
       if (c + 1 < c_end) issue_q(c + 1);
       const unsigned char* Qt = lds + (c & 1) * Cfg::kBuf + Cfg::kQ;
       if (w < 4) {   // q norms of token tile w
@@ -571,7 +641,6 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
         }
         finish_rows(mt, c, lds + (c & 1) * Cfg::kBuf);
       }
-      if (!fuse) store_o(c);
     }
   }
   if (fuse && c_end > c_begin) {   // the last chunk's norm: its partial sums, then store
