@@ -176,7 +176,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
   // Chunks entirely past the row's length (right pads: beta' = g' = 0) leave the state unchanged
   // and give O = diag(rq) Q S: only their Q tile (and gate rows) is staged and only the output
-  // products run.
+  // products run, after the other chunks (three at a time without the fused norm).
   int len_b = p.lengths ? p.lengths[b] : p.L;
   len_b = len_b < 0 ? 0 : (len_b > p.L ? p.L : len_b);
   const uint32_t kq_row = (uint32_t)p.Hk * D * 2, vo_row = (uint32_t)p.Hv * D * 2;
@@ -222,7 +222,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       }
     }
   };
-  // a chunk past the row's length (outputs only): its Q rows and, with the fused norm, gate rows
+  // a chunk past the row's length (outputs with the fused norm): its Q rows and gate rows
   auto issue_q = [&](int c) {
     unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
     const uint32_t t0 = (uint32_t)c * C;
