@@ -336,7 +336,7 @@ def main():
                     help="seconds of untimed steps before the warm-up (0 for counter runs)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -60,7 +60,7 @@ extern "C" {
 typedef enum {
   GDR_OK = 0,
   GDR_EINVAL = -1,        /* a null, misaligned, overlapping or inconsistent argument */
-  GDR_EUNSUPPORTED = -2,  /* a valid request this build does not implement (Dk, Dv != 128) */
+  GDR_EUNSUPPORTED = -2,  /* a valid request the library does not implement (Dk, Dv != 128) */
   GDR_EWORKSPACE = -3,    /* workspace missing or smaller than gdr_prefill_workspace_size */
   GDR_EHIP = -4           /* the HIP runtime reported an error while launching */
 } gdr_status;
