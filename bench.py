@@ -270,7 +270,7 @@ def bench_layer(a):
 
 
 def bench_all_configs(a):
-    """Every named workload (configs 1..5): median call time over 50 calls after 10 warm-up calls
+    """Every named workload of workloads.CONFIGS: median call time over 50 calls after 10 warm-up calls
     (HIP events around each call, inputs resident), throughput, TFLOP/s, algorithmic GB/s and
     both roofline fractions. One JSON line per config; a report, not the step metric."""
     import statistics
