@@ -30,12 +30,13 @@
 //   2. Gram tiles on MFMA, balanced over the waves: wave w forms the K K^T tiles of row 3 - w and
 //      (float32) the K Q^T tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator
 //      layout is exactly the operand layout of P, so P goes from registers straight to the record;
-//   3. A (fp32) into LDS over the staging area;
+//   3. A (fp32) into LDS (float32: over the staging area);
 //   4. T of the four 16x16 diagonal blocks by forward substitution, one lane per column, all in
-//      registers (wave 0);
+//      registers (one wave per value head), written over A;
 //   5. off-diagonal blocks by the 2x2 block rule T_BA = -T_BB A_BA T_AA, first within each
-//      32-row half (T_10, T_32), then across the halves, on fp32 MFMA;
+//      32-row half (T_10, T_32), then across the halves, on fp32 MFMA, each written over A;
 //   6. Tb = T diag(beta') gathered into operand order.
+// The bf16 prep runs phases 3-6 for two value heads of a key head at once.
 #include <algorithm>
 
 #include "gdr_device.h"
@@ -45,66 +46,92 @@ namespace gdr {
 template <typename T> struct PrepLayout;
 template <> struct PrepLayout<__bf16> { static constexpr int PK = D + 8; };   // 272-byte rows
 template <> struct PrepLayout<float> { static constexpr int PK = D + 4; };    // 528-byte rows
-constexpr int kFP = C + 4;   // pitch of the fp32 64x64 matrices A and T
+
+// The fp32 64x64 matrices A and T live in LDS as their ten lower 16x16 blocks (I >= J), block (I, J)
+// at kBlk (I (I + 1) / 2 + J) floats. In a block, row r = 4a + b, column c sits at
+// moff(r, c) = 64 a + 16 ((a + b) & 3) + 4 ((c >> 2) ^ a) + (c & 3): the 16 rows of one operand read
+// (four consecutive columns each) and the rows 4G + s of one accumulator-layout access each hit
+// the 64 banks once. kBlk = 260 rather than 256 puts the four diagonal blocks, which the forward
+// substitution reads at one address per block, in different banks.
+constexpr int kBlk = 260;
+constexpr int kMatFloats = 10 * kBlk;
+__device__ __forceinline__ int moff(int r, int c) {
+  const int a = r >> 2, b = r & 3;
+  return 64 * a + 16 * ((a + b) & 3) + 4 * ((c >> 2) ^ a) + (c & 3);
+}
 
 template <typename T>
 struct PrepSmem {
   static constexpr int PK = PrepLayout<T>::PK;
   union {
     struct { T k[C * PK]; T q[C * PK]; } in;   // phases 1-2
-    struct { float a[C * kFP]; float t[C * kFP]; } m;   // phases 3-6
+    float a[kMatFloats];   // phases 3-6: A, then T over it
   } u;
   float rk[C], rq[C], gam[C], bet[C];
 };
 
 // fp32 16x16 tile product with the k index of step s, lane group G standing for 4G + s: the A
-// operand is row m of a row-major LDS tile (one 16-byte read per lane), the B operand the
-// accumulator layout of the right factor (element s of lane (n, G) is row 4G + s).
-__device__ __forceinline__ void mma_lds_acc(f4& acc, const float* a_tile, int n16, int G, const f4& b) {
-  const f4 av = *reinterpret_cast<const f4*>(a_tile + n16 * kFP + 4 * G);
+// operand av is row n16 of the left tile (tile_row: one 16-byte LDS read per lane), the B operand
+// the accumulator layout of the right factor (element s of lane (n, G) is row 4G + s).
+__device__ __forceinline__ void mma_acc(f4& acc, const f4& av, const f4& b) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[s], b[s], acc, 0, 0, 0);
 }
-// The right factor in accumulator layout, read from a row-major LDS tile.
+// The A operand of such a product: row n16, columns 4G .. 4G + 3 of an LDS block.
+__device__ __forceinline__ f4 tile_row(const float* a_tile, int n16, int G) {
+  return *reinterpret_cast<const f4*>(a_tile + moff(n16, 4 * G));
+}
+__device__ __forceinline__ void mma_lds_acc(f4& acc, const float* a_tile, int n16, int G, const f4& b) {
+  mma_acc(acc, tile_row(a_tile, n16, G), b);
+}
+// The right factor in accumulator layout, read from an LDS block.
 __device__ __forceinline__ f4 tile_acc(const float* tile, int n16, int G) {
   f4 x;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) x[s] = tile[(4 * G + s) * kFP + n16];
+  for (int s = 0; s < 4; ++s) x[s] = tile[moff(4 * G + s, n16)];
   return x;
 }
 __device__ __forceinline__ void store_acc(float* tile, int n16, int G, const f4& x) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) tile[(4 * G + s) * kFP + n16] = x[s];
+  for (int s = 0; s < 4; ++s) tile[moff(4 * G + s, n16)] = x[s];
 }
-__device__ __forceinline__ const float* blk(const float* m, int I, int J) { return m + 16 * I * kFP + 16 * J; }
-__device__ __forceinline__ float* blk(float* m, int I, int J) { return m + 16 * I * kFP + 16 * J; }
+__device__ __forceinline__ const float* blk(const float* m, int I, int J) { return m + kBlk * (I * (I + 1) / 2 + J); }
+__device__ __forceinline__ float* blk(float* m, int I, int J) { return m + kBlk * (I * (I + 1) / 2 + J); }
 
-// Phase 2 of wave W: the Gram tiles, and (float32 records) P into the record. Kept a template on W
-// so that every tile choice is fixed at compile time. bf16 records carry no P: the output pass
-// forms it from the Q and K tiles it stages anyway, so only K K^T is formed here.
+// The lower 16x16 tiles (I, J) of K K^T that wave W forms and scales into A: its diagonal tile
+// (3 - W, 3 - W) first (the row norms come from its diagonal), then 2, 2, 1, 1 of the six tiles
+// below the diagonal, so that the Gram and A work is spread evenly over the four waves.
+template <int W> struct GramTiles;
+template <> struct GramTiles<0> { static constexpr int n = 3, I[3] = {3, 3, 3}, J[3] = {3, 0, 1}; };
+template <> struct GramTiles<1> { static constexpr int n = 3, I[3] = {2, 3, 2}, J[3] = {2, 2, 0}; };
+template <> struct GramTiles<2> { static constexpr int n = 2, I[3] = {1, 2, 0}, J[3] = {1, 1, 0}; };
+template <> struct GramTiles<3> { static constexpr int n = 2, I[3] = {0, 1, 0}, J[3] = {0, 0, 0}; };
+
+// Phase 2 of wave W (float32): the Gram tiles of GramTiles<W>, gk[t][e] = (K K^T)[16 I_t + 4G + e]
+// [16 J_t + n16], and P into the record (bf16 records carry no P: the output pass forms it from the
+// Q and K tiles it stages anyway). Kept a template on W so that every tile choice is fixed at
+// compile time.
 template <int W, typename T, int PK>
 __device__ __forceinline__ void gram_phase(const T* ks, const T* qs, const float* gam2, const float* rk,
                                            const float* rq, int n16, int G, int lane, unsigned char* pbase,
-                                           f4 (&gk)[4]) {
+                                           f4 (&gk)[3]) {
+  using TL = GramTiles<W>;
   constexpr bool kP = sizeof(T) == 4;
-  constexpr int Ik = 3 - W, Iq = kP ? W : -1;
+  constexpr int Iq = kP ? W : -1;
   f4 gq[4];
 #pragma unroll
-  for (int J = 0; J < 4; ++J) {
-    gk[J] = f4_splat(0.f);
-    gq[J] = f4_splat(0.f);
-  }
+  for (int J = 0; J < 4; ++J) gq[J] = f4_splat(0.f);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) gk[t] = f4_splat(0.f);
 #pragma unroll
   for (int kb = 0; kb < D / 32; ++kb) {
-    const Frag<T> ak = lds_frag(ks, PK, 16 * Ik + n16, 32 * kb, G);
     const Frag<T> bq = lds_frag(qs, PK, 16 * (kP ? Iq : 0) + n16, 32 * kb, G);
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
-      if (J > Ik && J > Iq) continue;
-      const Frag<T> kj = lds_frag(ks, PK, 16 * J + n16, 32 * kb, G);
-      if (J <= Ik) mma(gk[J], ak, kj);   // (K K^T)[16 Ik + 4G + e][16 J + n16]
-      if (J <= Iq) mma(gq[J], kj, bq);   // (K Q^T)[16 J + 4G + e][16 Iq + n16] = P^T
-    }
+    for (int t = 0; t < TL::n; ++t)
+      mma(gk[t], lds_frag(ks, PK, 16 * TL::I[t] + n16, 32 * kb, G), lds_frag(ks, PK, 16 * TL::J[t] + n16, 32 * kb, G));
+#pragma unroll
+    for (int J = 0; J <= Iq; ++J)   // (K Q^T)[16 J + 4G + e][16 Iq + n16] = P^T
+      mma(gq[J], lds_frag(ks, PK, 16 * J + n16, 32 * kb, G), bq);
   }
   if constexpr (!kP) return;
   // P[t][i], t = 16 Iq + n16, i = 16 J + 4G + e; each lane writes its eight slots of block (Iq, kb)
@@ -137,59 +164,78 @@ __device__ __forceinline__ void gram_phase(const T* ks, const T* qs, const float
   }
 }
 
-// Phase 3 of wave W: its K K^T tiles (row I = 3 - W) scaled into A.
+// Phase 3 of wave W: its K K^T tiles (GramTiles<W>) scaled into A.
 template <int W>
 __device__ __forceinline__ void a_phase(float* A, const float* gam2, const float* rk, const float* bet, int n16, int G,
-                                        const f4 (&gk)[4]) {
-  constexpr int I = 3 - W;
-  const f4 gr = *reinterpret_cast<const f4*>(gam2 + 16 * I + 4 * G);
-  const f4 rr = *reinterpret_cast<const f4*>(rk + 16 * I + 4 * G);
-  const f4 br = *reinterpret_cast<const f4*>(bet + 16 * I + 4 * G);
+                                        const f4 (&gk)[3]) {
+  using TL = GramTiles<W>;
 #pragma unroll
-  for (int J = 0; J <= I; ++J) {
+  for (int t = 0; t < TL::n; ++t) {
+    const int I = TL::I[t], J = TL::J[t];
+    const f4 gr = *reinterpret_cast<const f4*>(gam2 + 16 * I + 4 * G);
+    const f4 rr = *reinterpret_cast<const f4*>(rk + 16 * I + 4 * G);
+    const f4 br = *reinterpret_cast<const f4*>(bet + 16 * I + 4 * G);
     const int col = 16 * J + n16;
     const float gc = gam2[col], rc = rk[col];
+    float* ab = blk(A, I, J);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int row = 16 * I + 4 * G + e;
-      const float x = br[e] * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * rr[e] * rc * gk[J][e];
-      A[row * kFP + col] = row > col ? x : 0.f;
+      const float x = br[e] * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * rr[e] * rc * gk[t][e];
+      ab[moff(4 * G + e, n16)] = row > col ? x : 0.f;
     }
   }
 }
 
-// Phases 3-6 for one value head: A from the Gram tiles gk of this wave (row 3 - wave), the
-// blocked inverse in Amat / Tmat (64 x kFP floats each), and Tb into the record at rec. Four
-// barriers; on return every wave may still be reading Tmat (phase 6), so Amat may be rewritten
-// at once but Tmat only after a barrier.
-template <typename T>
-__device__ __forceinline__ void inverse_to_record(float* Amat, float* Tmat, const float* gam, const float* rk,
-                                                  const float* bet, const f4 (&gk)[4], int wave, int n16, int G,
-                                                  int lane, unsigned char* rec) {
+// Phases 3-6 for nh = 1 or 2 value heads at once (the second head's work interleaves with the
+// first's, so the pair costs about the latency of one): A of head j from the Gram tiles gk of this
+// wave (GramTiles) into M[j] (kMatFloats floats), the blocked inverse T = (I + A)^-1 in place over
+// A, and Tb into the record rec[j]. In place is safe because every block of A is read for the last
+// time before the barrier that precedes its overwrite (A_21 and A_31, still needed after the blocks
+// of the same phase are written, are read into registers one phase early). While waves 0 and 1
+// solve the diagonal blocks, waves 2 and 3 call idle(j) for head j = wave - 2 < nh. Four barriers;
+// on return every wave may still be reading M (phase 6), so M may be rewritten only after a barrier.
+// (Heads are passed as pointer pairs: a local array of LDS addresses would become a static
+// initializer, which the device compiler rejects.)
+template <typename T, typename Idle>
+__device__ __forceinline__ void inverse_to_records(float* M0, float* M1, const float* gam0, const float* gam1,
+                                                   const float* rk, const float* bet0, const float* bet1,
+                                                   const f4 (&gk)[3], int nh, int wave, int n16, int G, int lane,
+                                                   unsigned char* rec0, unsigned char* rec1, Idle&& idle) {
+  auto M = [&](int j) { return j ? M1 : M0; };
+  auto gam = [&](int j) { return j ? gam1 : gam0; };
+  auto bet = [&](int j) { return j ? bet1 : bet0; };
   // ---- 3. A, strictly lower, fp32
-  switch (wave) {
-    case 0: a_phase<0>(Amat, gam, rk, bet, n16, G, gk); break;
-    case 1: a_phase<1>(Amat, gam, rk, bet, n16, G, gk); break;
-    case 2: a_phase<2>(Amat, gam, rk, bet, n16, G, gk); break;
-    default: a_phase<3>(Amat, gam, rk, bet, n16, G, gk); break;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j >= nh) break;
+    switch (wave) {
+      case 0: a_phase<0>(M(j), gam(j), rk, bet(j), n16, G, gk); break;
+      case 1: a_phase<1>(M(j), gam(j), rk, bet(j), n16, G, gk); break;
+      case 2: a_phase<2>(M(j), gam(j), rk, bet(j), n16, G, gk); break;
+      default: a_phase<3>(M(j), gam(j), rk, bet(j), n16, G, gk); break;
+    }
   }
   lds_barrier();
 
-  // ---- 4. diagonal blocks: lane 16 w' + j solves column j of block w' (wave 0), column k of the
-  //         block read from LDS at step k (one address per block, broadcast over its 16 lanes)
-  if (wave == 0) {
-    const int o = 16 * G, j = n16;
-    const float* ablk = Amat + o * kFP + o;
+  // ---- 4. diagonal blocks of head `wave`: lane 16 w' + j solves column j of block w', column k of
+  //         the block read from LDS at step k (one address per block, broadcast over its 16
+  //         lanes); the column is written over the block once all of its reads are done
+  if (wave < nh) {
+    float* ablk = blk(M(wave), G, G);
+    const int j = n16;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
     for (int k = 0; k < 15; ++k) {
 #pragma unroll
-      for (int i = k + 1; i < 16; ++i) x[i] -= ablk[i * kFP + k] * x[k];
+      for (int i = k + 1; i < 16; ++i) x[i] -= ablk[moff(i, k)] * x[k];
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) Tmat[(o + i) * kFP + o + j] = x[i];
+    for (int i = 0; i < 16; ++i) ablk[moff(i, j)] = x[i];
+  } else if (wave >= 2 && wave - 2 < nh) {
+    idle(wave - 2);
   }
   lds_barrier();
 
@@ -198,54 +244,66 @@ __device__ __forceinline__ void inverse_to_record(float* Amat, float* Tmat, cons
   //         Across the halves (T_IJ for I in {2,3}, J in {0,1}), with Z = A_[23][01] T_[01][01]:
   //         T_2J = -T_22 Z_2J, T_3J = -(T_32 Z_2J + T_33 Z_3J); wave 2: T_20, wave 3: T_30,
   //         wave 0: T_21, wave 1: T_31.
-  const float* Am = Amat;
-  float* Tm = Tmat;
-  f4 pre0 = f4_splat(0.f), pre1 = f4_splat(0.f);
-  if (wave < 2) {
-    const int I = 2 * wave + 1, J = 2 * wave;   // (1, 0) or (3, 2)
-    f4 x = f4_splat(0.f);
-    mma_lds_acc(x, blk(Am, I, J), n16, G, tile_acc(blk(Tm, J, J), n16, G));
-    f4 y = f4_splat(0.f);
-    mma_lds_acc(y, blk(Tm, I, I), n16, G, x);
-    store_acc(blk(Tm, I, J), n16, G, -y);
-  } else {
-    const f4 t00 = tile_acc(blk(Tm, 0, 0), n16, G);
-    mma_lds_acc(pre0, blk(Am, 2, 0), n16, G, t00);            // A_20 T_00
-    if (wave == 3) mma_lds_acc(pre1, blk(Am, 3, 0), n16, G, t00);   // A_30 T_00
+  const bool row3 = (wave & 1) != 0;   // waves 1, 3 produce row 3 of the second step
+  f4 pre0[2], pre1[2], a21[2], a31[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    pre0[j] = pre1[j] = a21[j] = a31[j] = f4_splat(0.f);
+    if (j >= nh) break;
+    float* Mj = M(j);
+    a21[j] = tile_row(blk(Mj, 2, 1), n16, G);            // overwritten in the second step
+    if (row3) a31[j] = tile_row(blk(Mj, 3, 1), n16, G);
+    if (wave < 2) {
+      const int I = 2 * wave + 1, J = 2 * wave;   // (1, 0) or (3, 2)
+      f4 x = f4_splat(0.f);
+      mma_lds_acc(x, blk(Mj, I, J), n16, G, tile_acc(blk(Mj, J, J), n16, G));
+      f4 y = f4_splat(0.f);
+      mma_lds_acc(y, blk(Mj, I, I), n16, G, x);
+      store_acc(blk(Mj, I, J), n16, G, -y);
+    } else {
+      const f4 t00 = tile_acc(blk(Mj, 0, 0), n16, G);
+      mma_lds_acc(pre0[j], blk(Mj, 2, 0), n16, G, t00);            // A_20 T_00
+      if (wave == 3) mma_lds_acc(pre1[j], blk(Mj, 3, 0), n16, G, t00);   // A_30 T_00
+    }
   }
   lds_barrier();
-  {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j >= nh) break;
+    float* Mj = M(j);
     const int J = (wave >= 2) ? 0 : 1;
-    const bool row3 = (wave & 1) != 0;   // waves 1, 3 produce row 3
-    const f4 tj1 = tile_acc(blk(Tm, 1, J), n16, G);   // T_10 (J = 0) or T_11 (J = 1)
-    f4 z2 = pre0;                                      // Z_2J = A_20 T_0J + A_21 T_1J (T_01 = 0)
-    mma_lds_acc(z2, blk(Am, 2, 1), n16, G, tj1);
+    const f4 tj1 = tile_acc(blk(Mj, 1, J), n16, G);   // T_10 (J = 0) or T_11 (J = 1)
+    f4 z2 = pre0[j];                                   // Z_2J = A_20 T_0J + A_21 T_1J (T_01 = 0)
+    mma_acc(z2, a21[j], tj1);
     f4 out = f4_splat(0.f);
     if (!row3) {
-      mma_lds_acc(out, blk(Tm, 2, 2), n16, G, z2);
-      store_acc(blk(Tm, 2, J), n16, G, -out);
+      mma_lds_acc(out, blk(Mj, 2, 2), n16, G, z2);
+      store_acc(blk(Mj, 2, J), n16, G, -out);
     } else {
-      f4 z3 = pre1;                                    // Z_3J = A_30 T_0J + A_31 T_1J
-      mma_lds_acc(z3, blk(Am, 3, 1), n16, G, tj1);
-      mma_lds_acc(out, blk(Tm, 3, 2), n16, G, z2);
-      mma_lds_acc(out, blk(Tm, 3, 3), n16, G, z3);
-      store_acc(blk(Tm, 3, J), n16, G, -out);
+      f4 z3 = pre1[j];                                 // Z_3J = A_30 T_0J + A_31 T_1J
+      mma_acc(z3, a31[j], tj1);
+      mma_lds_acc(out, blk(Mj, 3, 2), n16, G, z2);
+      mma_lds_acc(out, blk(Mj, 3, 3), n16, G, z3);
+      store_acc(blk(Mj, 3, J), n16, G, -out);
     }
   }
   lds_barrier();
 
-  // ---- 6. Tb = T diag(beta') in operand order (zero above the diagonal): wave w writes blocks
-  //         w and w + 4; lane (m, g) of block (tile I, kb) holds row 16 I + m, columns
-  //         32 kb + 4g + {0..3} and 32 kb + 16 + 4g + {0..3}
+  // ---- 6. Tb = T diag(beta') in operand order (zero above the diagonal): the nh x 6 blocks
+  //         numbered 6 j + bk, wave w writing numbers w, w + 4, w + 8; lane (m, g) of block
+  //         (tile I, kb) holds row 16 I + m, columns 32 kb + 4g + {0..3} and 32 kb + 16 + 4g + {0..3}
 #pragma unroll
-  for (int i2 = 0; i2 < 2; ++i2) {
-    const int bk = wave + 4 * i2;
-    if (bk < kFragBlocks) {
-      const int row = 16 * block_tile(bk) + n16, c0 = 32 * block_kb(bk) + 4 * G;
-      const f4 t_lo = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0]);
-      const f4 t_hi = *reinterpret_cast<const f4*>(&Tm[row * kFP + c0 + 16]);
-      const f4 b_lo = *reinterpret_cast<const f4*>(&bet[c0]);
-      const f4 b_hi = *reinterpret_cast<const f4*>(&bet[c0 + 16]);
+  for (int i3 = 0; i3 < 3; ++i3) {
+    const int nb = wave + 4 * i3, j = nb >= kFragBlocks ? 1 : 0, bk = nb - kFragBlocks * j;
+    if (j < nh) {
+      const int I = block_tile(bk), kb = block_kb(bk);
+      const int row = 16 * I + n16, c0 = 32 * kb + 4 * G;
+      // columns c0.. lie in block (I, 2 kb), columns c0 + 16.. in block (I, 2 kb + 1), which is
+      // above the diagonal (not stored, all zero in T) when 2 kb + 1 > I
+      const f4 t_lo = tile_row(blk(M(j), I, 2 * kb), n16, G);
+      const f4 t_hi = 2 * kb + 1 <= I ? tile_row(blk(M(j), I, 2 * kb + 1), n16, G) : f4_splat(0.f);
+      const f4 b_lo = *reinterpret_cast<const f4*>(&bet(j)[c0]);
+      const f4 b_hi = *reinterpret_cast<const f4*>(&bet(j)[c0 + 16]);
       f4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -253,7 +311,7 @@ __device__ __forceinline__ void inverse_to_record(float* Amat, float* Tmat, cons
         hi[e] = (c0 + 16 + e <= row) ? t_hi[e] * b_hi[e] : 0.f;
       }
       const Frag<T> f = acc_frag<T>(lo, hi, f4_splat(1.f), f4_splat(1.f));
-      unsigned char* dst = rec + (size_t)bk * kBlockElems * sizeof(T) + (size_t)lane * 8 * sizeof(T);
+      unsigned char* dst = (j ? rec1 : rec0) + (size_t)bk * kBlockElems * sizeof(T) + (size_t)lane * 8 * sizeof(T);
       if constexpr (sizeof(T) == 2) {
         *reinterpret_cast<bf16x8*>(dst) = f.v;
       } else {
@@ -360,7 +418,7 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
 
   // ---- 2. Gram tiles: K K^T row 3 - wave, K Q^T column wave (P^T), five tiles per wave; P into
   //         the record straight from the accumulators; the scalars (wave 0)
-  f4 gk[4];
+  f4 gk[3];
   {
     unsigned char* pbase = rec + kMatBytes;
     switch (wave) {
@@ -384,16 +442,19 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
       sc[7 * C + lane] = 0.f;
     }
   }
-  lds_barrier();   // the staging area becomes A and T
+  lds_barrier();   // the staging area becomes A, then T
 
-  inverse_to_record<T>(sm.u.m.a, sm.u.m.t, sm.gam, sm.rk, sm.bet, gk, wave, n16, G, lane, rec);
+  inverse_to_records<T>(sm.u.a, sm.u.a, sm.gam, sm.gam, sm.rk, sm.bet, sm.bet, gk, 1, wave, n16, G, lane, rec, rec,
+                        [](int) {});
 }
 
 // ====================================================================== bf16: per key head, persistent
-// LDS of the key-head prep: the K tile (swizzled 256-byte rows, written by DMA), and A and T.
+// LDS of the key-head prep: the K tile (swizzled 256-byte rows, written by DMA), and A, then T in
+// place, of two value heads.
+constexpr int kPrepPerCU = 3;   // resident workgroups per compute unit (what the registers allow)
 struct PrepKhSmem {
   unsigned char k[C * 256];
-  float a[C * kFP], t[C * kFP];
+  float m[2][kMatFloats];   // A, then T over it, of two value heads
   float rk[C];
   float gam[4][C], bet[4][C];   // gates of up to four value heads (one batch of the key head's)
 };
@@ -405,6 +466,7 @@ struct PrepKhSmem {
 // g = -exp(A_log) softplus(a_raw + dt_bias) (model.py, _dn_gates).
 struct GateRaw {
   uint32_t x0, x1;   // g or a_raw, beta or b_raw (raw bits)
+  float dt_bias, A_log;   // with the fused prologue: the head's parameters
   int len, h, t;
 };
 template <typename TB>
@@ -419,6 +481,10 @@ __device__ __forceinline__ GateRaw gates_issue(const PrepParams& p, int b, int k
   const void* p0 = p.b_raw ? p.a_raw : static_cast<const void*>(p.g);
   const void* p1 = p.b_raw ? p.b_raw : p.beta;
   const bool w0 = p.b_raw != nullptr && sizeof(TB) == 2;   // element width 2 for raw projections in bf16
+  if (p.b_raw) {
+    gr.dt_bias = p.dt_bias[gr.h];
+    gr.A_log = p.A_log[gr.h];
+  }
   if (w0) {
     gr.x0 = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(make_rsrc(static_cast<const TB*>(p0) + row0, 2 * n), 2 * e, 0, 0);
   } else {
@@ -440,9 +506,9 @@ __device__ __forceinline__ void gates_finish(const PrepParams& p, const GateRaw&
   const bool half0 = p.b_raw != nullptr && half1;
   const float x0 = as_f(gr.x0, half0), x1 = as_f(gr.x1, half1);
   if (p.b_raw) {
-    const float x = x0 + p.dt_bias[gr.h];
+    const float x = x0 + gr.dt_bias;
     const float sp = fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));   // softplus without overflow
-    gv = -__expf(p.A_log[gr.h]) * sp;
+    gv = -__expf(gr.A_log) * sp;
     bv = __builtin_amdgcn_rcpf(1.0f + __expf(-x1));
   } else {
     gv = x0;
@@ -463,18 +529,18 @@ __device__ __forceinline__ void store_gates(float* gam, float* bet, float gv, fl
   bet[lane] = bv;
 }
 
-// Gram tiles K K^T of row Ik = 3 - W from the swizzled K tile: gk[J][e] = (K K^T)[16 Ik + 4G + e][16 J + n16].
+// Gram tiles GramTiles<W> from the swizzled K tile: gk[t][e] = (K K^T)[16 I_t + 4G + e][16 J_t + n16].
 // Both operands are 16-byte row reads (key 32 kb + 8G + e in slot e of lane group G).
 template <int W>
-__device__ __forceinline__ void gram_kk(const unsigned char* kt, int n16, int G, f4 (&gk)[4]) {
-  constexpr int Ik = 3 - W;
+__device__ __forceinline__ void gram_kk(const unsigned char* kt, int n16, int G, f4 (&gk)[3]) {
+  using TL = GramTiles<W>;
 #pragma unroll
-  for (int J = 0; J < 4; ++J) gk[J] = f4_splat(0.f);
+  for (int t = 0; t < 3; ++t) gk[t] = f4_splat(0.f);
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    const bf16x8 a = lds16(kt + swz(16 * Ik + n16, 4 * kb + G));
 #pragma unroll
-    for (int J = 0; J <= Ik; ++J) gk[J] = mfma(a, lds16(kt + swz(16 * J + n16, 4 * kb + G)), gk[J]);
+    for (int t = 0; t < TL::n; ++t)
+      gk[t] = mfma(lds16(kt + swz(16 * TL::I[t] + n16, 4 * kb + G)), lds16(kt + swz(16 * TL::J[t] + n16, 4 * kb + G)), gk[t]);
   }
 }
 
@@ -513,7 +579,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, in
 }
 
 template <typename TB, bool kList>
-__global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int items) {
+__global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p, int items) {
   __shared__ __attribute__((aligned(16))) PrepKhSmem sm;
   constexpr int kRecBytes = kFragBlocks * kBlockElems * 2 + kScalarBytes;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -559,29 +625,32 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     }
   };
 
+  // Wave 3 - j handles the gates of value head j of a batch of four: the waves with the fewest Gram
+  // tiles (row 3 - wave) do the gate work.
+  const int jg = 3 - wave;
   int it = blockIdx.x;
-  GateRaw graw{};   // raw gates of value head `wave` of item it (first batch of four), in flight
+  GateRaw graw{};   // raw gates of value head jg of item it (first batch of four), in flight
   Item nxt{};       // item it, then the next one
   if (it < items) {
     nxt = item(it);
     issue_k(nxt);
-    if (wave < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, wave, lane);
+    if (jg < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, jg, lane);
   }
   for (; it < items; it += gridDim.x) {
     const int kh = nxt.kh, b = nxt.b, c = nxt.c;
     // this wave's part of the K tile (and its gates) have landed; every wave is done with the
     // previous item's A, T and gates
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as a builtin so that the compiler knows its own loads are done
     lds_barrier();
 
     // ---- 1-2. gates of the first (up to) four value heads; Gram tiles of row 3 - wave; rk from
     //           the Gram diagonal, rk_t = (|k_t|^2 + 1e-6)^-1/2 (model.py, _l2norm)
-    if (wave < r) {
+    if (jg < r) {
       float gv, bv;
       gates_finish<TB>(p, graw, gv, bv);
-      store_gates(sm.gam[wave], sm.bet[wave], gv, bv, lane);
+      store_gates(sm.gam[jg], sm.bet[jg], gv, bv, lane);
     }
-    f4 gk[4];
+    f4 gk[3];
     switch (wave) {
       case 0: gram_kk<0>(sm.k, n16, G, gk); break;
       case 1: gram_kk<1>(sm.k, n16, G, gk); break;
@@ -590,7 +659,7 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     }
     {
       const int Ik = 3 - wave, e = n16 & 3;   // diagonal element (16 Ik + n16, 16 Ik + n16): lane group n16 / 4
-      const f4 dg = gk[Ik];
+      const f4 dg = gk[0];                    // the wave's diagonal tile
       const float ss = e == 0 ? dg[0] : e == 1 ? dg[1] : e == 2 ? dg[2] : dg[3];
       if ((n16 >> 2) == G) sm.rk[16 * Ik + n16] = 1.0f / sqrtf(ss + 1e-6f);
     }
@@ -600,38 +669,43 @@ __global__ __launch_bounds__(256, 3) void gdr_prep_keyhead(PrepParams p, int ite
     if (it + (int)gridDim.x < items) {
       nxt = item(it + gridDim.x);
       issue_k(nxt);
-      if (wave < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, wave, lane);
+      if (jg < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, jg, lane);
     }
 
-    // ---- 3-6 for each value head of the key head
+    // ---- 3-6 for the value heads of the key head, two at a time
     for (int hb = 0; 4 * hb < r; ++hb) {
       if (hb > 0) {   // more than four value heads per key head: the next batch's gates, read now
         float g2 = 0.f, b2 = 0.f;
-        if (4 * hb + wave < r) gates_finish<TB>(p, gates_issue<TB>(p, b, kh, c, 4 * hb + wave, lane), g2, b2);
-        lds_barrier();   // the previous batch's gates are no longer read
-        if (4 * hb + wave < r) store_gates(sm.gam[wave], sm.bet[wave], g2, b2, lane);
+        if (4 * hb + jg < r) gates_finish<TB>(p, gates_issue<TB>(p, b, kh, c, 4 * hb + jg, lane), g2, b2);
+        lds_barrier();   // the previous batch's gates and matrices are no longer read
+        if (4 * hb + jg < r) store_gates(sm.gam[jg], sm.bet[jg], g2, b2, lane);
         lds_barrier();
       }
-      for (int j = 0; j < 4 && 4 * hb + j < r; ++j) {
-        const int h = kh * r + 4 * hb + j;
-        unsigned char* rec = reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + h) * p.NC + c) * kRecBytes;
-        if (wave == 3) {   // scalars (rows c and rq are not used by bf16 records)
-          const float g2 = sm.gam[j][lane], g2C = sm.gam[j][C - 1], rkl = sm.rk[lane];
-          float* sc = reinterpret_cast<float*>(rec + kFragBlocks * kBlockElems * 2);
+      for (int j = 0; j < 4 && 4 * hb + j < r; j += 2) {
+        if (j > 0) lds_barrier();   // the previous pair's records are read out of M
+        const int nh = 4 * hb + j + 1 < r ? 2 : 1;
+        auto rec = [&](int i) {
+          return reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + kh * r + 4 * hb + j + i) * p.NC + c) * kRecBytes;
+        };
+        // the scalar rows of head j + i (rows c and rq are not used by bf16 records)
+        auto scalars = [&](int i) {
+          const float g2 = sm.gam[j + i][lane], g2C = sm.gam[j + i][C - 1], rkl = sm.rk[lane];
+          float* sc = reinterpret_cast<float*>(rec(i) + kFragBlocks * kBlockElems * 2);
           sc[kScA * C + lane] = __builtin_amdgcn_exp2f(g2) * rkl;
           sc[kScD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
           sc[kScEgC * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
           sc[kScGam2 * C + lane] = g2;
           sc[kScRk * C + lane] = rkl;
-        }
-        inverse_to_record<__bf16>(sm.a, sm.t, sm.gam[j], sm.rk, sm.bet[j], gk, wave, n16, G, lane, rec);
+        };
+        inverse_to_records<__bf16>(sm.m[0], sm.m[1], sm.gam[j], sm.gam[j + nh - 1], sm.rk, sm.bet[j],
+                                   sm.bet[j + nh - 1], gk, nh, wave, n16, G, lane, rec(0), rec(nh - 1), scalars);
       }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA into LDS may be in flight at the end
 }
 
-// Workgroups of the persistent prep: three per compute unit of the current device (what fits).
+// Workgroups of the persistent prep: kPrepPerCU per compute unit of the current device (what fits).
 static int prep_workgroups() {
   static int cache[64];
   int dev = 0;
@@ -640,8 +714,8 @@ static int prep_workgroups() {
   if (slot && *slot > 0) return *slot;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (slot) *slot = 3 * cus;
-  return 3 * cus;
+  if (slot) *slot = kPrepPerCU * cus;
+  return kPrepPerCU * cus;
 }
 
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s) {
