@@ -79,6 +79,15 @@ def test_no_head_sharing_and_ratio_4():
         check(x, o, s, label=f"Hk={Hk} Hv={Hv}")
 
 
+def test_odd_value_heads_per_key_head():
+    # the bf16 prep forms the records of a key head's value heads two at a time: an odd count
+    # leaves one head alone (3 = pair + single; 5 = a batch of four gates, then one more)
+    for Hk, Hv, seed in ((2, 6, 514), (1, 5, 515)):
+        x = draw(2, 200, Hk, Hv, 128, "R1", seed, torch.bfloat16, lengths=[200, 90], s0_rows=2)
+        o, s = run_gpu(x)
+        check(x, o, s, label=f"Hk={Hk} Hv={Hv}")
+
+
 def test_eight_value_heads_per_key_head():
     # more than four value heads share a key head: the prep forms their records in two batches
     # of gates (both dtypes, with ragged rows and initial states)
