@@ -27,8 +27,9 @@
 // Phases (one barrier each; the waves exchange data through LDS only, so the barriers do not
 // wait for the global stores of the record):
 //   1. stage k (and q) rows in LDS, row norms, gates and gamma;
-//   2. Gram tiles on MFMA, balanced over the waves: wave w forms the K K^T tiles of row 3 - w and
-//      (float32) the K Q^T tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator
+//   2. Gram tiles on MFMA, balanced over the waves: wave w forms its diagonal K K^T tile (3 - w,
+//      3 - w) and 2, 2, 1, 1 of the tiles below the diagonal (GramTiles), and (float32) the K Q^T
+//      tiles of column w. The K Q^T tile (J, I) is P^T, whose accumulator
 //      layout is exactly the operand layout of P, so P goes from registers straight to the record;
 //   3. A (fp32) into LDS (float32: over the staging area);
 //   4. T of the four 16x16 diagonal blocks by forward substitution, one lane per column, all in
@@ -189,8 +190,8 @@ __device__ __forceinline__ void a_phase(float* A, const float* gam2, const float
 
 // Phases 3-6 for nh = 1 or 2 value heads at once (the second head's work interleaves with the
 // first's, so the pair costs about the latency of one): A of head j from the Gram tiles gk of this
-// wave (GramTiles) into M[j] (kMatFloats floats), the blocked inverse T = (I + A)^-1 in place over
-// A, and Tb into the record rec[j]. In place is safe because every block of A is read for the last
+// wave (GramTiles) into M0 or M1 (kMatFloats floats each), the blocked inverse T = (I + A)^-1 in
+// place over A, and Tb into the record rec0 or rec1. In place is safe because every block of A is read for the last
 // time before the barrier that precedes its overwrite (A_21 and A_31, still needed after the blocks
 // of the same phase are written, are read into registers one phase early). While waves 0 and 1
 // solve the diagonal blocks, waves 2 and 3 call idle(j) for head j = wave - 2 < nh. Four barriers;
@@ -416,8 +417,8 @@ __global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
   }
   lds_barrier();
 
-  // ---- 2. Gram tiles: K K^T row 3 - wave, K Q^T column wave (P^T), five tiles per wave; P into
-  //         the record straight from the accumulators; the scalars (wave 0)
+  // ---- 2. Gram tiles: K K^T tiles GramTiles<wave>, K Q^T column wave (P^T); P into the record
+  //         straight from the accumulators; the scalars (wave 0)
   f4 gk[3];
   {
     unsigned char* pbase = rec + kMatBytes;
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p
   };
 
   // Wave 3 - j handles the gates of value head j of a batch of four: the waves with the fewest Gram
-  // tiles (row 3 - wave) do the gate work.
+  // tiles do the gate work.
   const int jg = 3 - wave;
   int it = blockIdx.x;
   GateRaw graw{};   // raw gates of value head jg of item it (first batch of four), in flight
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as a builtin so that the compiler knows its own loads are done
     lds_barrier();
 
-    // ---- 1-2. gates of the first (up to) four value heads; Gram tiles of row 3 - wave; rk from
+    // ---- 1-2. gates of the first (up to) four value heads; Gram tiles GramTiles<wave>; rk from
     //           the Gram diagonal, rk_t = (|k_t|^2 + 1e-6)^-1/2 (model.py, _l2norm)
     if (jg < r) {
       float gv, bv;
