@@ -19,7 +19,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["prefill", "workspace_size", "check", "last_error", "library", "timing_enable",
+__all__ = ["prefill", "workspace_size", "check", "last_error", "library", "timing_enable", "set_truncation",
+           "status_offset",
            "timing_read", "kernel_name", "GdrError", "KERNELS", "LIB_PATH", "decode", "gates", "conv_silu",
            "gated_rmsnorm"]
 
@@ -28,7 +29,7 @@ HEAD_DIM = 128
 GDR_F32, GDR_BF16 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_EINVAL", -2: "GDR_EUNSUPPORTED", -3: "GDR_EWORKSPACE", -4: "GDR_EHIP"}
 KERNELS = ("gdr_prep", "gdr_scan", "gdr_transition", "gdr_combine", "gdr_decode", "gdr_gates", "gdr_conv_silu",
-           "gdr_gated_rmsnorm")
+           "gdr_gated_rmsnorm", "gdr_finalize")
 
 
 class GdrError(RuntimeError):
@@ -80,6 +81,10 @@ def library() -> ctypes.CDLL:
     lib.gdr_timing_read.restype = i32
     lib.gdr_kernel_name.argtypes = [i32]
     lib.gdr_kernel_name.restype = ctypes.c_char_p
+    lib.gdr_set_truncation.argtypes = [i32]
+    lib.gdr_set_truncation.restype = i32
+    lib.gdr_prefill_status_offset.argtypes = [ctypes.POINTER(Desc)]
+    lib.gdr_prefill_status_offset.restype = sz
     _lib = lib
     return lib
 
@@ -112,6 +117,17 @@ def check(desc: Desc, ptrs, ws_bytes: int) -> int:
 
 def kernel_name(i: int) -> str:
     return library().gdr_kernel_name(i).decode()
+
+
+def set_truncation(on: bool = True):
+    """Allow (default) or forbid truncated segment starts for every later call (gdr_set_truncation)."""
+    _raise(library().gdr_set_truncation(1 if on else 0))
+
+
+def status_offset(desc: Desc):
+    """Byte offset of the finalize status word in the workspace, or None when the shape has no segments."""
+    n = library().gdr_prefill_status_offset(ctypes.byref(desc))
+    return None if n == ctypes.c_size_t(-1).value else n
 
 
 def timing_enable(on: bool = True):

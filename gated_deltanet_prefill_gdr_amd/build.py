@@ -33,6 +33,8 @@ def flags() -> list[str]:
         # packed fp32 VALU ops are kept off for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-I", CSRC,
+        # inline assembly must not name reserved registers in its clobber lists
+        "-Werror=inline-asm",
     ]
 
 

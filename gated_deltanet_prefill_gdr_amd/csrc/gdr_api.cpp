@@ -156,6 +156,7 @@ struct TimingRecord {
   hipEvent_t start, stop;
 };
 bool g_timing = false;
+bool g_truncation = true;
 std::vector<TimingRecord> g_records;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -187,8 +188,9 @@ hipError_t timed(int kernel, hipStream_t s, F&& launch) {
   return e;
 }
 
-const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep",  "gdr_scan",      "gdr_transition",   "gdr_combine",
-                                                    "gdr_decode", "gdr_gates", "gdr_conv_silu", "gdr_gated_rmsnorm"};
+const char* const kKernelNames[GDR_KERNEL_COUNT] = {"gdr_prep",   "gdr_scan",  "gdr_transition", "gdr_combine",
+                                                    "gdr_decode", "gdr_gates", "gdr_conv_silu",  "gdr_gated_rmsnorm",
+                                                    "gdr_finalize"};
 
 bool bad_dtype(int dt) { return dt != GDR_F32 && dt != GDR_BF16; }
 
@@ -264,6 +266,15 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
                           : nullptr;
   gdr::ScanParams sp{q, k, v, lengths, s0, s0_row, o, s_final, NC > 0 ? ws : nullptr, seg,
                      d->B, d->L, d->Hk, d->Hv, NC, s0 ? d->n_s0 : 0, plan.P, plan.Ls};
+  if (plan.P > 1) {   // truncated segment starts: plan, certificate parts and status in the workspace
+    const size_t esz = dtype_size(d->qkv_dtype);
+    char* tr = static_cast<char*>(ws) + gdr::trunc_offset(d->B, d->Hv, NC, esz);
+    const size_t n = size_t(d->B) * d->Hv * plan.P;
+    sp.status = reinterpret_cast<int32_t*>(tr);
+    sp.plan = reinterpret_cast<gdr::PlanEntry*>(tr + gdr::kTruncHeader);
+    sp.cert = reinterpret_cast<float*>(tr + gdr::kTruncHeader + n * sizeof(gdr::PlanEntry));
+    sp.trunc = g_truncation ? 1 : 0;
+  }
   if (fused_norm && bf16) {   // applied in the output pass's registers
     sp.z = fu->z;
     sp.norm_w = fu->norm_w;
@@ -277,6 +288,10 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
   }
   hipError_t e = timed(GDR_KERNEL_SCAN, s, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));
+  if (plan.P > 1) {
+    e = timed(GDR_KERNEL_FINALIZE, s, [&] { return gdr::launch_finalize(sp, s); });
+    if (e != hipSuccess) return fail(GDR_EHIP, "finalize launch: %s", hipGetErrorString(e));
+  }
   if (fused_norm && !bf16 && d->L > 0) {   // float32: normalise o in place
     gdr::NormParams np{o, fu->z, fu->norm_w, fu->norm_eps, o, int64_t(d->B) * d->L * d->Hv};
     e = timed(GDR_KERNEL_NORM, s, [&] { return gdr::launch_gated_rmsnorm(np, 0, s); });
@@ -404,6 +419,19 @@ gdr_status gdr_gated_rmsnorm(int64_t rows, gdr_dtype dtype, const void* x, const
 }
 
 const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+gdr_status gdr_set_truncation(int on) {
+  g_truncation = on != 0;
+  return GDR_OK;
+}
+
+size_t gdr_prefill_status_offset(const gdr_desc* d) {
+  if (check_desc(d) != GDR_OK) return size_t(-1);
+  const int NC = num_chunks(d->L);
+  const size_t esz = dtype_size(d->qkv_dtype);
+  if (size_t(d->B) * d->L == 0 || gdr::trunc_bytes(d->B, d->Hv, NC, esz) == 0) return size_t(-1);
+  return gdr::trunc_offset(d->B, d->Hv, NC, esz);
+}
 
 gdr_status gdr_timing_enable(int on) {
   g_timing = on != 0;

@@ -155,11 +155,19 @@ __device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16
 // 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
 // range: zeros). Written as inline assembly so that the compiler neither waits for these loads
 // at every barrier nor moves LDS accesses across them; the kernel counts them itself (vmcnt).
+// The load takes its LDS base from M0, which the compiler may be using for something else: the
+// statement saves M0 in an SGPR of its own, sets it, issues the load and puts the old value back,
+// so M0 is unchanged when the statement ends and nothing reserved appears in a clobber list.
 __device__ __forceinline__ void dma16(const i32x4& r, uint32_t off, const unsigned char* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  // M0 is not otherwise used by these kernels; one wait state separates its write from the load.
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(off), "s"(r)
-               : "memory", "m0");
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  uint32_t saved;
+  // one wait state separates the write of M0 from the load that reads it
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(base), "v"(off), "s"(r)
+      : "memory");
 }
 
 __device__ __forceinline__ bf16x8 pack8(const f4& lo, const f4& hi) {

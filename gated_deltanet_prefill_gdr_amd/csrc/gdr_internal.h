@@ -27,6 +27,10 @@ constexpr int kFragBlocks = 6;
 constexpr int kBlockElems = 64 * 8;
 constexpr int kScalarBytes = 8 * kChunk * 4;
 constexpr int kScA = 0, kScC = 1, kScD = 2, kScEgC = 3, kScGam2 = 4, kScRk = 5, kScRq = 6;   // rows of 64
+// bf16 records use neither c nor rq; their row 6 holds at [6][0] the flag kBetaOk (1 when every
+// beta' of the chunk lies in [0, 2], where each token's map S -> e^{g'} (I - beta' k_hat k_hat^T) S
+// has spectral norm at most e^{g'}; 0 otherwise).
+constexpr int kScBetaOk = 6;
 
 inline size_t record_bytes(size_t elem) {
   return (elem == 2 ? 1 : 2) * size_t(kFragBlocks) * kBlockElems * elem + kScalarBytes;
@@ -69,8 +73,39 @@ inline size_t seg_bytes(int B, int Hv, int NC, size_t elem) {
 // given, row-major: int32 count U, then U entries b NC + c.
 inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 4 * (1 + size_t(B) * NC) : 0; }
 
+// Truncated segment starts (bf16 with P > 1). The state entering segment j >= 1 is
+// S_j = Phi S(c_j - W) + S~_j, where S~_j is the state that the last W chunks before c_j reach from
+// zero and Phi is the product of those chunks' maps, ||Phi||_2 <= 2^{l2} with l2 the sum of g' log2 e
+// over the window (when every beta' there lies in [0, 2]). When a window with l2 <= -kTruncLog2 exists
+// for every boundary of a (row, head), the transition pass computes S~_j over that window alone and the
+// combine is skipped; the output pass records ||S(c_j - W)||_F, and the finalize pass checks the bound
+// eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <= 2^-24 ||S~_j||_F at every boundary, rerunning
+// the (row, head) without truncation where it fails.
+constexpr float kTruncLog2 = 40.f;     // a-priori window decay: 2^-40
+constexpr float kCertRel = 5.9604645e-8f;   // 2^-24
+constexpr int kTruncMaxW = 8;           // longest window, in chunks
+struct PlanEntry {                      // per (row, head, boundary j), written by the transition pass
+  int32_t W;                            // window length in chunks (0: no window, boundary not truncated)
+  float l2;                             // sum of g' log2(e) over the window
+  int32_t trunc;                        // the (row, head) takes the truncated path (same in every entry)
+  int32_t pad;
+};
+constexpr int kCertFloats = 16;         // [0, 8): per-wave ||S(c_j - W)||^2 parts, [8, 16): ||S~_j||^2 parts
+constexpr size_t kTruncHeader = 256;    // int32 status: (row, head) pairs rerun by the last call's finalize
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t trunc_offset(int B, int Hv, int NC, size_t elem) {
+  return align256(records_bytes(B, Hv, NC, elem) + seg_bytes(B, Hv, NC, elem) + chunk_list_bytes(B, NC, elem));
+}
+inline size_t trunc_bytes(int B, int Hv, int NC, size_t elem) {
+  const SegPlan sp = seg_plan(B, Hv, NC, elem == 2);
+  return sp.P > 1 ? kTruncHeader + size_t(B) * Hv * sp.P * (sizeof(PlanEntry) + kCertFloats * sizeof(float)) : 0;
+}
+
 inline size_t workspace_bytes(int B, int Hv, int NC, size_t elem) {
-  return records_bytes(B, Hv, NC, elem) + seg_bytes(B, Hv, NC, elem) + chunk_list_bytes(B, NC, elem);
+  const size_t t = trunc_bytes(B, Hv, NC, elem);
+  return t ? trunc_offset(B, Hv, NC, elem) + t
+           : records_bytes(B, Hv, NC, elem) + seg_bytes(B, Hv, NC, elem) + chunk_list_bytes(B, NC, elem);
 }
 
 struct PrepParams {
@@ -103,6 +138,12 @@ struct ScanParams {
   float* seg;        // segment states (bf16 with P > 1), see above
   int B, L, Hk, Hv, NC, n_s0;
   int P, Ls;         // segments and chunks per segment
+  // truncated segment starts (bf16 with P > 1; see PlanEntry): plan [B Hv P], certificate parts
+  // [B Hv P][kCertFloats], the finalize status word; trunc = 0 forces the exact path everywhere
+  PlanEntry* plan;
+  float* cert;
+  int32_t* status;
+  int trunc;
   // fused gated RMSNorm of o (bf16 output pass; null z = plain o): o <- w o / rms(o) silu(z)
   const void* z;     // [B, L, Hv, 128], o's dtype
   const float* norm_w;   // [128]
@@ -178,6 +219,9 @@ hipError_t launch_decode(const DecodeParams& p, int qkv_bf16, int beta_bf16, hip
 hipError_t launch_transition(const ScanParams& p, hipStream_t s);
 hipError_t launch_combine(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s);
+// bf16 with P > 1, after launch_scan: checks the truncation certificates of every (row, head) that
+// took the truncated path and reruns those whose bound fails from their entering state.
+hipError_t launch_finalize(const ScanParams& p, hipStream_t s);
 
 }  // namespace gdr
 

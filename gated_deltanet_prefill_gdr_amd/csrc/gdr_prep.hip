@@ -324,7 +324,7 @@ __device__ __forceinline__ void inverse_to_records(float* M0, float* M1, const f
 }
 
 template <typename T, typename TB>
-__global__ __launch_bounds__(256, 4) void gdr_prep(PrepParams p) {
+__global__ __launch_bounds__(256, 2) void gdr_prep(PrepParams p) {
   __shared__ __attribute__((aligned(16))) PrepSmem<T> sm;
   constexpr int PK = PrepSmem<T>::PK;
   constexpr int VN = Vec16<T>::N;     // elements per 16-byte vector
@@ -697,6 +697,10 @@ __global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p
           sc[kScEgC * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
           sc[kScGam2 * C + lane] = g2;
           sc[kScRk * C + lane] = rkl;
+          // every beta' of the chunk in [0, 2]: then each token's map has spectral norm <= e^{g'}
+          const float bt = sm.bet[j + i][lane];
+          const bool ok = __all(bt >= 0.f && bt <= 2.f);
+          sc[kScBetaOk * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
         };
         inverse_to_records<__bf16>(sm.m[0], sm.m[1], sm.gam[j], sm.gam[j + nh - 1], sm.rk, sm.bet[j],
                                    sm.bet[j + nh - 1], gk, nh, wave, n16, G, lane, rec(0), rec(nh - 1), scalars);

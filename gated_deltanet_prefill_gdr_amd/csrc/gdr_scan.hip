@@ -148,20 +148,40 @@ template <bool kOut> __device__ __forceinline__ constexpr bool seg_has_v(int sl)
   return kOut || sl < SegCfg<kOut>::NSL / 2;
 }
 
+// What one workgroup runs: chunks [c_begin, c_end) of (row b, value head h), from an entering state,
+// and where its results go.
+struct SegRun {
+  int c_begin, c_end;
+  int src_kind;         // 0: zero (identity for the transitions' M columns), 1: src (pitch 2D), 2: s0 row
+  const float* src;     // the entering state in a segment slot, columns 0 .. 127
+  bool last;            // outputs: the run ends the row, so it writes s_final
+  int cert_chunk;       // outputs: at the top of this chunk (-1: none) each wave writes the sum of
+  float* cert;          //   squares of its part of the state into cert[wave]
+  float* end_b;         // transitions: the state of the value columns (slot, pitch 2D)
+  float* end_m;         // transitions: the identity columns' state M (slot columns 128.., or null)
+  float* n2;            // transitions: each wave's sum of squares of its value columns (or null)
+};
+
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
 template <bool kOut>
-__device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds, int b, int h, int j) {
+__device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds, int b, int h, const SegRun& run) {
   using Cfg = SegCfg<kOut>;
   constexpr int NSL = Cfg::NSL, NW = Cfg::NW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, G = lane >> 4;
   const int kh = h / (p.Hv / p.Hk);
-  const int c_begin = j * p.Ls, c_end = min(c_begin + p.Ls, p.NC);
+  const int c_begin = run.c_begin, c_end = run.c_end;
   const __bf16* qg = reinterpret_cast<const __bf16*>(p.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(p.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(p.v);
   __bf16* og = reinterpret_cast<__bf16*>(p.o);
-  const size_t slot0 = ((size_t)b * p.Hv + h) * p.P;   // this head's first segment slot
 
   int srow = 0;
   if (kOut && row_is_bad(p, b, srow)) {
@@ -169,7 +189,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     const int t_end = min(c_end * C, p.L);
     for (int i = c_begin * C * D + tid; i < t_end * D; i += 64 * NW)
       og[((size_t)b * p.L + i / D) * p.Hv * D + (size_t)h * D + i % D] = (__bf16)nan;
-    if (p.s_final && j == p.P - 1)
+    if (p.s_final && run.last)
       for (int i = tid; i < D * D; i += 64 * NW) p.s_final[((size_t)b * p.Hv + h) * D * D + i] = nan;
     return;
   }
@@ -259,14 +279,12 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   {
     const float* src = nullptr;
     size_t pitch = 0;
-    if constexpr (kOut) {
-      if (p.P > 1) {
-        src = p.seg + (slot0 + j) * kSlotFloats;
-        pitch = 2 * D;
-      } else if (p.s0) {
-        src = p.s0 + ((size_t)srow * p.Hv + h) * D * D;
-        pitch = D;
-      }
+    if (run.src_kind == 1) {
+      src = run.src;
+      pitch = 2 * D;
+    } else if (run.src_kind == 2 && p.s0) {
+      src = p.s0 + ((size_t)srow * p.Hv + h) * D * D;
+      pitch = D;
     }
     if (src) {
 #pragma unroll
@@ -385,6 +403,19 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     else
       wait_and_barrier<Cfg::kStores>();
     if (fuse && c > c_begin) finish_norm(c - 1);
+    if (kOut && c == run.cert_chunk) {   // ||S||_F^2 of the state entering chunk c, this wave's part
+      float ss = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss += S[sl][kb][s2][i] * S[sl][kb][s2][i];
+      ss = wave_sum(ss);
+      if (lane == 0) run.cert[w] = ss;
+    }
     // The next chunk's staging. The output pass spreads it over the iteration: K here, Q after the
     // P formation, V after X, the record before the P barrier. Issued all at once, these loads
     // hold up this chunk's first LDS reads and products (about a tenth of the pass at the long
@@ -650,7 +681,22 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   __builtin_amdgcn_s_waitcnt(0);   // no load into LDS may still be in flight when the workgroup ends
 
   // ---- end state
-  if (kOut && !(p.s_final && j == p.P - 1)) return;
+  if (kOut && !(p.s_final && run.last)) return;
+  if (!kOut && run.n2) {   // each wave's sum of squares of its value columns
+    float ss = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      if (!seg_has_v<kOut>(sl)) continue;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ss += S[sl][kb][s2][i] * S[sl][kb][s2][i];
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) run.n2[w] = ss;
+  }
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) {
     float* dst;
@@ -659,7 +705,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       dst = p.s_final + ((size_t)b * p.Hv + h) * D * D;
       pitch = D;
     } else {
-      dst = p.seg + (slot0 + (seg_has_v<kOut>(sl) ? j + 1 : j)) * kSlotFloats;   // B_j into slot j+1, M_j into slot j
+      dst = seg_has_v<kOut>(sl) ? run.end_b : run.end_m;   // B into slot j + 1, M into slot j
+      if (!dst) continue;
       pitch = 2 * D;
     }
     const int col = seg_col<kOut>(w, sl) + n16;
@@ -672,20 +719,138 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   }
 }
 
+__device__ __forceinline__ size_t head_index(const ScanParams& p, int b, int h) { return (size_t)b * p.Hv + h; }
+__device__ __forceinline__ float* slot_ptr(const ScanParams& p, int b, int h, int j) {
+  return p.seg + (head_index(p, b, h) * p.P + j) * kSlotFloats;
+}
+
 // Outputs: one workgroup per (row, segment, value head), heads fastest.
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % p.P, b = lam / (p.Hv * p.P);
-  seg_body<true>(p, lds, b, h, j);
+  SegRun run{};
+  run.c_begin = j * p.Ls;
+  run.c_end = min(run.c_begin + p.Ls, p.NC);
+  run.src_kind = p.P > 1 ? 1 : 2;   // with segments, the combine has put every entering state in its slot
+  run.src = p.P > 1 ? slot_ptr(p, b, h, j) : nullptr;
+  run.last = j == p.P - 1;
+  run.cert_chunk = -1;
+  if (p.P > 1 && p.trunc && j + 1 < p.P) {
+    const PlanEntry e = p.plan[head_index(p, b, h) * p.P + j + 1];
+    if (e.trunc) {   // the window of boundary j + 1 starts inside this segment
+      run.cert_chunk = (j + 1) * p.Ls - e.W;
+      run.cert = p.cert + (head_index(p, b, h) * p.P + j + 1) * kCertFloats;
+    }
+  }
+  seg_body<true>(p, lds, b, h, run);
 }
 
-// Transitions: one workgroup per (row, segment < P - 1, value head).
+// Truncation plan of boundary jb (1 <= jb < P) of (row b, head h), from the chunk records: the shortest
+// window of W <= min(Ls, kTruncMaxW) chunks ending at c = jb Ls whose chunks all hold valid tokens, all
+// have beta' in [0, 2] and whose decay sums to l2 = sum g' log2 e <= -kTruncLog2. W = 0 when there is
+// none (or the row's length or s0 row is out of range).
+__device__ __forceinline__ void boundary_plan(const ScanParams& p, int b, int h, int jb, int& W, float& l2) {
+  W = 0;
+  l2 = 0.f;
+  int srow = 0;
+  if (row_is_bad(p, b, srow)) return;
+  const int len = p.lengths ? p.lengths[b] : p.L;
+  const int c_valid = (len + C - 1) / C;   // chunks that hold valid tokens
+  const int cb = jb * p.Ls;
+  if (cb > c_valid) return;
+  const unsigned char* recs = reinterpret_cast<const unsigned char*>(p.ws) + head_index(p, b, h) * p.NC * kRecB;
+  const int wmax = min(min(p.Ls, kTruncMaxW), cb);
+  float acc = 0.f;
+  for (int w = 1; w <= wmax; ++w) {
+    const float* sc = reinterpret_cast<const float*>(recs + (size_t)(cb - w) * kRecB + kScOff);
+    if (!(sc[kScBetaOk * C] == 1.f)) return;
+    acc += sc[kScGam2 * C + C - 1];   // the chunk's whole decay, in log2
+    if (acc <= -kTruncLog2) {
+      W = w;
+      l2 = acc;
+      return;
+    }
+  }
+}
+
+// Transitions: one workgroup per (row, segment j < P - 1, value head). Every workgroup first plans the
+// boundaries of its (row, head) (thread t: boundary t + 1; P <= 256 < threads); the (row, head) is
+// truncated when every boundary has a window. Then segment j's workgroup either runs the window before
+// boundary j + 1 from zero, leaving the entering state of segment j + 1 in its slot (truncated), or
+// runs the whole segment on the augmented start [0 | I], leaving B_j and M_j (exact).
 __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<false>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
-  seg_body<false>(p, lds, b, h, j);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0;   // read by the finalize pass only
+  const int t = threadIdx.x, jb_t = t + 1;
+  int W = 0;
+  float l2 = 0.f;
+  if (p.trunc && jb_t < p.P) boundary_plan(p, b, h, jb_t, W, l2);
+  const bool trunc = __syncthreads_and(jb_t >= p.P || W > 0) != 0 && p.trunc;
+  const size_t hb = head_index(p, b, h) * p.P;
+  __shared__ int w_own;   // the window of this segment's own boundary j + 1
+  if (jb_t == j + 1) {
+    p.plan[hb + jb_t] = PlanEntry{W, l2, trunc ? 1 : 0, 0};
+    w_own = W;
+  }
+  __syncthreads();
+  SegRun run{};
+  run.src_kind = 0;
+  run.end_b = slot_ptr(p, b, h, j + 1);
+  if (trunc) {
+    run.c_end = (j + 1) * p.Ls;
+    run.c_begin = run.c_end - w_own;
+    run.end_m = nullptr;
+    run.n2 = p.cert + (hb + j + 1) * kCertFloats + 8;
+  } else {
+    run.c_begin = j * p.Ls;
+    run.c_end = min(run.c_begin + p.Ls, p.NC);
+    run.end_m = slot_ptr(p, b, h, j);
+    run.n2 = nullptr;
+  }
+  seg_body<false>(p, lds, b, h, run);
+}
+
+// Finalize (bf16 with P > 1): one workgroup per (row, value head). For a (row, head) that took the
+// truncated path it checks, boundary by boundary, eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <=
+// 2^-24 ||S~_j||_F (the norms from the certificate parts the output and transition passes left); where
+// that fails it counts the (row, head) in the status word and runs it again in one piece from its
+// entering state in slot 0 (s0 or zero, copied there by the combine), overwriting o and s_final.
+__global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
+  __shared__ int redo;
+  const int h = blockIdx.x % p.Hv, b = blockIdx.x / p.Hv;
+  const size_t hb = head_index(p, b, h) * p.P;
+  if (!p.trunc || !p.plan[hb + 1].trunc) return;   // exact path: nothing to check
+  if (threadIdx.x == 0) {
+    float eps = 0.f;
+    bool ok = true;
+    for (int jb = 1; jb < p.P && ok; ++jb) {
+      const PlanEntry e = p.plan[hb + jb];
+      const float* ct = p.cert + (hb + jb) * kCertFloats;
+      float n1 = 0.f, n2 = 0.f;
+      for (int i = 0; i < 8; ++i) {
+        n1 += ct[i];
+        n2 += ct[8 + i];
+      }
+      eps = __builtin_amdgcn_exp2f(e.l2) * (sqrtf(n1) + eps);
+      ok = eps <= kCertRel * sqrtf(n2);   // false for NaN or infinity as well
+    }
+    redo = ok ? 0 : 1;
+    if (!ok) atomicAdd(p.status, 1);
+  }
+  __syncthreads();
+  if (!redo) return;
+  SegRun run{};
+  run.c_begin = 0;
+  run.c_end = p.NC;
+  run.src_kind = 1;
+  run.src = slot_ptr(p, b, h, 0);
+  run.last = true;
+  run.cert_chunk = -1;
+  seg_body<true>(p, lds, b, h, run);
 }
 
 // Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero). One
@@ -743,6 +908,9 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+  // A truncated (row, head): the transition pass has already left the entering state of every
+  // segment j >= 1 in its slot, and segment 0's (s0 or zero) is now in slot 0.
+  if (p.trunc && p.plan[((size_t)b * p.Hv + h) * p.P + 1].trunc) return;
   // With no initial state S_1 = B_0, which is already in its slot: the chain starts at step 1.
   const int steps = p.P - 1, first = p.s0 ? 0 : 1;
   if (!p.s0 && steps > 0) {
@@ -1050,6 +1218,11 @@ hipError_t launch_transition(const ScanParams& p, hipStream_t s) {
 
 hipError_t launch_combine(const ScanParams& p, hipStream_t s) {
   hipLaunchKernelGGL(gdr_combine, dim3(p.B * p.Hv * kSlices16), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const ScanParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(gdr_finalize_bf16, dim3(p.B * p.Hv), dim3(64 * SegCfg<true>::NW), 0, s, p);
   return hipGetLastError();
 }
 

@@ -186,6 +186,25 @@ gdr_status gdr_decode_ex(const gdr_desc* desc, const void* q, const void* k, con
                          const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
                          const gdr_fusion* fusion, void* o, float* s_final, void* stream);
 
+/* Truncated segment starts (bf16 sequences cut into segments). The state map of a run of tokens is
+ * S -> Phi S + B with ||Phi||_2 <= exp(sum of g' over the run) whenever every beta' of the run lies in
+ * [0, 2] (each token multiplies S by exp(g') (I - beta' k_hat k_hat^T), whose spectral norm is then at
+ * most exp(g'), since |k_hat| < 1). When, for every segment boundary of a (row, head), the last few
+ * chunks (at most 8) before the boundary decay by at least 2^-40 in that sense, the library takes the
+ * state entering the segment from those chunks alone, run from zero, instead of composing the maps of
+ * all earlier segments. The dropped term is at most 2^-40 times the norm of the state where the window
+ * starts; the kernels measure that norm and, in a last pass, check at every boundary that the error
+ * bound carried along the segments stays below 2^-24 of the norm of the state used, and rerun the
+ * (row, head) without truncation where it does not. Results therefore agree with the untruncated
+ * computation to within that relative bound. On by default; gdr_set_truncation(0) makes every call on
+ * any thread take the untruncated path (process-wide setting, not synchronised with calls in flight). */
+gdr_status gdr_set_truncation(int on);
+
+/* Byte offset in the workspace of an int32 that the finalize pass of the last gdr_prefill call on
+ * that workspace sets to the number of (row, head) pairs it recomputed without truncation (valid once
+ * the call has finished), or (size_t)-1 when this shape has no segments or the desc is invalid. */
+size_t gdr_prefill_status_offset(const gdr_desc* desc);
+
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* gdr_last_error(void);
 
@@ -202,7 +221,8 @@ enum {
   GDR_KERNEL_GATES = 5,       /* gdr_gates */
   GDR_KERNEL_CONV = 6,        /* gdr_conv_silu */
   GDR_KERNEL_NORM = 7,        /* gdr_gated_rmsnorm */
-  GDR_KERNEL_COUNT = 8
+  GDR_KERNEL_FINALIZE = 8,    /* bf16 long sequences: checks truncated segment starts, reruns */
+  GDR_KERNEL_COUNT = 9
 };
 gdr_status gdr_timing_enable(int on);
 gdr_status gdr_timing_read(double* total_ms, int64_t* launches, int n_kernels);

@@ -94,9 +94,19 @@ def test_workspace_size():
     # bf16 also keeps a list of the chunks that hold valid tokens (used when lengths are given):
     # an int32 count and one int32 per (row, chunk)
     lst = lambda B, NC: 4 * (1 + B * NC)
-    assert gdr.workspace_size(gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)) == 32 * 256 * rec_bf16 + 32 * 8 * slot + lst(1, 256)
-    assert gdr.workspace_size(gdr.make_desc(1, 200, 1, 2, qkv_bf16=True)) == 2 * 4 * rec_bf16 + 2 * 4 * slot + lst(1, 4)
-    assert gdr.workspace_size(gdr.make_desc(1, 640, 2, 100, qkv_bf16=True)) == 100 * 10 * rec_bf16 + 100 * 3 * slot + lst(1, 10)
+    # with segments, a 256-byte-aligned tail: a 256-byte status header, then per (row, head, segment)
+    # a 16-byte truncation plan entry and 16 floats of certificate parts
+    up = lambda x: (x + 255) // 256 * 256
+    tail = lambda n: 256 + n * (16 + 64)
+    base = 32 * 256 * rec_bf16 + 32 * 8 * slot + lst(1, 256)
+    assert gdr.workspace_size(gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)) == up(base) + tail(32 * 8)
+    base = 2 * 4 * rec_bf16 + 2 * 4 * slot + lst(1, 4)
+    assert gdr.workspace_size(gdr.make_desc(1, 200, 1, 2, qkv_bf16=True)) == up(base) + tail(2 * 4)
+    base = 100 * 10 * rec_bf16 + 100 * 3 * slot + lst(1, 10)
+    assert gdr.workspace_size(gdr.make_desc(1, 640, 2, 100, qkv_bf16=True)) == up(base) + tail(100 * 3)
+    d = gdr.make_desc(1, 16384, 16, 32, qkv_bf16=True)
+    assert gdr.status_offset(d) == up(32 * 256 * rec_bf16 + 32 * 8 * slot + lst(1, 256))
+    assert gdr.status_offset(gdr.make_desc(64, 1024, 16, 32, qkv_bf16=True)) is None   # one segment
     assert gdr.workspace_size(gdr.make_desc(64, 1024, 16, 32, qkv_bf16=True)) == 64 * 32 * 16 * rec_bf16 + lst(64, 16)
     assert gdr.workspace_size(gdr.make_desc(2, 130, 2, 4)) == 2 * 4 * 3 * rec_f32
     assert gdr.workspace_size(gdr.make_desc(0, 100, 1, 1)) == 0

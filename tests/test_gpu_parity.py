@@ -47,6 +47,12 @@ def test_config4_forks_sampled_rows():
     check(x, o, s, rows=rows, label=f"{CONFIGS[4].name} rows={rows}")
 
 
+def test_config4_forks_all_rows():
+    x = CONFIGS[4].draw()
+    o, s = run_gpu(x)
+    check(x, o, s, label=f"{CONFIGS[4].name} all 64 rows")
+
+
 def test_config5_long_sampled_heads():
     x = CONFIGS[5].draw()
     o, s = run_gpu(x)
