@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["prefill", "workspace_size", "check", "last_error", "library", "timing_enable", "set_truncation",
+__all__ = ["prefill", "prefill_noalloc", "workspace_size", "check", "last_error", "library", "timing_enable", "set_truncation",
            "status_offset",
            "timing_read", "kernel_name", "GdrError", "KERNELS", "LIB_PATH", "decode", "gates", "conv_silu",
            "gated_rmsnorm"]
@@ -62,6 +62,8 @@ def library() -> ctypes.CDLL:
     lib.gdr_prefill.restype = i32
     lib.gdr_prefill_ex.argtypes = [ctypes.POINTER(Desc)] + [vp] * 8 + [ctypes.POINTER(Fusion)] + [vp] * 3 + [sz, vp]
     lib.gdr_prefill_ex.restype = i32
+    lib.gdr_prefill_noalloc.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10 + [vp]
+    lib.gdr_prefill_noalloc.restype = i32
     lib.gdr_decode.argtypes = [ctypes.POINTER(Desc)] + [vp] * 10 + [vp]
     lib.gdr_decode_ex.argtypes = [ctypes.POINTER(Desc)] + [vp] * 8 + [ctypes.POINTER(Fusion)] + [vp] * 2 + [vp]
     lib.gdr_decode_ex.restype = i32
@@ -287,6 +289,25 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, n
                                       _ptr(o), _ptr(s_final), _ptr(workspace), need, stream)
     _raise(st)
     return o, s_final
+
+
+def prefill_noalloc(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, out, s_final=None):
+    """gdr_prefill_noalloc: the prefill with the library's device-resident workspace (no workspace
+    argument; shapes needing more than 128 MiB of workspace are rejected). The outputs are the
+    caller's: out [B, L, Hv, 128] in v's dtype and s_final [B, Hv, 128, 128] float32 (or None)."""
+    import torch
+    desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row)
+    _on(dev, out=out, s_final=s_final)
+    if tuple(out.shape) != (B, L, Hv, Dv) or out.dtype != v.dtype:
+        raise ValueError(f"out must be [{B}, {L}, {Hv}, {Dv}] in v's dtype")
+    if s_final is not None and (tuple(s_final.shape) != (B, Hv, Dk, Dv) or s_final.dtype != torch.float32):
+        raise ValueError(f"s_final must be float32 [{B}, {Hv}, {Dk}, {Dv}]")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = library().gdr_prefill_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(lengths), _ptr(s0), _ptr(s0_row), _ptr(out), _ptr(s_final), stream)
+    _raise(st)
+    return out, s_final
 
 
 def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, norm=None, want_state=True, out=None,

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgdr.so")
-SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_decode.hip", "gdr_layer.hip", "gdr_api.cpp"]
+SOURCES = ["gdr_prep.hip", "gdr_scan.hip", "gdr_decode.hip", "gdr_layer.hip", "gdr_noalloc.hip", "gdr_api.cpp"]
 ARCH = "gfx950"
 
 

@@ -172,16 +172,19 @@ hipEvent_t take_event() {
 }
 
 // Launch through `launch` (returns hipError_t), bracketed by timing events when timing is on.
+// Set while gdr_prefill_noalloc runs on this thread: no timing events (creating one may allocate).
+thread_local bool t_no_alloc = false;
+
 template <typename F>
 hipError_t timed(int kernel, hipStream_t s, F&& launch) {
   TimingRecord rec{kernel, nullptr, nullptr};
-  if (g_timing) {
+  if (g_timing && !t_no_alloc) {
     rec.start = take_event();
     rec.stop = take_event();
     if (rec.start) (void)hipEventRecord(rec.start, s);
   }
   hipError_t e = launch();
-  if (g_timing && rec.start && rec.stop) {
+  if (g_timing && !t_no_alloc && rec.start && rec.stop) {
     (void)hipEventRecord(rec.stop, s);
     g_records.push_back(rec);
   }
@@ -298,6 +301,31 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
     if (e != hipSuccess) return fail(GDR_EHIP, "norm launch: %s", hipGetErrorString(e));
   }
   return GDR_OK;
+}
+
+gdr_status gdr_prefill_noalloc(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                               const void* beta, const int32_t* lengths, const float* s0, const int32_t* s0_row,
+                               void* o, float* s_final, void* stream) {
+  const gdr_status st = check_desc(d);
+  if (st != GDR_OK) return st;
+  const size_t need = gdr_prefill_workspace_size(d);
+  if (need > gdr::kNoAllocScratchBytes)
+    return fail(GDR_EUNSUPPORTED, "gdr_prefill_noalloc: this shape needs %zu bytes of workspace; the device-resident "
+                "workspace holds at most %zu bytes (use gdr_prefill with a workspace of its own)",
+                need, gdr::kNoAllocScratchBytes);
+  // host-checkable errors first, as for every entry point (the workspace is checked below, once known)
+  gdr_status chk = check_all(d, q, k, v, g, beta, lengths, s0, s0_row, o, s_final, nullptr, 0, /*need_ws=*/false);
+  if (chk != GDR_OK) return chk;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = gdr::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(GDR_EHIP, "gdr_prefill_noalloc: device workspace lookup: %s", hipGetErrorString(e));
+  }
+  t_no_alloc = true;
+  const gdr_status r = gdr_prefill_ex(d, q, k, v, g, beta, lengths, s0, s0_row, nullptr, o, s_final, ws,
+                                      need > 0 ? gdr::kNoAllocScratchBytes : 0, stream);
+  t_no_alloc = false;
+  return r;
 }
 
 gdr_status gdr_decode(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,

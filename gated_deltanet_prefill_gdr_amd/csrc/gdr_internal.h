@@ -108,6 +108,11 @@ inline size_t workspace_bytes(int B, int Hv, int NC, size_t elem) {
            : records_bytes(B, Hv, NC, elem) + seg_bytes(B, Hv, NC, elem) + chunk_list_bytes(B, NC, elem);
 }
 
+// gdr_prefill_noalloc: the workspace lives in a fixed device array of this many bytes (per GPU).
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;
+// Address of this device's array (looked up once per device, with the device current).
+hipError_t noalloc_scratch(void** out);
+
 struct PrepParams {
   const void* q;
   const void* k;

@@ -99,6 +99,21 @@ gdr_status gdr_prefill(const gdr_desc* desc, const void* q, const void* k, const
                        const int32_t* s0_row, void* o, float* s_final, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* gdr_prefill for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. Same arguments, layouts, results and errors as
+ * gdr_prefill, without the workspace: the library uses a fixed 128 MiB array in device memory
+ * instead, one per GPU it runs on, held from the first use of the library on that GPU until the
+ * process ends. The first call on a device looks up that device's array (with the device current);
+ * no call allocates, frees or creates anything (per-kernel timing events are not recorded).
+ * Shapes whose gdr_prefill_workspace_size exceeds 128 MiB (134217728 bytes) are rejected with
+ * GDR_EUNSUPPORTED before anything is launched (the long prefill, B = 1, L = 16384, 32 value heads,
+ * needs about 101 MB). Every call on a GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (on different streams or threads without ordering
+ * between them) race and give wrong results; calls in one stream are safe. */
+gdr_status gdr_prefill_noalloc(const gdr_desc* desc, const void* q, const void* k, const void* v,
+                               const float* g, const void* beta, const int32_t* lengths, const float* s0,
+                               const int32_t* s0_row, void* o, float* s_final, void* stream);
+
 /* Work fused into gdr_prefill_ex (model page, model.py, _linear_layer: the gate prologue feeds the
  * delta rule and the gated RMSNorm follows it). Either part may be left out (NULL pointers).
  *   Gate prologue: b_raw, a_raw [B, L, Hv] in desc->beta_dtype (the raw projections) and A_log,
