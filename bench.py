@@ -99,20 +99,66 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(x, heads):
-    """The float64 oracle as it stands, on a bounded sample of the same workload."""
+_CPU_X = None   # the inputs of the CPU baseline, shared with its forked worker processes
+
+
+def _oracle_pair(bh):
+    """Worker: the float64 oracle on one (row, value head) of _CPU_X; returns its CPU seconds."""
     from threadpoolctl import threadpool_limits
     from oracle import gated_delta_rule
-    q, k, v = x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy()
-    g, beta = x.g.double().numpy(), x.beta.double().numpy()
-    L = q.shape[1]
+    b, h = bh
+    x = _CPU_X
+    t0 = time.process_time()
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        gated_delta_rule(q, k, v, g, beta, heads=list(range(heads)))
-        dt = time.perf_counter() - t0
-    return {"value": L * heads / dt, "unit": "tokens·heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {L} tokens of value heads 0..{heads - 1} of 32 (B=1), float64 numpy, "
-                      f"1 thread, {dt:.1f} s"}
+        gated_delta_rule(x["q"], x["k"], x["v"], x["g"], x["beta"], lengths=x["lengths"], s0=x["s0"],
+                         s0_row=x["s0_row"], rows=[b], heads=[h])
+    return time.process_time() - t0
+
+
+def cpu_workers():
+    """Worker processes for the oracle: one per host core this process may use, at most 16 (a
+    one-GPU share of the GPU machine's host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, pairs=None):
+    """The float64 oracle as it stands, over the (row, value head) pairs of the workload (all of them
+    unless `pairs` is given), one worker process per host core, each pair's token loop inside one
+    process; wall time end to end. Must run before this process touches the GPU (the workers are
+    forked)."""
+    import multiprocessing as mp
+    import numpy as np
+    global _CPU_X
+    B, L, Hk, Hv = x.q.shape[0], x.q.shape[1], x.q.shape[2], x.v.shape[2]
+    _CPU_X = {"q": x.q.double().numpy(), "k": x.k.double().numpy(), "v": x.v.double().numpy(),
+              "g": x.g.double().numpy(), "beta": x.beta.double().numpy(),
+              "lengths": None if x.lengths is None else x.lengths.numpy(),
+              "s0": None if x.s0 is None else x.s0.double().numpy(),
+              "s0_row": None if x.s0_row is None else x.s0_row.numpy()}
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(Hv)]
+    workers = min(cpu_workers(), len(pairs))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        cpu_s = sum(pool.map(_oracle_pair, pairs, chunksize=1))
+    wall = time.perf_counter() - t0
+    _CPU_X = None
+    units = len(pairs) * L
+    return {"value": units / wall, "unit": "tokens·heads/s", "cores": workers, "kind": "oracle",
+            "sample": f"{len(pairs)} of {B * Hv} (row, value head) pairs, all {L} tokens each, float64 numpy, "
+                      f"{workers} processes x 1 thread, {wall:.1f} s wall, {cpu_s:.1f} s CPU",
+            "cpu_model": cpu_model(), "numpy": np.__version__, "wall_s": wall, "cpu_s": cpu_s}
 
 
 def copy_probe(nbytes=1 << 30, reps=3):
@@ -277,6 +323,10 @@ def bench_all_configs(a):
     import torch
     import gated_deltanet_prefill_gdr_amd as gdr
     from workloads import CONFIGS
+    cpu = {}
+    if not a.no_cpu_baseline:   # every config's oracle time first: its workers are forked
+        for i in sorted(CONFIGS):
+            cpu[i] = cpu_baseline(CONFIGS[i].draw())
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     for i in sorted(CONFIGS):
@@ -315,7 +365,8 @@ def bench_all_configs(a):
                 "us": ms * 1e3, "tokens_heads_per_s": units / (ms * 1e-3),
                 "valid_tokens_heads_per_s": valid_units / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
                 "alg_GBs": nbytes / (ms * 1e-3) / 1e9, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak,
-                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": nbytes, "alg_flops": flops}
+                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": nbytes, "alg_flops": flops,
+                "cpu_baseline": cpu.get(i)}
         print(json.dumps(line), flush=True)
 
 
@@ -325,7 +376,6 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--rows", type=int, default=64)
@@ -359,6 +409,9 @@ def main():
     spec = CONFIGS[5]
     x = spec.draw()
     B, L, Hk, Hv, Dk, Dv = x.shape
+    cpu = None
+    if not a.no_cpu_baseline and not a.fused:   # forked workers: before anything touches the GPU
+        cpu = cpu_baseline(x)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     q, k, v, g, beta = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
@@ -391,17 +444,19 @@ def main():
     dominant = max(per_kernel, key=lambda n: per_kernel[n][0])
     k_ms = per_kernel[dominant][0]
     k_bytes = kernel_bytes(dominant, B, L, Hk, Hv, 2, P, fused=a.fused)
-    # roofline of the dominant kernel: the path's algorithmic bytes per unit (one token x one value
-    # head) times the units one launch processes (every kernel of the path processes all of them),
-    # over that kernel's average launch time
-    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    # roofline of the whole call (every kernel of the path, back to back): the path's algorithmic bytes
+    # (per unit, one token x one value head, times the units of the call) over the measured step time.
+    # The dominant kernel's own figures sit under "dominant_kernel": the same algorithmic bytes over
+    # its average launch time (the bound it would reach if the other kernels cost nothing), and its
+    # interface bytes (what it reads and writes itself, intermediates included) over that time.
+    achieved = nbytes / (ms * 1e-3) / 1e9
     traffic = None
     prof = os.path.join(ROOT, "profiles", "traffic_l16384_bf16.json")
-    if os.path.exists(prof):
+    if os.path.exists(prof) and not a.fused:
         with open(prof) as f:
             tr = json.load(f)
         if tr.get("source_hash") == source_hash():   # counters of these very kernels only
-            traffic = tr.get("kernels", {}).get(dominant, {}).get("hbm_bytes")
+            traffic = sum(k.get("hbm_bytes", 0) for k in tr.get("kernels", {}).values()) or None
     line = {
         "metric": METRIC if not a.fused else METRIC + ", gate prologue and gated RMSNorm fused",
         "value": units / (ms * 1e-3),
@@ -422,19 +477,19 @@ def main():
                    "B": B, "L": L, "Hk": Hk, "Hv": Hv, "D": Dk, "global_batch": B, "seq_len": L,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dominant,
-                     "kernel_ms": k_ms, "alg_bytes_per_unit": nbytes / units, "units": units,
-                     "interface_bytes": k_bytes, "interface_GBs": k_bytes / (k_ms * 1e-3) / 1e9},
-        "path": {"ms": ms, "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                 "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                 "tflops": flops / (ms * 1e-3) / 1e12, "alg_bytes": nbytes, "alg_flops": flops,
-                 "kernel_ms": {n: t for n, (t, c) in per_kernel.items()},
-                 "segments": P,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "scope": "whole gdr_prefill call (all kernels), algorithmic bytes / step time",
+                     "alg_bytes_per_unit": nbytes / units, "units": units, "alg_bytes": nbytes,
+                     "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "tflops": flops / (ms * 1e-3) / 1e12,
+                     "dominant_kernel": {"name": dominant, "ms": k_ms,
+                                         "frac_alg_bytes": nbytes / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                         "interface_bytes": k_bytes,
+                                         "interface_GBs": k_bytes / (k_ms * 1e-3) / 1e9}},
+        "path": {"ms": ms, "kernel_ms": {n: t for n, (t, c) in per_kernel.items()}, "segments": P,
                  "source_hash": source_hash()},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
-    if not a.no_cpu_baseline and not a.fused:
-        line["cpu_baseline"] = cpu_baseline(x, a.cpu_heads)
     print(json.dumps(line), flush=True)
 
 

@@ -275,12 +275,18 @@ def prefill(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, n
     desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row, gates)
     fu = _fusion(gates, norm, v, dev)
     need = workspace_size(desc)
+    if out is not None:
+        check_buffer("out", out, (B, L, Hv, Dv), v.dtype, dev)
     o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
+    if s_final is not None:
+        check_buffer("s_final", s_final, (B, Hv, Dk, Dv), torch.float32, dev)
     if want_state and s_final is None:
         s_final = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
     if not want_state:
         s_final = None
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
+    if workspace is not None:
+        check_workspace(workspace, need, dev)
+    else:
         workspace = torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
@@ -297,11 +303,9 @@ def prefill_noalloc(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, out, 
     caller's: out [B, L, Hv, 128] in v's dtype and s_final [B, Hv, 128, 128] float32 (or None)."""
     import torch
     desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row)
-    _on(dev, out=out, s_final=s_final)
-    if tuple(out.shape) != (B, L, Hv, Dv) or out.dtype != v.dtype:
-        raise ValueError(f"out must be [{B}, {L}, {Hv}, {Dv}] in v's dtype")
-    if s_final is not None and (tuple(s_final.shape) != (B, Hv, Dk, Dv) or s_final.dtype != torch.float32):
-        raise ValueError(f"s_final must be float32 [{B}, {Hv}, {Dk}, {Dv}]")
+    check_buffer("out", out, (B, L, Hv, Dv), v.dtype, dev)
+    if s_final is not None:
+        check_buffer("s_final", s_final, (B, Hv, Dk, Dv), torch.float32, dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         st = library().gdr_prefill_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -317,7 +321,11 @@ def decode(q, k, v, g, beta, valid=None, s0=None, s0_row=None, *, gates=None, no
     import torch
     desc, lengths, s0_row, (B, L, Hk, Hv, Dk, Dv), dev = _inputs(q, k, v, g, beta, valid, s0, s0_row, gates)
     fu = _fusion(gates, norm, v, dev)
+    if out is not None:
+        check_buffer("out", out, (B, L, Hv, Dv), v.dtype, dev)
     o = out if out is not None else torch.empty(B, L, Hv, Dv, device=dev, dtype=v.dtype)
+    if s_final is not None:
+        check_buffer("s_final", s_final, (B, Hv, Dk, Dv), torch.float32, dev)
     if want_state and s_final is None:
         s_final = torch.empty(B, Hv, Dk, Dv, device=dev, dtype=torch.float32)
     if not want_state:
@@ -338,6 +346,26 @@ def _dtype_code(t):
     if t.dtype == torch.float32:
         return GDR_F32
     raise ValueError("tensors must be float32 or bfloat16")
+
+
+def check_buffer(name, t, shape, dtype, dev):
+    """A caller-supplied output buffer must be exactly what the kernels write: the C ABI sizes every
+    range from the descriptor and cannot see the real allocation, so a short, mistyped, strided or
+    foreign buffer would be written out of bounds. Raises ValueError otherwise."""
+    shape = tuple(int(x) for x in shape)
+    if tuple(t.shape) != shape or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {list(shape)}, got {t.dtype} {list(t.shape)}")
+    if t.device != dev or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+
+
+def check_workspace(ws, need, dev):
+    """The workspace must be a contiguous uint8 tensor on the call's device with at least `need` bytes."""
+    import torch
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or ws.device != dev or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {dev}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace has {ws.numel()} bytes, {need} needed")
 
 
 def _on(dev, **tensors):
@@ -363,6 +391,10 @@ def gates(b, a, A_log, dt_bias, valid=None, *, beta_out=None, g_out=None):
         raise ValueError(f"A_log and dt_bias must be float32 [{Hv}]")
     _on(dev, b=b, a=a, A_log=A_log, dt_bias=dt_bias)
     lengths = _lengths_from_valid(valid, B, L, dev)
+    if beta_out is not None:
+        check_buffer("beta_out", beta_out, (B, L, Hv), b.dtype, dev)
+    if g_out is not None:
+        check_buffer("g_out", g_out, (B, L, Hv), torch.float32, dev)
     beta = beta_out if beta_out is not None else torch.empty_like(b)
     g = g_out if g_out is not None else torch.empty(B, L, Hv, device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -394,8 +426,15 @@ def conv_silu(mixed, w, Hk, Hv, tail=None, valid=None, *, want_tail=True, new_ta
     K = w.shape[1]
     if tail is not None and (tail.shape != (B, K - 1, Cm) or tail.dtype != mixed.dtype):
         raise ValueError(f"tail must be [{B}, {K - 1}, {Cm}] in mixed's dtype")
-    _on(dev, mixed=mixed, w=w, tail=tail, new_tail=new_tail)
+    _on(dev, mixed=mixed, w=w, tail=tail)
+    if new_tail is not None:
+        check_buffer("new_tail", new_tail, (B, K - 1, Cm), mixed.dtype, dev)
     lengths = _lengths_from_valid(valid, B, L, dev)
+    if out is not None:
+        if len(out) != 3:
+            raise ValueError("out must be a tuple (q, k, v)")
+        for name, t, H in (("q", out[0], Hk), ("k", out[1], Hk), ("v", out[2], Hv)):
+            check_buffer(f"out {name}", t, (B, L, H, HEAD_DIM), mixed.dtype, dev)
     if out is None:
         q = torch.empty(B, L, Hk, HEAD_DIM, device=dev, dtype=mixed.dtype)
         k = torch.empty_like(q)
@@ -427,7 +466,9 @@ def gated_rmsnorm(x, z, w, eps, *, out=None):
     code = _dtype_code(x)
     if w.shape != (HEAD_DIM,) or w.dtype != torch.float32:
         raise ValueError("w must be float32 [128]")
-    _on(dev, x=x, z=z, w=w, out=out)
+    _on(dev, x=x, z=z, w=w)
+    if out is not None:
+        check_buffer("out", out, tuple(x.shape), x.dtype, dev)
     y = out if out is not None else torch.empty_like(x)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):

@@ -38,18 +38,12 @@ constexpr int kBufK = C * D * 2;                                       // one 64
 // LDS staging of one chunk (every wave reads every part of it): K, V (and Q) tiles of 64 rows x
 // 256 bytes, swizzled as below, and the record as written by the prep kernel. Two buffers: chunk
 // c + 1 is loaded while chunk c is computed.
-#ifndef GDR_SEG_WAVES_OUT
-#define GDR_SEG_WAVES_OUT 8
-#endif
-#ifndef GDR_SEG_WAVES_TRANSITION
-#define GDR_SEG_WAVES_TRANSITION 8
-#endif
 // Right-pad chunks of the output pass without the fused norm are taken kPadGroup at a time: their Q
 // tiles fill the Q, K and V regions of one buffer while the next group loads into the other.
 constexpr int kPadGroup = 3;
 template <bool kOut> struct SegCfg {
-  static constexpr int NW = kOut ? GDR_SEG_WAVES_OUT : GDR_SEG_WAVES_TRANSITION;   // waves per workgroup
-  static constexpr int NSL = (kOut ? 8 : 16) / NW;      // 16-column slices per wave
+  static constexpr int NW = 8;                          // waves per workgroup (two per SIMD)
+  static constexpr int NSL = (kOut ? 8 : 16) / NW;      // 16-column slices per wave: 1 (outputs), 2 (transitions)
   static constexpr int kK = 0, kV = kBufK, kRec = 2 * kBufK;
   static constexpr int kQ = kRec + kRecB;               // outputs only
   static constexpr int kZ = kQ + kBufK;                 // outputs only: the fused norm's gate rows
@@ -62,7 +56,7 @@ template <bool kOut> struct SegCfg {
   static constexpr int kRq = kPart + 2 * NW * C * 4;    // outputs only: |q_t|^2 of the chunk's tokens
   static constexpr int kLds = kOut ? kRq + kPadGroup * C * 4 : 2 * kBuf;
   static constexpr int kStores = kOut ? 4 * NSL : 0;    // output stores per wave per chunk
-  static_assert(NW == 4 || NW == 8, "row split written for four or eight waves");
+  static_assert(NW == 8, "the staging split and the P' block assignment are written for eight waves");
 };
 
 // K and Q tiles use the row swizzle swz of the device header. V tiles: position q ^ 2(r & 7), which
@@ -445,8 +439,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // token tile) also form the tile's Q Q^T on MFMA and leave its diagonal in LDS.
     if constexpr (kOut) {
       const unsigned char* Qt = Bf + Cfg::kQ;
-      // eight waves: one block each (waves 0..5); four waves: blocks w and w + 4
-      for (int blk = w; blk < (NW >= kFragBlocks ? w + 1 : kFragBlocks) && blk < kFragBlocks; blk += NW) {
+      // one block each for waves 0..5
+      for (int blk = w; blk < w + 1 && blk < kFragBlocks; ++blk) {
         const int mt = block_tile(blk), kb2 = block_kb(blk);
         f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)}, qq = f4_splat(0.f);
 #pragma unroll

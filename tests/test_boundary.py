@@ -352,3 +352,28 @@ def test_decode_ex_validates_fusion_like_prefill_ex():
     ptrs[3] = ptrs[4] = None
     st = lib.gdr_decode_ex(ctypes.byref(c.desc), *ptrs[:8], ctypes.byref(fu), ptrs[8], ptrs[9], None)
     assert st == EINVAL and "norm_eps" in gdr.last_error()
+
+
+# ---------------------------------------------------------------- caller-supplied outputs (binding)
+def test_binding_rejects_bad_output_buffers():
+    """The binding checks every caller-supplied output like the inputs: the C ABI sizes writes from
+    the descriptor and cannot see the real allocation (CPU tensors stand in for device ones here)."""
+    import torch
+    cpu = torch.device("cpu")
+    ok = torch.empty(2, 3, 4, 128, dtype=torch.bfloat16)
+    gdr.check_buffer("out", ok, (2, 3, 4, 128), torch.bfloat16, cpu)
+    bad = {
+        "short": torch.empty(2, 3, 3, 128, dtype=torch.bfloat16),
+        "dtype": torch.empty(2, 3, 4, 128, dtype=torch.float32),
+        "strided": torch.empty(2, 3, 128, 4, dtype=torch.bfloat16).transpose(2, 3),
+    }
+    for why, t in bad.items():
+        with pytest.raises(ValueError):
+            gdr.check_buffer("out", t, (2, 3, 4, 128), torch.bfloat16, cpu)
+    with pytest.raises(ValueError):   # another device
+        gdr.check_buffer("out", ok, (2, 3, 4, 128), torch.bfloat16, torch.device("cuda", 0))
+    gdr.check_workspace(torch.empty(100, dtype=torch.uint8), 100, cpu)
+    for ws in (torch.empty(99, dtype=torch.uint8), torch.empty(25, dtype=torch.float32),
+               torch.empty(200, dtype=torch.uint8)[::2], torch.empty(10, 10, dtype=torch.uint8)):
+        with pytest.raises(ValueError):
+            gdr.check_workspace(ws, 100, cpu)

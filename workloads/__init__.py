@@ -4,8 +4,8 @@ This module only draws random tensors. It holds none of the method's arithmetic 
 normalisation, no decay, no recurrence), so both the float64 oracle and the HIP path can
 be fed from it without sharing any computation.
 
-The regimes follow the input generator of the kernel-test page
-(``r15_kernel_test.py``, function ``regime``):
+The regimes are the numerical situations of the kernel-test page (``r15_kernel_test.py``,
+its input regimes), each a row of ``REGIME_TABLE`` read by one sampler:
 
 * ``R1``: random keys, strong decay: beta ~ U(0.2, 0.9), g ~ -U(0.05, 3.0)
 * ``R2``: random keys, weak decay:   beta ~ U(0.2, 0.9), g ~ -0.02 U(0, 1)
@@ -15,8 +15,8 @@ The regimes follow the input generator of the kernel-test page
 * ``LONG``: random keys, beta ~ U(0.2, 0.9), g ~ -U(0.0, 0.5)  (the long-prefill case)
 
 Draws are made in float32 with ``torch.Generator('cpu').manual_seed(seed)`` in the order
-q, k, v, beta, g, s0 (the page's order; ``R3`` draws its direction u between q and the key
-noise), then q, k and v are cast to the requested dtype. Right pads (positions at or past a
+q, k, v, beta, g, s0 (``R3`` draws its direction u between q and the key noise; constant gates
+draw nothing), then q, k and v are cast to the requested dtype. Right pads (positions at or past a
 row's length) get beta = g = 0 in the tensors as well, as the page on the fork model
 (``model.py``, class ``State`` docstring and ``_dn_gates``) makes pads exact no-ops.
 
@@ -29,9 +29,50 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Inputs", "draw", "config", "CONFIGS", "ConfigSpec", "LayerInputs", "draw_layer"]
+__all__ = ["Inputs", "draw", "config", "CONFIGS", "ConfigSpec", "LayerInputs", "draw_layer", "REGIME_TABLE",
+           "Regime"]
 
-REGIMES = ("R1", "R2", "R3", "R4", "LONG")
+@dataclass(frozen=True)
+class Regime:
+    """How one regime draws its keys and gates.
+
+    keys: "random" (k ~ N(0,1)), "direction" (k = u sqrt(D)/|u| + 0.3 N(0,1), one unit direction u per
+    (row, key head), drawn before the key noise) or "single" (one N(0,1) key per (row, key head),
+    repeated at every token). beta and decay: (base, width) for base + width U(0,1) (beta) and
+    -(base + width U(0,1)) (g), or a plain number for a constant.
+    """
+
+    keys: str
+    beta: object
+    decay: object
+
+
+REGIME_TABLE = {
+    "R1": Regime("random", (0.2, 0.7), (0.05, 2.95)),     # strong decay
+    "R2": Regime("random", (0.2, 0.7), (0.0, 0.02)),      # weak decay
+    "R3": Regime("direction", (0.3, 0.7), (0.0, 0.02)),   # correlated keys, weak decay
+    "R4": Regime("single", 0.5, 0.0),                     # one key, no decay
+    "LONG": Regime("random", (0.2, 0.7), (0.0, 0.5)),     # the long-prefill case
+}
+REGIMES = tuple(REGIME_TABLE)
+
+
+def _uniform(spec, shape, gen):
+    """base + width U(0, 1) for a (base, width) pair, else the constant."""
+    if isinstance(spec, tuple):
+        base, width = spec
+        return base + width * torch.rand(*shape, generator=gen)
+    return torch.full(shape, float(spec))
+
+
+def _keys(mode, B, L, Hk, D, gen):
+    if mode == "random":
+        return torch.randn(B, L, Hk, D, generator=gen)
+    if mode == "direction":
+        u = torch.randn(B, 1, Hk, D, generator=gen)
+        u = u / u.norm(dim=-1, keepdim=True) * D ** 0.5   # unit direction, length sqrt(D)
+        return u + 0.3 * torch.randn(B, L, Hk, D, generator=gen)
+    return torch.randn(B, 1, Hk, D, generator=gen).expand(B, L, Hk, D).contiguous()   # "single"
 
 
 @dataclass
@@ -58,6 +99,25 @@ class Inputs:
         return B, L, Hk, self.v.shape[2], D, self.v.shape[3]
 
 
+def _row_lengths(lengths, B, L, gen):
+    """(lengths [B] int64 or None, L): an int, a sequence, or "random:lo:hi" (drawn first; with L <= 0
+    the rows are padded to a whole number of 64-token chunks)."""
+    if lengths is None:
+        return None, L
+    if isinstance(lengths, str):
+        _, lo, hi = lengths.split(":")
+        lens = torch.randint(int(lo), int(hi) + 1, (B,), generator=gen, dtype=torch.int64)
+        if L <= 0:
+            L = 64 * math.ceil(int(lens.max()) / 64)
+        return lens, L
+    if isinstance(lengths, int):
+        return torch.full((B,), lengths, dtype=torch.int64), L
+    lens = torch.as_tensor(list(lengths), dtype=torch.int64)
+    if lens.shape != (B,):
+        raise ValueError("lengths must have B entries")
+    return lens, L
+
+
 def draw(B: int, L: int, Hk: int, Hv: int, D: int, regime: str, seed: int,
          dtype: torch.dtype = torch.float32, lengths=None, s0_rows: int = 0,
          s0_row=None, Dv: int | None = None, zero_pads: bool = True) -> Inputs:
@@ -68,56 +128,26 @@ def draw(B: int, L: int, Hk: int, Hv: int, D: int, regime: str, seed: int,
     s0_rows: 0 for no initial state, else the number of state rows to draw
     (0.1 N(0,1) each). s0_row: None or a sequence of B row indices into those rows.
     """
-    if regime not in REGIMES:
+    spec = REGIME_TABLE.get(regime)
+    if spec is None:
         raise ValueError(f"unknown regime {regime!r}")
     if Hv % Hk:
         raise ValueError("Hv must be a multiple of Hk")
     Dv = D if Dv is None else Dv
     gen = torch.Generator().manual_seed(seed)
-    lens = None
-    if isinstance(lengths, str):
-        _, lo, hi = lengths.split(":")
-        lens = torch.randint(int(lo), int(hi) + 1, (B,), generator=gen, dtype=torch.int64)
-        if L <= 0:  # pad to a whole number of 64-token chunks
-            L = 64 * math.ceil(int(lens.max()) / 64)
-    elif isinstance(lengths, int):
-        lens = torch.full((B,), lengths, dtype=torch.int64)
-    elif lengths is not None:
-        lens = torch.as_tensor(list(lengths), dtype=torch.int64)
-        if lens.shape != (B,):
-            raise ValueError("lengths must have B entries")
+    lens, L = _row_lengths(lengths, B, L, gen)
     q = torch.randn(B, L, Hk, D, generator=gen)
-    if regime in ("R1", "R2", "LONG"):
-        k = torch.randn(B, L, Hk, D, generator=gen)
-    elif regime == "R3":
-        u = torch.randn(B, 1, Hk, D, generator=gen)
-        u = u / u.norm(dim=-1, keepdim=True) * D ** 0.5
-        k = u + 0.3 * torch.randn(B, L, Hk, D, generator=gen)
-    else:  # R4: one key per (row, key head) for every token
-        k = torch.randn(B, 1, Hk, D, generator=gen).expand(B, L, Hk, D).contiguous()
+    k = _keys(spec.keys, B, L, Hk, D, gen)
     v = torch.randn(B, L, Hv, Dv, generator=gen)
-    if regime in ("R1", "LONG"):
-        beta = 0.2 + 0.7 * torch.rand(B, L, Hv, generator=gen)
-    elif regime in ("R2", "R3"):
-        beta = (0.2 if regime == "R2" else 0.3) + 0.7 * torch.rand(B, L, Hv, generator=gen)
-    else:
-        beta = torch.full((B, L, Hv), 0.5)
-    if regime == "R1":
-        g = -(0.05 + 2.95 * torch.rand(B, L, Hv, generator=gen))
-    elif regime in ("R2", "R3"):
-        g = -0.02 * torch.rand(B, L, Hv, generator=gen)
-    elif regime == "LONG":
-        g = -0.5 * torch.rand(B, L, Hv, generator=gen)
-    else:
-        g = torch.zeros(B, L, Hv)
+    beta = _uniform(spec.beta, (B, L, Hv), gen)
+    g = -_uniform(spec.decay, (B, L, Hv), gen) if isinstance(spec.decay, tuple) else \
+        torch.full((B, L, Hv), -float(spec.decay) + 0.0)
     s0 = torch.randn(s0_rows, Hv, D, Dv, generator=gen) * 0.1 if s0_rows else None
     if lens is not None and zero_pads:
-        pad = torch.arange(L)[None, :] >= lens[:, None]  # [B, L]
-        beta = beta.masked_fill(pad[..., None], 0.0)
-        g = g.masked_fill(pad[..., None], 0.0)
-    rows = None
-    if s0_row is not None:
-        rows = torch.as_tensor(list(s0_row), dtype=torch.int32)
+        pad = (torch.arange(L)[None, :] >= lens[:, None])[..., None]  # [B, L, 1]
+        beta = beta.masked_fill(pad, 0.0)
+        g = g.masked_fill(pad, 0.0)
+    rows = None if s0_row is None else torch.as_tensor(list(s0_row), dtype=torch.int32)
     return Inputs(q=q.to(dtype).contiguous(), k=k.to(dtype).contiguous(), v=v.to(dtype).contiguous(),
                   g=g.contiguous(), beta=beta.contiguous(),
                   lengths=None if lens is None else lens.to(torch.int32),
