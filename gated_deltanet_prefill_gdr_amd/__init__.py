@@ -127,7 +127,8 @@ def set_truncation(on: bool = True):
 
 
 def status_offset(desc: Desc):
-    """Byte offset of the finalize status word in the workspace, or None when the shape has no segments."""
+    """Byte offset of the status word (heads rerun without truncation) in the workspace, or None when the
+    shape has no segments."""
     n = library().gdr_prefill_status_offset(ctypes.byref(desc))
     return None if n == ctypes.c_size_t(-1).value else n
 

@@ -119,10 +119,12 @@ constexpr int kBufferConfig = 0x00020000;   // descriptor word 3 for the gfx9 fa
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferConfig);
 }
-// The same descriptor as four scalar words, for loads written as inline assembly.
+// The same descriptor as four scalar words, for loads written as inline assembly (made wave-uniform
+// explicitly, so that they stay in scalar registers also where the compiler cannot prove it).
 __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32) & 0xffff, (int)bytes, kBufferConfig};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff),
+               __builtin_amdgcn_readfirstlane((int)bytes), kBufferConfig};
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));

@@ -79,8 +79,8 @@ inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 
 // over the window (when every beta' there lies in [0, 2]). When a window with l2 <= -kTruncLog2 exists
 // for every boundary of a (row, head), the transition pass computes S~_j over that window alone and the
 // combine is skipped; the output pass records ||S(c_j - W)||_F, and the finalize pass checks the bound
-// eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <= 2^-24 ||S~_j||_F at every boundary, rerunning
-// the (row, head) without truncation where it fails.
+// eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <= 2^-24 ||S~_j||_F at every boundary, rerunning the
+// (row, head) without truncation where it fails.
 constexpr float kTruncLog2 = 40.f;     // a-priori window decay: 2^-40
 constexpr float kCertRel = 5.9604645e-8f;   // 2^-24
 constexpr int kTruncMaxW = 8;           // longest window, in chunks
@@ -91,7 +91,7 @@ struct PlanEntry {                      // per (row, head, boundary j), written 
   int32_t pad;
 };
 constexpr int kCertFloats = 16;         // [0, 8): per-wave ||S(c_j - W)||^2 parts, [8, 16): ||S~_j||^2 parts
-constexpr size_t kTruncHeader = 256;    // int32 status: (row, head) pairs rerun by the last call's finalize
+constexpr size_t kTruncHeader = 256;    // int32 status: (row, head) pairs the last call reran
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline size_t trunc_offset(int B, int Hv, int NC, size_t elem) {
@@ -144,7 +144,7 @@ struct ScanParams {
   int B, L, Hk, Hv, NC, n_s0;
   int P, Ls;         // segments and chunks per segment
   // truncated segment starts (bf16 with P > 1; see PlanEntry): plan [B Hv P], certificate parts
-  // [B Hv P][kCertFloats], the finalize status word; trunc = 0 forces the exact path everywhere
+  // [B Hv P][kCertFloats], the status word; trunc = 0 forces the exact path everywhere
   PlanEntry* plan;
   float* cert;
   int32_t* status;

@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void gdr_prep(PrepParams p) {
 // ====================================================================== bf16: per key head, persistent
 // LDS of the key-head prep: the K tile (swizzled 256-byte rows, written by DMA), and A, then T in
 // place, of two value heads.
-constexpr int kPrepPerCU = 3;   // resident workgroups per compute unit (what the registers allow)
+constexpr int kPrepPerCU = 3;   // resident workgroups per compute unit (measured: 4 is slower)
 struct PrepKhSmem {
   unsigned char k[C * 256];
   float m[2][kMatFloats];   // A, then T over it, of two value heads

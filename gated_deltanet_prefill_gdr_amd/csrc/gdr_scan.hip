@@ -718,6 +718,40 @@ __device__ __forceinline__ float* slot_ptr(const ScanParams& p, int b, int h, in
   return p.seg + (head_index(p, b, h) * p.P + j) * kSlotFloats;
 }
 
+// The certificate of a truncated (row, head): eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <=
+// 2^-24 ||S~_j||_F at every boundary j (the norms from the certificate parts the output and transition
+// passes left). Called by the whole workgroup: thread j - 1 loads boundary j's parts (all at once), thread
+// 0 runs the recurrence over them from LDS. `scratch` holds 3 P floats (P <= 256). False for NaN or
+// infinity.
+__device__ __forceinline__ bool certificate_holds(const ScanParams& p, size_t hb, float* scratch) {
+  const int t = threadIdx.x;
+  for (int jb = t + 1; jb < p.P; jb += blockDim.x) {
+    const float* ct = p.cert + (hb + jb) * kCertFloats;
+    float n1 = 0.f, n2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      n1 += ct[i];
+      n2 += ct[8 + i];
+    }
+    scratch[3 * jb] = __builtin_amdgcn_exp2f(p.plan[hb + jb].l2);
+    scratch[3 * jb + 1] = sqrtf(n1);
+    scratch[3 * jb + 2] = sqrtf(n2);
+  }
+  __syncthreads();
+  int ok = 1;
+  if (t == 0) {
+    float eps = 0.f;
+    for (int jb = 1; jb < p.P && ok; ++jb) {
+      eps = scratch[3 * jb] * (scratch[3 * jb + 1] + eps);
+      ok = eps <= kCertRel * scratch[3 * jb + 2];
+    }
+    scratch[0] = ok ? 1.f : 0.f;
+  }
+  __syncthreads();
+  return scratch[0] != 0.f;
+}
+
+
 // Outputs: one workgroup per (row, segment, value head), heads fastest.
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
@@ -777,27 +811,41 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<false>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
-  if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0;   // read by the finalize pass only
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0;   // read by the caller only
   const int t = threadIdx.x, jb_t = t + 1;
   int W = 0;
   float l2 = 0.f;
   if (p.trunc && jb_t < p.P) boundary_plan(p, b, h, jb_t, W, l2);
-  const bool trunc = __syncthreads_and(jb_t >= p.P || W > 0) != 0 && p.trunc;
-  const size_t hb = head_index(p, b, h) * p.P;
-  __shared__ int w_own;   // the window of this segment's own boundary j + 1
-  if (jb_t == j + 1) {
-    p.plan[hb + jb_t] = PlanEntry{W, l2, trunc ? 1 : 0, 0};
-    w_own = W;
-  }
+  // every boundary has a window: an AND over the workgroup in the first word of the (not yet used)
+  // staging area, so that the kernel needs no LDS beyond its two 40 KiB buffers
+  int* all_ok = reinterpret_cast<int*>(lds);
+  if (t == 0) *all_ok = 1;
   __syncthreads();
+  if (!(jb_t >= p.P || W > 0)) *all_ok = 0;
+  __syncthreads();
+  const bool trunc = *all_ok != 0 && p.trunc;
+  __syncthreads();   // read before the staging area is written
+  const size_t hb = head_index(p, b, h) * p.P;
+  if (jb_t == j + 1) p.plan[hb + jb_t] = PlanEntry{W, l2, trunc ? 1 : 0, 0};
   SegRun run{};
   run.src_kind = 0;
   run.end_b = slot_ptr(p, b, h, j + 1);
   if (trunc) {
+    // the window of this segment's own boundary, evaluated by every thread (the same few record words)
+    int w_own = 0;
+    float l2_own;
+    boundary_plan(p, b, h, j + 1, w_own, l2_own);
     run.c_end = (j + 1) * p.Ls;
     run.c_begin = run.c_end - w_own;
     run.end_m = nullptr;
     run.n2 = p.cert + (hb + j + 1) * kCertFloats + 8;
+    if (j == 0) {   // segment 0 enters with s0 (or zero); kept in slot 0, where a rerun starts from
+      int srow = 0;
+      const bool bad = row_is_bad(p, b, srow);   // bad rows are never truncated; kept for clarity
+      const float* s0 = (p.s0 && !bad) ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
+      float* s = slot_ptr(p, b, h, 0);
+      for (int i = t; i < D * D; i += 64 * SegCfg<false>::NW) s[(i / D) * 2 * D + i % D] = s0 ? s0[i] : 0.f;
+    }
   } else {
     run.c_begin = j * p.Ls;
     run.c_end = min(run.c_begin + p.Ls, p.NC);
@@ -807,44 +855,29 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   seg_body<false>(p, lds, b, h, run);
 }
 
+
 // Finalize (bf16 with P > 1): one workgroup per (row, value head). For a (row, head) that took the
-// truncated path it checks, boundary by boundary, eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <=
-// 2^-24 ||S~_j||_F (the norms from the certificate parts the output and transition passes left); where
-// that fails it counts the (row, head) in the status word and runs it again in one piece from its
-// entering state in slot 0 (s0 or zero, copied there by the combine), overwriting o and s_final.
+// truncated path it checks the certificate and, where it fails, counts the (row, head) in the status
+// word and runs it again in one piece from its entering state in slot 0 (s0 or zero, put there by the
+// transition pass), overwriting o and s_final. (Checking in the output pass's last workgroup per head
+// instead would need device-scope fences around a per-head counter, which write back and invalidate
+// the compute die's L2 once per workgroup and cost far more than this launch.)
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
-  __shared__ int redo;
   const int h = blockIdx.x % p.Hv, b = blockIdx.x / p.Hv;
   const size_t hb = head_index(p, b, h) * p.P;
   if (!p.trunc || !p.plan[hb + 1].trunc) return;   // exact path: nothing to check
-  if (threadIdx.x == 0) {
-    float eps = 0.f;
-    bool ok = true;
-    for (int jb = 1; jb < p.P && ok; ++jb) {
-      const PlanEntry e = p.plan[hb + jb];
-      const float* ct = p.cert + (hb + jb) * kCertFloats;
-      float n1 = 0.f, n2 = 0.f;
-      for (int i = 0; i < 8; ++i) {
-        n1 += ct[i];
-        n2 += ct[8 + i];
-      }
-      eps = __builtin_amdgcn_exp2f(e.l2) * (sqrtf(n1) + eps);
-      ok = eps <= kCertRel * sqrtf(n2);   // false for NaN or infinity as well
-    }
-    redo = ok ? 0 : 1;
-    if (!ok) atomicAdd(p.status, 1);
-  }
-  __syncthreads();
-  if (!redo) return;
-  SegRun run{};
-  run.c_begin = 0;
-  run.c_end = p.NC;
-  run.src_kind = 1;
-  run.src = slot_ptr(p, b, h, 0);
-  run.last = true;
-  run.cert_chunk = -1;
-  seg_body<true>(p, lds, b, h, run);
+  if (certificate_holds(p, hb, reinterpret_cast<float*>(lds))) return;
+  if (threadIdx.x == 0) atomicAdd(p.status, 1);
+  __syncthreads();   // the scratch is read before the staging area is written
+  SegRun all{};
+  all.c_begin = 0;
+  all.c_end = p.NC;
+  all.src_kind = 1;
+  all.src = slot_ptr(p, b, h, 0);
+  all.last = true;
+  all.cert_chunk = -1;
+  seg_body<true>(p, lds, b, h, all);
 }
 
 // Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero). One
@@ -886,6 +919,9 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   const int slice = lam % kSlices16, h = (lam / kSlices16) % p.Hv, b = lam / (kSlices16 * p.Hv);
   int srow = 0;
   if (row_is_bad(p, b, srow)) return;   // the output pass writes NaN for this row
+  // A truncated (row, head): the transition pass has left the entering state of every segment in its
+  // slot (slot 0: s0 or zero).
+  if (p.trunc && p.plan[((size_t)b * p.Hv + h) * p.P + 1].trunc) return;
   const int col = 16 * slice + n16;
   float* slots = p.seg + ((size_t)b * p.Hv + h) * p.P * kSlotFloats;
   i32x4 rs = rsrc_words(slots, (uint32_t)(p.P * kSlotFloats * sizeof(float)));
@@ -902,9 +938,6 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
-  // A truncated (row, head): the transition pass has already left the entering state of every
-  // segment j >= 1 in its slot, and segment 0's (s0 or zero) is now in slot 0.
-  if (p.trunc && p.plan[((size_t)b * p.Hv + h) * p.P + 1].trunc) return;
   // With no initial state S_1 = B_0, which is already in its slot: the chain starts at step 1.
   const int steps = p.P - 1, first = p.s0 ? 0 : 1;
   if (!p.s0 && steps > 0) {

@@ -215,9 +215,9 @@ gdr_status gdr_decode_ex(const gdr_desc* desc, const void* q, const void* k, con
  * any thread take the untruncated path (process-wide setting, not synchronised with calls in flight). */
 gdr_status gdr_set_truncation(int on);
 
-/* Byte offset in the workspace of an int32 that the finalize pass of the last gdr_prefill call on
- * that workspace sets to the number of (row, head) pairs it recomputed without truncation (valid once
- * the call has finished), or (size_t)-1 when this shape has no segments or the desc is invalid. */
+/* Byte offset in the workspace of an int32 that the last gdr_prefill call on that workspace sets to
+ * the number of (row, head) pairs it recomputed without truncation (valid once the call has finished),
+ * or (size_t)-1 when this shape has no segments or the desc is invalid. */
 size_t gdr_prefill_status_offset(const gdr_desc* desc);
 
 /* Message of the last non-OK status returned on this thread ("" if none). */

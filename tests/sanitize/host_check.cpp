@@ -159,7 +159,7 @@ int main() {
     expect(c.run() == GDR_OK, "timed call");
     double ms[GDR_KERNEL_COUNT];
     int64_t n[GDR_KERNEL_COUNT];
-    expect(gdr_timing_read(ms, n, GDR_KERNEL_COUNT) == GDR_OK && n[GDR_KERNEL_PREP] == 1 && n[GDR_KERNEL_FINALIZE] == 1,
+    expect(gdr_timing_read(ms, n, GDR_KERNEL_COUNT) == GDR_OK && n[GDR_KERNEL_PREP] == 1 && n[GDR_KERNEL_SCAN] == 1,
            "timing read");
     gdr_timing_enable(0);
   }

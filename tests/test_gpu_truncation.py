@@ -2,10 +2,9 @@
 
 For bf16 sequences cut into segments, the state entering a segment may be taken from the last few
 chunks of the segment before it, run from zero, when their decay bounds the dropped term by 2^-40
-of the state where that window starts; a finalize pass checks the carried bound against the
-measured state norms and reruns a (row, head) in one piece where it exceeds 2^-24. These tests
-check the results against the oracle on both paths, and read the finalize pass's status word (the
-number of (row, head) pairs it reran) and the plan entries from the workspace.
+of the state where that window starts; a finalize pass checks the carried bound against the measured
+state norms and reruns a (row, head) in one piece where it exceeds 2^-24. These tests check the results against the oracle on both paths, and read the status word (the
+number of (row, head) pairs rerun) and the plan entries from the workspace.
 """
 import numpy as np
 import pytest
@@ -36,8 +35,8 @@ def seg_plan(B, Hv, NC):
 
 
 def run(x, in_place=False):
-    """Prefill through the binding with a workspace of our own; returns o, s_final, the finalize
-    status word and the per-(row, head) truncation flags (None without segments)."""
+    """Prefill through the binding with a workspace of our own; returns o, s_final, the status word and
+    the per-(row, head) truncation flags (None without segments)."""
     d = to_dev(x)
     B, L, Hk, Hv, Dk, Dv = x.shape
     desc = gdr.make_desc(B, L, Hk, Hv, 0 if x.s0 is None else x.s0.shape[0], True, False)
