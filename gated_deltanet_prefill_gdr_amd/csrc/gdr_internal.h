@@ -29,7 +29,8 @@ constexpr int kScalarBytes = 8 * kChunk * 4;
 constexpr int kScA = 0, kScC = 1, kScD = 2, kScEgC = 3, kScGam2 = 4, kScRk = 5, kScRq = 6;   // rows of 64
 // bf16 records use neither c nor rq; their row 6 holds at [6][0] the flag kBetaOk (1 when every
 // beta' of the chunk lies in [0, 2], where each token's map S -> e^{g'} (I - beta' k_hat k_hat^T) S
-// has spectral norm at most e^{g'}; 0 otherwise).
+// has spectral norm at most e^{g'}, and the chunk's decay sum is <= 0, so that the chunk's map has
+// spectral norm at most 1; 0 otherwise).
 constexpr int kScBetaOk = 6;
 
 inline size_t record_bytes(size_t elem) {

@@ -697,9 +697,10 @@ __global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p
           sc[kScEgC * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
           sc[kScGam2 * C + lane] = g2;
           sc[kScRk * C + lane] = rkl;
-          // every beta' of the chunk in [0, 2]: then each token's map has spectral norm <= e^{g'}
+          // every beta' of the chunk in [0, 2] (each token's map then has spectral norm <= e^{g'}) and
+          // the chunk's decay sum <= 0: the chunk's map has spectral norm <= e^{sum g'} <= 1
           const float bt = sm.bet[j + i][lane];
-          const bool ok = __all(bt >= 0.f && bt <= 2.f);
+          const bool ok = __all(bt >= 0.f && bt <= 2.f) && g2C <= 0.f;
           sc[kScBetaOk * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
         };
         inverse_to_records<__bf16>(sm.m[0], sm.m[1], sm.gam[j], sm.gam[j + nh - 1], sm.rk, sm.bet[j],

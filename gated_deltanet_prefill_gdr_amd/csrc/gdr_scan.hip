@@ -151,9 +151,9 @@ struct SegRun {
   bool last;            // outputs: the run ends the row, so it writes s_final
   int cert_chunk;       // outputs: at the top of this chunk (-1: none) each wave writes the sum of
   float* cert;          //   squares of its part of the state into cert[wave]
-  float* end_b;         // transitions: the state of the value columns (slot, pitch 2D)
+  float* end_b;         // transitions, windows: the end state of the value columns (slot, pitch 2D)
   float* end_m;         // transitions: the identity columns' state M (slot columns 128.., or null)
-  float* n2;            // transitions: each wave's sum of squares of its value columns (or null)
+  float* n2;            // windows: each wave's sum of squares of the end state (transitions: null)
 };
 
 // Sum over the 64 lanes of a wave, in every lane.
@@ -163,8 +163,11 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-template <bool kOut>
+// kWin (with kOut): a window, the chunks c_begin .. c_end - 1 run from zero on the value columns in
+// the output pass's layout but without its outputs; it leaves the end state and its norm.
+template <bool kOut, bool kWin = false>
 __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds, int b, int h, const SegRun& run) {
+  static_assert(kOut || !kWin, "a window runs in the output pass's layout");
   using Cfg = SegCfg<kOut>;
   constexpr int NSL = Cfg::NSL, NW = Cfg::NW;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -178,7 +181,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   __bf16* og = reinterpret_cast<__bf16*>(p.o);
 
   int srow = 0;
-  if (kOut && row_is_bad(p, b, srow)) {
+  if (kOut && !kWin && row_is_bad(p, b, srow)) {
     const float nan = __builtin_nanf("");
     const int t_end = min(c_end * C, p.L);
     for (int i = c_begin * C * D + tid; i < t_end * D; i += 64 * NW)
@@ -301,6 +304,101 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
             for (int i = 0; i < 4; ++i)   // zero, or e_k for the identity columns
               S[sl][kb][s2][i] = (seg_col<kOut>(w, sl) + n16 - D == 32 * kb + 8 * G + 4 * s2 + i) ? 1.f : 0.f;
     }
+  }
+
+  if constexpr (kWin) {
+    // Every chunk of a window holds valid tokens (the plan makes sure): no pads, no Q, no outputs.
+    constexpr int kParts = kStK | kStV | kStRec;
+    if (c_begin < c_end) issue(c_begin, kParts);
+    for (int c = c_begin; c < c_end; ++c) {
+      wait_and_barrier<0>();   // chunk c has landed; every wave is done with chunk c - 1's buffer
+      if (c + 1 < c_end) issue(c + 1, kParts);
+      const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
+      const unsigned char* Kt = Bf + Cfg::kK;
+      const float* sc = reinterpret_cast<const float*>(Bf + Cfg::kRec + kScOff);
+      bf16x8 Sop[NSL][4];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
+      // X = K S, R = V - diag(a) X, Delta = Tb R (lower-triangular blocks only)
+      f4 X[NSL][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 kf = lds16(Kt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = mfma(kf, Sop[sl][kb], X[sl][mt]);
+        }
+      }
+      bf16x8 Rop[NSL][2];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        f4 R[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          R[mt] = v_col4(Bf + Cfg::kV, 16 * mt + 4 * G, seg_col<kOut>(w, sl), n16) -
+                  *reinterpret_cast<const f4*>(sc + 16 * mt + 4 * G) * X[sl][mt];
+        Rop[sl][0] = pack8(R[0], R[1]);
+        Rop[sl][1] = pack8(R[2], R[3]);
+      }
+      f4 Dl[NSL][4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = f4_splat(0.f);
+#pragma unroll
+        for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
+          const bf16x8 tf = lds16(Bf + Cfg::kRec + 1024 * frag_block(mt, kb2) + 16 * lane);
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = mfma(tf, Rop[sl][kb2], Dl[sl][mt]);
+        }
+        const f4 d4 = *reinterpret_cast<const f4*>(sc + 2 * C + 16 * mt + 4 * G);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] *= d4;   // diag(d) Delta
+      }
+      bf16x8 Ddop[NSL][2];   // the operand K^T diag(d) Delta is formed from
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        Ddop[sl][0] = pack8(Dl[sl][0], Dl[sl][1]);
+        Ddop[sl][1] = pack8(Dl[sl][2], Dl[sl][3]);
+      }
+      // S <- e^{gamma_63} S + K^T diag(d) Delta
+      const float egc = sc[3 * C];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] *= egc;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {
+            const bf16x8 kt = kt_frag(Kt, kb, s2, kb2, G, n16);
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] = mfma(kt, Ddop[sl][kb2], S[sl][kb][s2]);
+          }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // no load into LDS may still be in flight when the workgroup ends
+    float ss = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = S[sl][kb][s2][i];
+            ss += x * x;
+            run.end_b[(32 * kb + 8 * G + 4 * s2 + i) * 2 * D + seg_col<kOut>(w, sl) + n16] = x;
+          }
+    ss = wave_sum(ss);
+    if (lane == 0) run.n2[w] = ss;
+    return;
   }
 
   // Output tiles of a chunk and, with the fused gated RMSNorm, its gate values. The norm needs each
@@ -676,21 +774,6 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
   // ---- end state
   if (kOut && !(p.s_final && run.last)) return;
-  if (!kOut && run.n2) {   // each wave's sum of squares of its value columns
-    float ss = 0.f;
-#pragma unroll
-    for (int sl = 0; sl < NSL; ++sl) {
-      if (!seg_has_v<kOut>(sl)) continue;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ss += S[sl][kb][s2][i] * S[sl][kb][s2][i];
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) run.n2[w] = ss;
-  }
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl) {
     float* dst;
@@ -781,19 +864,30 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
 __device__ __forceinline__ void boundary_plan(const ScanParams& p, int b, int h, int jb, int& W, float& l2) {
   W = 0;
   l2 = 0.f;
+  const int cb = jb * p.Ls;
+  const int wmax = min(min(p.Ls, kTruncMaxW), cb);
+  // every candidate chunk's flag and decay first (chunks cb - wmax .. cb - 1 < NC), all loads at once
+  const unsigned char* recs = reinterpret_cast<const unsigned char*>(p.ws) + head_index(p, b, h) * p.NC * kRecB;
+  float flag[kTruncMaxW], dec[kTruncMaxW];
+#pragma unroll
+  for (int w = 1; w <= kTruncMaxW; ++w) {
+    flag[w - 1] = 0.f;
+    dec[w - 1] = 0.f;
+    if (w <= wmax) {
+      const float* sc = reinterpret_cast<const float*>(recs + (size_t)(cb - w) * kRecB + kScOff);
+      flag[w - 1] = sc[kScBetaOk * C];
+      dec[w - 1] = sc[kScGam2 * C + C - 1];   // the chunk's whole decay, in log2
+    }
+  }
   int srow = 0;
   if (row_is_bad(p, b, srow)) return;
   const int len = p.lengths ? p.lengths[b] : p.L;
-  const int c_valid = (len + C - 1) / C;   // chunks that hold valid tokens
-  const int cb = jb * p.Ls;
-  if (cb > c_valid) return;
-  const unsigned char* recs = reinterpret_cast<const unsigned char*>(p.ws) + head_index(p, b, h) * p.NC * kRecB;
-  const int wmax = min(min(p.Ls, kTruncMaxW), cb);
+  if (cb > (len + C - 1) / C) return;   // the window would reach into the row's pads
   float acc = 0.f;
-  for (int w = 1; w <= wmax; ++w) {
-    const float* sc = reinterpret_cast<const float*>(recs + (size_t)(cb - w) * kRecB + kScOff);
-    if (!(sc[kScBetaOk * C] == 1.f)) return;
-    acc += sc[kScGam2 * C + C - 1];   // the chunk's whole decay, in log2
+#pragma unroll
+  for (int w = 1; w <= kTruncMaxW; ++w) {
+    if (w > wmax || !(flag[w - 1] == 1.f)) return;
+    acc += dec[w - 1];
     if (acc <= -kTruncLog2) {
       W = w;
       l2 = acc;
@@ -802,43 +896,55 @@ __device__ __forceinline__ void boundary_plan(const ScanParams& p, int b, int h,
   }
 }
 
+// Every chunk of row b, head h from start to the last boundary that holds valid tokens contracts (its
+// flag: every beta' in [0, 2] and a decay sum <= 0, so that its state map has spectral norm <= 1), checked
+// by the workgroup's threads together (thread t: chunks t, t + stride, ...). Then an error in the state
+// at one boundary does not grow on its way to the next window.
+__device__ __forceinline__ bool chunks_contract(const ScanParams& p, int b, int h, int t, int stride) {
+  const unsigned char* recs = reinterpret_cast<const unsigned char*>(p.ws) + head_index(p, b, h) * p.NC * kRecB;
+  const int c_last = (p.P - 1) * p.Ls;   // < NC
+  const int len = p.lengths ? min(max(p.lengths[b], 0), p.L) : p.L;   // loaded beside the flags
+  bool ok = true;
+  for (int c = t; c < c_last; c += stride) {
+    const float f = reinterpret_cast<const float*>(recs + (size_t)c * kRecB + kScOff)[kScBetaOk * C];
+    ok = ok && (f == 1.f || c >= (len + C - 1) / C);
+  }
+  return ok;
+}
+
 // Transitions: one workgroup per (row, segment j < P - 1, value head). Every workgroup first plans the
 // boundaries of its (row, head) (thread t: boundary t + 1; P <= 256 < threads); the (row, head) is
-// truncated when every boundary has a window. Then segment j's workgroup either runs the window before
-// boundary j + 1 from zero, leaving the entering state of segment j + 1 in its slot (truncated), or
-// runs the whole segment on the augmented start [0 | I], leaving B_j and M_j (exact).
+// truncated when every boundary has a window and every chunk up to the last boundary contracts. Then
+// segment j's workgroup either runs the window before boundary j + 1 from zero on the value columns
+// alone (the output pass's layout, without outputs), leaving the entering state of segment j + 1 in its
+// slot and its norm in the certificate (truncated), or runs the whole segment on the augmented start
+// [0 | I], leaving B_j and M_j for the combine (exact). The grid is below 256 + B Hv workgroups, so
+// the output pass's larger LDS (one workgroup per CU) costs no parallelism.
+static_assert(SegCfg<true>::kLds >= SegCfg<false>::kLds && SegCfg<true>::NW == SegCfg<false>::NW, "shared LDS");
 __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(ScanParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<false>::kLds];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0;   // read by the caller only
   const int t = threadIdx.x, jb_t = t + 1;
+  const bool contract = !p.trunc || chunks_contract(p, b, h, t, blockDim.x);
   int W = 0;
   float l2 = 0.f;
   if (p.trunc && jb_t < p.P) boundary_plan(p, b, h, jb_t, W, l2);
   // every boundary has a window: an AND over the workgroup in the first word of the (not yet used)
-  // staging area, so that the kernel needs no LDS beyond its two 40 KiB buffers
+  // staging area; the second word passes on the window of boundary j + 1
   int* all_ok = reinterpret_cast<int*>(lds);
   if (t == 0) *all_ok = 1;
   __syncthreads();
-  if (!(jb_t >= p.P || W > 0)) *all_ok = 0;
+  if (!(jb_t >= p.P || W > 0) || !contract) *all_ok = 0;
+  if (jb_t == j + 1) all_ok[1] = W;
   __syncthreads();
   const bool trunc = *all_ok != 0 && p.trunc;
+  const int w_own = all_ok[1];
   __syncthreads();   // read before the staging area is written
   const size_t hb = head_index(p, b, h) * p.P;
   if (jb_t == j + 1) p.plan[hb + jb_t] = PlanEntry{W, l2, trunc ? 1 : 0, 0};
-  SegRun run{};
-  run.src_kind = 0;
-  run.end_b = slot_ptr(p, b, h, j + 1);
   if (trunc) {
-    // the window of this segment's own boundary, evaluated by every thread (the same few record words)
-    int w_own = 0;
-    float l2_own;
-    boundary_plan(p, b, h, j + 1, w_own, l2_own);
-    run.c_end = (j + 1) * p.Ls;
-    run.c_begin = run.c_end - w_own;
-    run.end_m = nullptr;
-    run.n2 = p.cert + (hb + j + 1) * kCertFloats + 8;
     if (j == 0) {   // segment 0 enters with s0 (or zero); kept in slot 0, where a rerun starts from
       int srow = 0;
       const bool bad = row_is_bad(p, b, srow);   // bad rows are never truncated; kept for clarity
@@ -846,12 +952,23 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
       float* s = slot_ptr(p, b, h, 0);
       for (int i = t; i < D * D; i += 64 * SegCfg<false>::NW) s[(i / D) * 2 * D + i % D] = s0 ? s0[i] : 0.f;
     }
-  } else {
-    run.c_begin = j * p.Ls;
-    run.c_end = min(run.c_begin + p.Ls, p.NC);
-    run.end_m = slot_ptr(p, b, h, j);
-    run.n2 = nullptr;
+    SegRun win{};   // chunks (j + 1) Ls - W .. (j + 1) Ls - 1
+    win.c_end = (j + 1) * p.Ls;
+    win.c_begin = win.c_end - w_own;
+    win.src_kind = 0;
+    win.cert_chunk = -1;
+    win.n2 = p.cert + (hb + j + 1) * kCertFloats + 8;
+    win.end_b = slot_ptr(p, b, h, j + 1);
+    seg_body<true, true>(p, lds, b, h, win);
+    return;
   }
+  SegRun run{};
+  run.src_kind = 0;
+  run.end_b = slot_ptr(p, b, h, j + 1);
+  run.c_begin = j * p.Ls;
+  run.c_end = min(run.c_begin + p.Ls, p.NC);
+  run.end_m = slot_ptr(p, b, h, j);
+  run.n2 = nullptr;
   seg_body<false>(p, lds, b, h, run);
 }
 
