@@ -17,9 +17,9 @@
 // are the identity map: the transitions skip them and the output pass gives them a short loop of
 // their own (O = diag(rq) Q S).
 //
-// gdr_scan_f32: float32 inputs; one workgroup per (row, value head, 64-column slice), each wave
-// owning 16 columns and walking all chunks on its own (fp32 MFMA, K^T staged in LDS, each chunk
-// loaded into registers one chunk ahead).
+// gdr_scan_f32: float32 inputs; one workgroup per (row, value head, 16-column slice), its four
+// waves splitting the slice's state by key blocks and walking all chunks together (fp32 MFMA, each
+// chunk loaded into registers one chunk ahead).
 #include "gdr_device.h"
 
 namespace gdr {
@@ -1157,27 +1157,38 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
 
 // ====================================================================== fp32 scan
 constexpr int kRecF = 2 * kFragBlocks * kBlockElems * 4 + kScalarBytes;   // fp32 record bytes (26624)
-constexpr int kPK32 = D + 4, kPT32 = C + 4;
+constexpr int kPK32 = D + 4, kPT32 = C + 4, kPV32 = 16 + 4;
 
 struct ScanSmemF {
   float k[C * kPK32];      // K chunk, [token][dk]
   float q[C * kPK32];      // Q chunk, [token][dk]
-  float kt[D * kPT32];     // K chunk transposed, [dk][token]
   float tb[C * kPT32];     // T diag(beta'), [token][token]
   float pm[C * kPT32];     // decayed causal scores, [token][token]
-  float v[C * kPT32];      // this workgroup's 64 value columns, [token][col]
+  float v[C * kPV32];      // this workgroup's 16 value columns, [token][col]
   float sc[4 * C];         // a, c, d, e^{gamma_63}
+  f4 xp[4][4][64];         // [wave][token tile][lane]: the waves' partial K S over their 32 keys
+  f4 op[4][4][64];         // the same for Q S
 };
 
+// One workgroup per (row, value head, 16-column slice); wave w owns keys 32 w .. 32 w + 31 of the
+// slice's state (two accumulator tiles) and the chunk's token tile w of the outputs. Per chunk:
+// every wave forms its key block's share of X = K S and of Q S (the state's rows split the sum),
+// the shares meet in LDS, every wave sums X and forms R = V - diag(a) X and Delta = Tb R in full,
+// its output tile O_w = diag(c) (Q S)_w + P_w Delta, and its own key block of
+// S <- e^{gamma_63} S + K^T diag(d) Delta, whose K^T operand it reads from the K tile as stored
+// (one element per lane and slot, the sixteen keys of a read on distinct banks). The chunk's tiles
+// are loaded into registers one chunk ahead and written to LDS after the chunk before it is done.
 __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
   __shared__ __attribute__((aligned(16))) ScanSmemF sm;
-  constexpr int NW = 4, NT = 256;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NT = 256;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, G = lane >> 4;
-  const int cg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);   // the slices of a head on one XCD (one L2)
+  const int cs = lam % kSlices16, h = (lam / kSlices16) % p.Hv, b = lam / (kSlices16 * p.Hv);
   const int kh = h / (p.Hv / p.Hk);
-  const int col0 = cg * (16 * NW);
-  const int ncol = col0 + 16 * wave + n16;
+  const int col0 = 16 * cs;
+  const int ncol = col0 + n16;
   const float* qg = reinterpret_cast<const float*>(p.q);
   const float* kg = reinterpret_cast<const float*>(p.k);
   const float* vg = reinterpret_cast<const float*>(p.v);
@@ -1188,28 +1199,26 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
   const int srow = p.s0 ? (p.s0_row ? p.s0_row[b] : b) : 0;
   if ((len < 0 || len > p.L) || (p.s0 && (srow < 0 || srow >= p.n_s0))) {
     const float nan = __builtin_nanf("");
-    for (int i = tid; i < p.L * 16 * NW; i += NT)
-      og[((size_t)b * p.L + i / (16 * NW)) * p.Hv * D + (size_t)h * D + col0 + i % (16 * NW)] = nan;
+    for (int i = tid; i < p.L * 16; i += NT) og[((size_t)b * p.L + i / 16) * p.Hv * D + (size_t)h * D + col0 + i % 16] = nan;
     if (p.s_final)
-      for (int i = tid; i < D * 16 * NW; i += NT)
-        p.s_final[(((size_t)b * p.Hv + h) * D + i / (16 * NW)) * D + col0 + i % (16 * NW)] = nan;
+      for (int i = tid; i < D * 16; i += NT) p.s_final[(((size_t)b * p.Hv + h) * D + i / 16) * D + col0 + i % 16] = nan;
     return;
   }
 
-  f4 S[8];
+  // this wave's key block: tiles st = 0, 1 are keys 32 wave + 16 st + 4 G + e, column ncol
+  f4 S[2];
   {
     const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[st][e] = s0 ? s0[(16 * st + 4 * G + e) * D + ncol] : 0.f;
+      for (int e = 0; e < 4; ++e) S[st][e] = s0 ? s0[(32 * wave + 16 * st + 4 * G + e) * D + ncol] : 0.f;
   }
 
-  // Chunk staging, one chunk ahead: the global loads of chunk c + 1 are issued into registers right
-  // after chunk c's tiles are in LDS, and land while chunk c computes. Per thread: eight 16-byte
-  // pieces of K and of Q, six of the record's Tb and P operand blocks (12 blocks of 64 lanes x 8),
-  // four of V and (64 threads) one of the scalars.
-  f4 kr[8], qr[8], rr[6], vr[4], sr = f4_splat(0.f);
+  // Chunk staging, one chunk ahead. Per thread: eight 16-byte pieces of K and of Q, six of the
+  // record's Tb and P operand blocks (12 blocks of 64 lanes x 8), one of V and (64 threads) one of
+  // the scalars.
+  f4 kr[8], qr[8], rr[6], vr, sr = f4_splat(0.f);
   auto load = [&](int c) {
     const int t0 = c * C;
     const unsigned char* rec = wsb + (((size_t)b * p.Hv + h) * p.NC + c) * kRecF;
@@ -1229,11 +1238,10 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
       rr[i] = *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(rec) + (q >> 7) * kBlockElems + ((q & 127) >> 1) * 8 +
                                            4 * (q & 1));
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + NT * i, row = idx >> 4, cv = idx & 15, t = t0 + row;
-      vr[i] = t < p.L ? *reinterpret_cast<const f4*>(vg + ((size_t)b * p.L + t) * p.Hv * D + (size_t)h * D + col0 + 4 * cv)
-                      : f4_splat(0.f);
+    {
+      const int row = tid >> 2, cv = tid & 3, t = t0 + row;
+      vr = t < p.L ? *reinterpret_cast<const f4*>(vg + ((size_t)b * p.L + t) * p.Hv * D + (size_t)h * D + col0 + 4 * cv)
+                   : f4_splat(0.f);
     }
     if (tid < C) sr = *reinterpret_cast<const f4*>(rec + 2 * kFragBlocks * kBlockElems * 4 + 16 * tid);
   };
@@ -1243,8 +1251,6 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
       const int idx = tid + NT * i, row = idx >> 5, cv = idx & 31;
       *reinterpret_cast<f4*>(&sm.k[row * kPK32 + 4 * cv]) = kr[i];
       *reinterpret_cast<f4*>(&sm.q[row * kPK32 + 4 * cv]) = qr[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.kt[(4 * cv + e) * kPT32 + row] = kr[i][e];
     }
 #pragma unroll
     for (int i = 0; i < 6; ++i) {   // lane (m, g) of block (tile I, kb): row 16 I + m, columns 32 kb + 4g (+16)
@@ -1252,11 +1258,7 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
       const int row = 16 * block_tile(bk) + (ln & 15), col = 32 * block_kb(bk) + 4 * (ln >> 4) + 16 * (q & 1);
       *reinterpret_cast<f4*>(&(blk < kFragBlocks ? sm.tb : sm.pm)[row * kPT32 + col]) = rr[i];
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = tid + NT * i, row = idx >> 4, cv = idx & 15;
-      *reinterpret_cast<f4*>(&sm.v[row * kPT32 + 4 * cv]) = vr[i];
-    }
+    *reinterpret_cast<f4*>(&sm.v[(tid >> 2) * kPV32 + 4 * (tid & 3)]) = vr;
     if (tid < C) *reinterpret_cast<f4*>(&sm.sc[4 * tid]) = sr;
   };
   // Tb and P are zero above their stored blocks (rows 0..31, columns 32..63); the blocks never
@@ -1268,6 +1270,7 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
   }
   if (p.NC > 0) load(0);
 
+  const f4 one = f4_splat(1.f);
   for (int c = 0; c < p.NC; ++c) {
     const int t0 = c * C;
     __syncthreads();   // the previous chunk is done with LDS
@@ -1275,43 +1278,43 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
     __syncthreads();
     if (c + 1 < p.NC) load(c + 1);
 
+    // this key block's shares of K S and Q S
+    const Frag<float> Sf = acc_frag<float>(S[0], S[1], one, one);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f4 x = f4_splat(0.f), o = f4_splat(0.f);
+      mma(x, lds_frag(sm.k, kPK32, 16 * mt + n16, 32 * wave, G), Sf);
+      mma(o, lds_frag(sm.q, kPK32, 16 * mt + n16, 32 * wave, G), Sf);
+      sm.xp[wave][mt][lane] = x;
+      sm.op[wave][mt][lane] = o;
+    }
+    __syncthreads();
+
     const float* sa = sm.sc;
     const float* scc = sm.sc + C;
     const float* sd = sm.sc + 2 * C;
     const float egC = sm.sc[3 * C];
-    const f4 one = f4_splat(1.f);
-
-    Frag<float> Sf[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Sf[kb] = acc_frag<float>(S[2 * kb], S[2 * kb + 1], one, one);
-    f4 X[4], OQ[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      X[mt] = f4_splat(0.f);
-      OQ[mt] = f4_splat(0.f);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        mma(X[mt], lds_frag(sm.k, kPK32, 16 * mt + n16, 32 * kb, G), Sf[kb]);
-        mma(OQ[mt], lds_frag(sm.q, kPK32, 16 * mt + n16, 32 * kb, G), Sf[kb]);
-      }
-    }
+    // R = V - diag(a) X over the chunk's 64 tokens
     f4 R[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 4; ++mt) {
+      const f4 X = sm.xp[0][mt][lane] + sm.xp[1][mt][lane] + sm.xp[2][mt][lane] + sm.xp[3][mt][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * mt + 4 * G + e;
-        R[mt][e] = sm.v[t * kPT32 + 16 * wave + n16] - sa[t] * X[mt][e];
+        R[mt][e] = sm.v[t * kPV32 + n16] - sa[t] * X[e];
       }
+    }
     Frag<float> Rf[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Rf[kb] = acc_frag<float>(R[2 * kb], R[2 * kb + 1], one, one);
+    // Delta = Tb R (the blocks above the diagonal are zero: token tiles 0, 1 need key block 0 only)
     f4 Dl[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       Dl[mt] = f4_splat(0.f);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(Dl[mt], lds_frag(sm.tb, kPT32, 16 * mt + n16, 32 * kb, G), Rf[kb]);
+      for (int kb = 0; kb <= (mt >> 1); ++kb) mma(Dl[mt], lds_frag(sm.tb, kPT32, 16 * mt + n16, 32 * kb, G), Rf[kb]);
     }
     Frag<float> Df[2], Ddf[2];
 #pragma unroll
@@ -1325,33 +1328,47 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
       }
       Ddf[kb] = acc_frag<float>(Dl[2 * kb], Dl[2 * kb + 1], d0, d1);
     }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    // output tile `wave`: O = diag(c) Q S + P Delta
+    {
+      const int mt = wave;
+      const f4 qs = sm.op[0][mt][lane] + sm.op[1][mt][lane] + sm.op[2][mt][lane] + sm.op[3][mt][lane];
       f4 O;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[e] = scc[16 * mt + 4 * G + e] * OQ[mt][e];
+      for (int e = 0; e < 4; ++e) O[e] = scc[16 * mt + 4 * G + e] * qs[e];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(O, lds_frag(sm.pm, kPT32, 16 * mt + n16, 32 * kb, G), Df[kb]);
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= (mt >> 1)) mma(O, lds_frag(sm.pm, kPT32, 16 * mt + n16, 32 * kb, G), Df[kb]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = t0 + 16 * mt + 4 * G + e;
         if (t < p.L) og[((size_t)b * p.L + t) * p.Hv * D + (size_t)h * D + ncol] = O[e];
       }
     }
+    // this key block of S <- e^{gamma_63} S + K^T diag(d) Delta; the K^T operand row (key) is
+    // column 32 wave + 16 st + n16 of the K tile, its slots the tokens 32 kb + 4 G + j (+ 16)
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
+    for (int st = 0; st < 2; ++st) {
       S[st] *= egC;
+      const int key = 32 * wave + 16 * st + n16;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) mma(S[st], lds_frag(sm.kt, kPT32, 16 * st + n16, 32 * kb, G), Ddf[kb]);
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<float> kt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kt.v[j] = sm.k[(32 * kb + 4 * G + j) * kPK32 + key];
+          kt.v[4 + j] = sm.k[(32 * kb + 16 + 4 * G + j) * kPK32 + key];
+        }
+        mma(S[st], kt, Ddf[kb]);
+      }
     }
   }
 
   if (p.s_final) {
     float* sf = p.s_final + ((size_t)b * p.Hv + h) * D * D;
 #pragma unroll
-    for (int st = 0; st < 8; ++st)
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sf[(16 * st + 4 * G + e) * D + ncol] = S[st][e];
+      for (int e = 0; e < 4; ++e) sf[(32 * wave + 16 * st + 4 * G + e) * D + ncol] = S[st][e];
   }
 }
 
@@ -1374,7 +1391,7 @@ hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s) {
   if (qkv_bf16) {
     hipLaunchKernelGGL(gdr_scan_bf16, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
   } else {
-    hipLaunchKernelGGL(gdr_scan_f32, dim3(D / 64, p.Hv, p.B), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(gdr_scan_f32, dim3(p.B * p.Hv * kSlices16), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
