@@ -804,34 +804,40 @@ __device__ __forceinline__ float* slot_ptr(const ScanParams& p, int b, int h, in
 // The certificate of a truncated (row, head): eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <=
 // 2^-24 ||S~_j||_F at every boundary j (the norms from the certificate parts the output and transition
 // passes left). Called by the whole workgroup: thread j - 1 loads boundary j's parts (all at once), thread
-// 0 runs the recurrence over them from LDS. `scratch` holds 3 P floats (P <= 256). False for NaN or
-// infinity.
-__device__ __forceinline__ bool certificate_holds(const ScanParams& p, size_t hb, float* scratch) {
-  const int t = threadIdx.x;
-  for (int jb = t + 1; jb < p.P; jb += blockDim.x) {
+// 0 runs the recurrence over them from LDS. `scratch` holds 3 P floats (P <= 256). Returns 0 for a
+// (row, head) on the exact path, 1 when the certificate holds, 2 when it fails (NaN or infinity fail).
+static_assert(kSegTargetWorkgroups < 64 * SegCfg<true>::NW, "one boundary per thread: P <= kSegTargetWorkgroups");
+__device__ __forceinline__ int certificate_status(const ScanParams& p, size_t hb, float* scratch) {
+  // every load first (one memory round trip): whether the (row, head) is truncated, and thread t's
+  // boundary t + 1 (P <= 256 < threads)
+  const int t = threadIdx.x, jb = t + 1;
+  const int truncated = p.plan[hb + 1].trunc;
+  float l2 = 0.f, n1 = 0.f, n2 = 0.f;
+  if (jb < p.P) {
     const float* ct = p.cert + (hb + jb) * kCertFloats;
-    float n1 = 0.f, n2 = 0.f;
+    l2 = p.plan[hb + jb].l2;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       n1 += ct[i];
       n2 += ct[8 + i];
     }
-    scratch[3 * jb] = __builtin_amdgcn_exp2f(p.plan[hb + jb].l2);
+    scratch[3 * jb] = __builtin_amdgcn_exp2f(l2);
     scratch[3 * jb + 1] = sqrtf(n1);
     scratch[3 * jb + 2] = sqrtf(n2);
   }
   __syncthreads();
+  if (!truncated) return 0;
   int ok = 1;
   if (t == 0) {
     float eps = 0.f;
-    for (int jb = 1; jb < p.P && ok; ++jb) {
-      eps = scratch[3 * jb] * (scratch[3 * jb + 1] + eps);
-      ok = eps <= kCertRel * scratch[3 * jb + 2];
+    for (int j = 1; j < p.P && ok; ++j) {
+      eps = scratch[3 * j] * (scratch[3 * j + 1] + eps);
+      ok = eps <= kCertRel * scratch[3 * j + 2];
     }
     scratch[0] = ok ? 1.f : 0.f;
   }
   __syncthreads();
-  return scratch[0] != 0.f;
+  return scratch[0] != 0.f ? 1 : 2;
 }
 
 
@@ -857,37 +863,52 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
   seg_body<true>(p, lds, b, h, run);
 }
 
-// Truncation plan of boundary jb (1 <= jb < P) of (row b, head h), from the chunk records: the shortest
-// window of W <= min(Ls, kTruncMaxW) chunks ending at c = jb Ls whose chunks all hold valid tokens, all
-// have beta' in [0, 2] and whose decay sums to l2 = sum g' log2 e <= -kTruncLog2. W = 0 when there is
-// none (or the row's length or s0 row is out of range).
-__device__ __forceinline__ void boundary_plan(const ScanParams& p, int b, int h, int jb, int& W, float& l2) {
-  W = 0;
-  l2 = 0.f;
-  const int cb = jb * p.Ls;
-  const int wmax = min(min(p.Ls, kTruncMaxW), cb);
-  // every candidate chunk's flag and decay first (chunks cb - wmax .. cb - 1 < NC), all loads at once
-  const unsigned char* recs = reinterpret_cast<const unsigned char*>(p.ws) + head_index(p, b, h) * p.NC * kRecB;
-  float flag[kTruncMaxW], dec[kTruncMaxW];
+// Truncation plan of a (row, head), from the chunk records. Its loads are issued first, all of them
+// together (one memory round trip), and decided on after: PlanLoads holds what thread t of the
+// workgroup reads, decide_window / chunks_contract decide from it.
+struct PlanLoads {
+  int len, srow;                                // the row's length and s0 row, as stored
+  float flag[kTruncMaxW], dec[kTruncMaxW];      // boundary t + 1's window candidates cb - 1, cb - 2, ...
+  float cflag;                                  // contraction flag of chunk t (1 past the last boundary)
+};
+__device__ __forceinline__ const float* rec_scalars(const ScanParams& p, int b, int h, int c) {
+  return reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(p.ws) +
+                                        (head_index(p, b, h) * p.NC + c) * kRecB + kScOff);
+}
+__device__ __forceinline__ PlanLoads plan_loads(const ScanParams& p, int b, int h, int t) {
+  PlanLoads pl;
+  pl.len = p.lengths ? p.lengths[b] : p.L;
+  pl.srow = p.s0 ? (p.s0_row ? p.s0_row[b] : b) : 0;
+  // Straight-line loads of in-range records (chunk indices clamped into [0, NC)); candidates past
+  // min(Ls, kTruncMaxW) or before chunk 0, and chunks past the last boundary, are ignored later.
+  const int cb = min(t + 1, p.P - 1) * p.Ls;   // <= (P - 1) Ls < NC
 #pragma unroll
   for (int w = 1; w <= kTruncMaxW; ++w) {
-    flag[w - 1] = 0.f;
-    dec[w - 1] = 0.f;
-    if (w <= wmax) {
-      const float* sc = reinterpret_cast<const float*>(recs + (size_t)(cb - w) * kRecB + kScOff);
-      flag[w - 1] = sc[kScBetaOk * C];
-      dec[w - 1] = sc[kScGam2 * C + C - 1];   // the chunk's whole decay, in log2
-    }
+    const float* sc = rec_scalars(p, b, h, max(cb - w, 0));
+    pl.flag[w - 1] = sc[kScBetaOk * C];
+    pl.dec[w - 1] = sc[kScGam2 * C + C - 1];   // the chunk's whole decay, in log2
   }
-  int srow = 0;
-  if (row_is_bad(p, b, srow)) return;
-  const int len = p.lengths ? p.lengths[b] : p.L;
-  if (cb > (len + C - 1) / C) return;   // the window would reach into the row's pads
+  pl.cflag = rec_scalars(p, b, h, min(t, p.NC - 1))[kScBetaOk * C];
+  return pl;
+}
+
+// Boundary jb = t + 1 (1 <= jb < P): the shortest window of W <= min(Ls, kTruncMaxW) chunks ending at
+// c = jb Ls whose chunks all hold valid tokens, all carry the contraction flag (every beta' in [0, 2],
+// decay sum <= 0) and whose decay sums to l2 = sum g' log2 e <= -kTruncLog2. W = 0 when there is none
+// (or the row's length or s0 row is out of range).
+__device__ __forceinline__ void decide_window(const ScanParams& p, const PlanLoads& pl, int jb, int& W, float& l2) {
+  W = 0;
+  l2 = 0.f;
+  if (jb >= p.P) return;
+  if ((pl.len < 0 || pl.len > p.L) || (p.s0 && (pl.srow < 0 || pl.srow >= p.n_s0))) return;   // a bad row
+  const int cb = jb * p.Ls;
+  if (cb > (pl.len + C - 1) / C) return;   // the window would reach into the row's pads
+  const int wmax = min(min(p.Ls, kTruncMaxW), cb);
   float acc = 0.f;
 #pragma unroll
   for (int w = 1; w <= kTruncMaxW; ++w) {
-    if (w > wmax || !(flag[w - 1] == 1.f)) return;
-    acc += dec[w - 1];
+    if (w > wmax || !(pl.flag[w - 1] == 1.f)) return;
+    acc += pl.dec[w - 1];
     if (acc <= -kTruncLog2) {
       W = w;
       l2 = acc;
@@ -896,19 +917,16 @@ __device__ __forceinline__ void boundary_plan(const ScanParams& p, int b, int h,
   }
 }
 
-// Every chunk of row b, head h from start to the last boundary that holds valid tokens contracts (its
+// Every chunk of the (row, head) from start to the last boundary that holds valid tokens contracts (its
 // flag: every beta' in [0, 2] and a decay sum <= 0, so that its state map has spectral norm <= 1), checked
-// by the workgroup's threads together (thread t: chunks t, t + stride, ...). Then an error in the state
-// at one boundary does not grow on its way to the next window.
-__device__ __forceinline__ bool chunks_contract(const ScanParams& p, int b, int h, int t, int stride) {
-  const unsigned char* recs = reinterpret_cast<const unsigned char*>(p.ws) + head_index(p, b, h) * p.NC * kRecB;
-  const int c_last = (p.P - 1) * p.Ls;   // < NC
-  const int len = p.lengths ? min(max(p.lengths[b], 0), p.L) : p.L;   // loaded beside the flags
-  bool ok = true;
-  for (int c = t; c < c_last; c += stride) {
-    const float f = reinterpret_cast<const float*>(recs + (size_t)c * kRecB + kScOff)[kScBetaOk * C];
-    ok = ok && (f == 1.f || c >= (len + C - 1) / C);
-  }
+// by the workgroup's threads together (thread t: chunk t from the loads, then t + stride, ... for very
+// long rows). Then an error in the state at one boundary does not grow on its way to the next window.
+__device__ __forceinline__ bool chunks_contract(const ScanParams& p, const PlanLoads& pl, int b, int h, int t,
+                                                int stride) {
+  const int c_valid = (min(max(pl.len, 0), p.L) + C - 1) / C;
+  bool ok = pl.cflag == 1.f || t >= c_valid || t >= (p.P - 1) * p.Ls;
+  for (int c = t + stride; c < (p.P - 1) * p.Ls; c += stride)
+    ok = ok && (rec_scalars(p, b, h, c)[kScBetaOk * C] == 1.f || c >= c_valid);
   return ok;
 }
 
@@ -927,10 +945,14 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0;   // read by the caller only
   const int t = threadIdx.x, jb_t = t + 1;
-  const bool contract = !p.trunc || chunks_contract(p, b, h, t, blockDim.x);
   int W = 0;
   float l2 = 0.f;
-  if (p.trunc && jb_t < p.P) boundary_plan(p, b, h, jb_t, W, l2);
+  bool contract = true;
+  if (p.trunc) {
+    const PlanLoads pl = plan_loads(p, b, h, t);
+    decide_window(p, pl, jb_t, W, l2);
+    contract = chunks_contract(p, pl, b, h, t, blockDim.x);
+  }
   // every boundary has a window: an AND over the workgroup in the first word of the (not yet used)
   // staging area; the second word passes on the window of boundary j + 1
   int* all_ok = reinterpret_cast<int*>(lds);
@@ -983,8 +1005,9 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanP
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
   const int h = blockIdx.x % p.Hv, b = blockIdx.x / p.Hv;
   const size_t hb = head_index(p, b, h) * p.P;
-  if (!p.trunc || !p.plan[hb + 1].trunc) return;   // exact path: nothing to check
-  if (certificate_holds(p, hb, reinterpret_cast<float*>(lds))) return;
+  if (!p.trunc) return;
+  // 0: the exact path (nothing to check), 1: the certificate holds
+  if (certificate_status(p, hb, reinterpret_cast<float*>(lds)) != 2) return;
   if (threadIdx.x == 0) atomicAdd(p.status, 1);
   __syncthreads();   // the scratch is read before the staging area is written
   SegRun all{};
