@@ -27,11 +27,13 @@ constexpr int kFragBlocks = 6;
 constexpr int kBlockElems = 64 * 8;
 constexpr int kScalarBytes = 8 * kChunk * 4;
 constexpr int kScA = 0, kScC = 1, kScD = 2, kScEgC = 3, kScGam2 = 4, kScRk = 5, kScRq = 6;   // rows of 64
-// bf16 records use neither c nor rq; their row 6 holds at [6][0] the flag kBetaOk (1 when every
-// beta' of the chunk lies in [0, 2], where each token's map S -> e^{g'} (I - beta' k_hat k_hat^T) S
-// has spectral norm at most e^{g'}, and the chunk's decay sum is <= 0, so that the chunk's map has
-// spectral norm at most 1; 0 otherwise).
-constexpr int kScBetaOk = 6;
+// bf16 records order their scalar rows differently: rows 0..3, the first 1 KiB (the only scalar
+// block the segment kernels stage), hold a, d, gamma log2 e and rk (e^{gamma_63} is formed from
+// gamma_63 where it is used); row 4 holds at [4][0] the contraction flag (1 when every beta' of the
+// chunk lies in [0, 2], where each token's map S -> e^{g'} (I - beta' k_hat k_hat^T) S has spectral
+// norm at most e^{g'}, and the chunk's decay sum is <= 0, so that the chunk's map has spectral norm
+// at most 1; 0 otherwise); rows 5..7 are not used.
+constexpr int kBfA = 0, kBfD = 1, kBfGam2 = 2, kBfRk = 3, kBfFlag = 4;
 
 inline size_t record_bytes(size_t elem) {
   return (elem == 2 ? 1 : 2) * size_t(kFragBlocks) * kBlockElems * elem + kScalarBytes;

@@ -692,16 +692,15 @@ __global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p
         auto scalars = [&](int i) {
           const float g2 = sm.gam[j + i][lane], g2C = sm.gam[j + i][C - 1], rkl = sm.rk[lane];
           float* sc = reinterpret_cast<float*>(rec(i) + kFragBlocks * kBlockElems * 2);
-          sc[kScA * C + lane] = __builtin_amdgcn_exp2f(g2) * rkl;
-          sc[kScD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
-          sc[kScEgC * C + lane] = (lane == 0) ? __builtin_amdgcn_exp2f(g2C) : 0.f;
-          sc[kScGam2 * C + lane] = g2;
-          sc[kScRk * C + lane] = rkl;
+          sc[kBfA * C + lane] = __builtin_amdgcn_exp2f(g2) * rkl;
+          sc[kBfD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
+          sc[kBfGam2 * C + lane] = g2;
+          sc[kBfRk * C + lane] = rkl;
           // every beta' of the chunk in [0, 2] (each token's map then has spectral norm <= e^{g'}) and
           // the chunk's decay sum <= 0: the chunk's map has spectral norm <= e^{sum g'} <= 1
           const float bt = sm.bet[j + i][lane];
           const bool ok = __all(bt >= 0.f && bt <= 2.f) && g2C <= 0.f;
-          sc[kScBetaOk * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
+          sc[kBfFlag * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
         };
         inverse_to_records<__bf16>(sm.m[0], sm.m[1], sm.gam[j], sm.gam[j + nh - 1], sm.rk, sm.bet[j],
                                    sm.bet[j + nh - 1], gk, nh, wave, n16, G, lane, rec(0), rec(nh - 1), scalars);

@@ -32,7 +32,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // ====================================================================== bf16 segment scan
 constexpr int kScOff = kFragBlocks * kBlockElems * 2;                  // scalars within a bf16 record
 constexpr int kRecB = kScOff + kScalarBytes;                           // bf16 record bytes (8192)
-constexpr int kRecBlocks = kRecB / 1024;                               // 1 KiB loads per record
+constexpr int kRecBlocks = kFragBlocks + 1;   // 1 KiB loads per chunk: Tb and the first scalar block
 constexpr int kBufK = C * D * 2;                                       // one 64x128 bf16 tile
 
 // LDS staging of one chunk (every wave reads every part of it): K, V (and Q) tiles of 64 rows x
@@ -356,7 +356,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = mfma(tf, Rop[sl][kb2], Dl[sl][mt]);
         }
-        const f4 d4 = *reinterpret_cast<const f4*>(sc + 2 * C + 16 * mt + 4 * G);
+        const f4 d4 = *reinterpret_cast<const f4*>(sc + kBfD * C + 16 * mt + 4 * G);
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] *= d4;   // diag(d) Delta
       }
@@ -367,7 +367,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
         Ddop[sl][1] = pack8(Dl[sl][2], Dl[sl][3]);
       }
       // S <- e^{gamma_63} S + K^T diag(d) Delta
-      const float egc = sc[3 * C];
+      const float egc = __builtin_amdgcn_exp2f(sc[kBfGam2 * C + C - 1]);   // e^{gamma_63}
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -550,12 +550,12 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
         }
         if (kb2 == 0) put_qnorms(mt, qq);
         const int t = 16 * mt + n16;
-        const float gt = sc[kScGam2 * C + t];
+        const float gt = sc[kBfGam2 * C + t];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int i0 = 32 * kb2 + 16 * s2 + 4 * G;
-          const f4 gi = *reinterpret_cast<const f4*>(sc + kScGam2 * C + i0);
-          const f4 ri = *reinterpret_cast<const f4*>(sc + kScRk * C + i0);
+          const f4 gi = *reinterpret_cast<const f4*>(sc + kBfGam2 * C + i0);
+          const f4 ri = *reinterpret_cast<const f4*>(sc + kBfRk * C + i0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = ri[e] * __builtin_amdgcn_exp2f(fminf(gt - gi[e], 0.f)) * pt[s2][e];
@@ -624,7 +624,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     {
       f4 d4[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) d4[mt] = *reinterpret_cast<const f4*>(sc + 2 * C + 16 * mt + 4 * G);
+      for (int mt = 0; mt < 4; ++mt) d4[mt] = *reinterpret_cast<const f4*>(sc + kBfD * C + 16 * mt + 4 * G);
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl) {
         Ddop[sl][0] = pack8(Dl[sl][0] * d4[0], Dl[sl][1] * d4[1]);
@@ -653,7 +653,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
           for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
         }
-        const float eg = __builtin_amdgcn_exp2f(sc[kScGam2 * C + 16 * mt + n16]);   // e^gamma_t
+        const float eg = __builtin_amdgcn_exp2f(sc[kBfGam2 * C + 16 * mt + n16]);   // e^gamma_t
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= eg;
 #pragma unroll
@@ -667,7 +667,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       }
     }
     // S <- e^{gamma_63} S + K^T diag(d) Delta
-    const float egc = sc[3 * C];
+    const float egc = __builtin_amdgcn_exp2f(sc[kBfGam2 * C + C - 1]);   // e^{gamma_63}
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -885,10 +885,10 @@ __device__ __forceinline__ PlanLoads plan_loads(const ScanParams& p, int b, int 
 #pragma unroll
   for (int w = 1; w <= kTruncMaxW; ++w) {
     const float* sc = rec_scalars(p, b, h, max(cb - w, 0));
-    pl.flag[w - 1] = sc[kScBetaOk * C];
-    pl.dec[w - 1] = sc[kScGam2 * C + C - 1];   // the chunk's whole decay, in log2
+    pl.flag[w - 1] = sc[kBfFlag * C];
+    pl.dec[w - 1] = sc[kBfGam2 * C + C - 1];   // the chunk's whole decay, in log2
   }
-  pl.cflag = rec_scalars(p, b, h, min(t, p.NC - 1))[kScBetaOk * C];
+  pl.cflag = rec_scalars(p, b, h, min(t, p.NC - 1))[kBfFlag * C];
   return pl;
 }
 
@@ -926,7 +926,7 @@ __device__ __forceinline__ bool chunks_contract(const ScanParams& p, const PlanL
   const int c_valid = (min(max(pl.len, 0), p.L) + C - 1) / C;
   bool ok = pl.cflag == 1.f || t >= c_valid || t >= (p.P - 1) * p.Ls;
   for (int c = t + stride; c < (p.P - 1) * p.Ls; c += stride)
-    ok = ok && (rec_scalars(p, b, h, c)[kScBetaOk * C] == 1.f || c >= c_valid);
+    ok = ok && (rec_scalars(p, b, h, c)[kBfFlag * C] == 1.f || c >= c_valid);
   return ok;
 }
 
