@@ -710,6 +710,216 @@ __global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA into LDS may be in flight at the end
 }
 
+// ---- bf16 prep, one wave per value head (gdr_prep_wave)
+// One workgroup of kPrepWaves waves per work item (row b, key head kh, chunk c). The waves copy the
+// item's K tile HBM -> LDS by DMA (half of the rows each) and meet once; then each wave forms all ten
+// lower tiles of the Gram K K^T (bf16 MFMA; rk from their diagonal) and runs, for the value heads
+// kh r + j with j = wave, wave + kPrepWaves, ... on its own, the steps of the keyhead kernel above in
+// sequence: gates and gamma, A, the blocked inverse in its own LDS matrix, and the record. A wave's
+// LDS accesses complete in order, so no other barrier is needed; the latency of one wave's steps is
+// hidden by the other workgroups on the compute unit (four fit) rather than split over four waves
+// with a barrier between every two steps.
+constexpr int kPrepWaves = 2;
+struct PrepWaveSmem {
+  unsigned char k[C * 256];             // K tile, rows swizzled (swz)
+  float m[kPrepWaves][kMatFloats];      // per wave: A, then T over it
+  float rk[kPrepWaves][C], gam[kPrepWaves][C], bet[kPrepWaves][C];
+};
+
+// The ten lower Gram tiles in order t = I (I + 1) / 2 + J (I >= J): tile_i(t), tile_j(t).
+__device__ __forceinline__ constexpr int tile_i(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
+__device__ __forceinline__ constexpr int tile_j(int t) { return t - tile_i(t) * (tile_i(t) + 1) / 2; }
+
+// Orders this wave's LDS accesses around the statement for the compiler (the hardware keeps a wave's
+// LDS accesses in order).
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
+
+template <typename TB, bool kList>
+__global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
+  __shared__ __attribute__((aligned(16))) PrepWaveSmem sm;
+  constexpr int kRecBytes = kFragBlocks * kBlockElems * 2 + kScalarBytes;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, G = lane >> 4;
+  const int r = p.Hv / p.Hk;
+  // work item it: key head fastest (with lengths: kh + Hk u over the chunk list, else kh + Hk (b + B c))
+  const int it = blockIdx.x;
+  const int kh = it % p.Hk;
+  int b, c;
+  if constexpr (kList) {
+    if (it >= p.chunk_list[0] * p.Hk) return;   // uniform: past the chunks that hold valid tokens
+    const int e = p.chunk_list[1 + it / p.Hk];
+    b = e / p.NC;
+    c = e - b * p.NC;
+  } else {
+    b = (it / p.Hk) % p.B;
+    c = it / (p.Hk * p.B);
+  }
+
+  // ---- K tile: rows 32 wave .. 32 wave + 31, eight DMA loads of four rows (rows past L read zeros)
+  {
+    const uint32_t row_bytes = (uint32_t)p.Hk * D * 2;
+    const i32x4 rsk = rsrc_words(reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.L * p.Hk * D, (uint32_t)p.L * row_bytes);
+    constexpr int kRowsPerWave = C / kPrepWaves;
+#pragma unroll
+    for (int m = 0; m < kRowsPerWave / 4; ++m) {
+      const int row = kRowsPerWave * wave + 4 * m + (lane >> 4), pos = lane & 15;
+      dma16(rsk, (uint32_t)(c * C + row) * row_bytes + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(row)),
+            sm.k + (kRowsPerWave * wave + 4 * m) * 256);
+    }
+  }
+  // the first head's gates, in flight with the tile
+  GateRaw graw{};
+  if (wave < r) graw = gates_issue<TB>(p, b, kh, c, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as a builtin so that the compiler knows its own loads are done
+  lds_barrier();
+  if (wave >= r) return;   // uniform per wave; no barrier follows
+
+  // ---- Gram: gk[t][e] = (K K^T)[16 I + 4G + e][16 J + n16] for the ten lower tiles; rk from the diagonal
+  f4 gk[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t) gk[t] = f4_splat(0.f);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    bf16x8 rows[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) rows[I] = lds16(sm.k + swz(16 * I + n16, 4 * kb + G));
+#pragma unroll
+    for (int t = 0; t < 10; ++t) gk[t] = mfma(rows[tile_i(t)], rows[tile_j(t)], gk[t]);
+  }
+  float* rk = sm.rk[wave];
+  float* gam = sm.gam[wave];
+  float* bet = sm.bet[wave];
+  float* M = sm.m[wave];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {   // diagonal element (16 I + n16, 16 I + n16): lane group n16 / 4, slot n16 & 3
+    const f4 dg = gk[I * (I + 1) / 2 + I];
+    const int e = n16 & 3;
+    const float ss = e == 0 ? dg[0] : e == 1 ? dg[1] : e == 2 ? dg[2] : dg[3];
+    if ((n16 >> 2) == G) rk[16 * I + n16] = 1.0f / sqrtf(ss + 1e-6f);   // model.py, _l2norm
+  }
+
+  for (int j = wave; j < r; j += kPrepWaves) {
+    // ---- gates of value head kh r + j and gamma (the next head's gates are loaded here too)
+    float gv, bv;
+    gates_finish<TB>(p, j == wave ? graw : gates_issue<TB>(p, b, kh, c, j, lane), gv, bv);
+    store_gates(gam, bet, gv, bv, lane);
+    wave_lds_fence();
+
+    // ---- A (strictly lower, fp32) from the Gram tiles
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      const int I = tile_i(t), J = tile_j(t);
+      const f4 gr = *reinterpret_cast<const f4*>(gam + 16 * I + 4 * G);
+      const f4 rr = *reinterpret_cast<const f4*>(rk + 16 * I + 4 * G);
+      const f4 br = *reinterpret_cast<const f4*>(bet + 16 * I + 4 * G);
+      const int col = 16 * J + n16;
+      const float gc = gam[col], rc = rk[col];
+      float* ab = blk(M, I, J);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * I + 4 * G + e;
+        const float x = br[e] * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * rr[e] * rc * gk[t][e];
+        ab[moff(4 * G + e, n16)] = row > col ? x : 0.f;
+      }
+    }
+    wave_lds_fence();
+
+    // ---- diagonal blocks: lane 16 G + n16 solves column n16 of block G by forward substitution
+    {
+      float* ablk = blk(M, G, G);
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (i == n16) ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < 15; ++k) {
+#pragma unroll
+        for (int i = k + 1; i < 16; ++i) x[i] -= ablk[moff(i, k)] * x[k];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ablk[moff(i, n16)] = x[i];
+    }
+    wave_lds_fence();
+
+    // ---- off-diagonal blocks. A_20, A_21, A_30, A_31 are read before they are overwritten.
+    const f4 a21 = tile_row(blk(M, 2, 1), n16, G), a31 = tile_row(blk(M, 3, 1), n16, G);
+    f4 pre0 = f4_splat(0.f), pre1 = f4_splat(0.f);
+    {
+      const f4 t00 = tile_acc(blk(M, 0, 0), n16, G);
+      mma_lds_acc(pre0, blk(M, 2, 0), n16, G, t00);   // A_20 T_00
+      mma_lds_acc(pre1, blk(M, 3, 0), n16, G, t00);   // A_30 T_00
+    }
+    // within each 32-row half: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int I = 2 * hf + 1, J = 2 * hf;
+      f4 x = f4_splat(0.f), y = f4_splat(0.f);
+      mma_lds_acc(x, blk(M, I, J), n16, G, tile_acc(blk(M, J, J), n16, G));
+      mma_lds_acc(y, blk(M, I, I), n16, G, x);
+      store_acc(blk(M, I, J), n16, G, -y);
+    }
+    wave_lds_fence();
+    // across the halves: Z_IJ = A_I0 T_0J + A_I1 T_1J (T_01 = 0), T_2J = -T_22 Z_2J,
+    // T_3J = -(T_32 Z_2J + T_33 Z_3J), J = 0, 1
+    {
+      const f4 t10 = tile_acc(blk(M, 1, 0), n16, G), t11 = tile_acc(blk(M, 1, 1), n16, G);
+      f4 z20 = pre0, z30 = pre1, z21 = f4_splat(0.f), z31 = f4_splat(0.f);
+      mma_acc(z20, a21, t10);
+      mma_acc(z30, a31, t10);
+      mma_acc(z21, a21, t11);
+      mma_acc(z31, a31, t11);
+      f4 o20 = f4_splat(0.f), o21 = f4_splat(0.f), o30 = f4_splat(0.f), o31 = f4_splat(0.f);
+      mma_lds_acc(o20, blk(M, 2, 2), n16, G, z20);
+      mma_lds_acc(o21, blk(M, 2, 2), n16, G, z21);
+      mma_lds_acc(o30, blk(M, 3, 2), n16, G, z20);
+      mma_lds_acc(o30, blk(M, 3, 3), n16, G, z30);
+      mma_lds_acc(o31, blk(M, 3, 2), n16, G, z21);
+      mma_lds_acc(o31, blk(M, 3, 3), n16, G, z31);
+      store_acc(blk(M, 2, 0), n16, G, -o20);
+      store_acc(blk(M, 2, 1), n16, G, -o21);
+      store_acc(blk(M, 3, 0), n16, G, -o30);
+      store_acc(blk(M, 3, 1), n16, G, -o31);
+    }
+    wave_lds_fence();
+
+    // ---- the record: Tb = T diag(beta') as the six operand blocks (zero above the diagonal), then
+    //      the scalar rows a, d, gamma log2 e, rk and the contraction flag
+    unsigned char* rec = reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + kh * r + j) * p.NC + c) * kRecBytes;
+#pragma unroll
+    for (int bk = 0; bk < kFragBlocks; ++bk) {
+      const int I = block_tile(bk), kb = block_kb(bk);
+      const int row = 16 * I + n16, c0 = 32 * kb + 4 * G;
+      // columns c0.. lie in block (I, 2 kb), columns c0 + 16.. in block (I, 2 kb + 1), which is above
+      // the diagonal (not stored, all zero in T) when 2 kb + 1 > I
+      const f4 t_lo = tile_row(blk(M, I, 2 * kb), n16, G);
+      const f4 t_hi = 2 * kb + 1 <= I ? tile_row(blk(M, I, 2 * kb + 1), n16, G) : f4_splat(0.f);
+      const f4 b_lo = *reinterpret_cast<const f4*>(&bet[c0]);
+      const f4 b_hi = *reinterpret_cast<const f4*>(&bet[c0 + 16]);
+      f4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = (c0 + e <= row) ? t_lo[e] * b_lo[e] : 0.f;
+        hi[e] = (c0 + 16 + e <= row) ? t_hi[e] * b_hi[e] : 0.f;
+      }
+      *reinterpret_cast<bf16x8*>(rec + (size_t)bk * kBlockElems * 2 + (size_t)lane * 16) = pack8(lo, hi);
+    }
+    {
+      const float g2 = gam[lane], g2C = gam[C - 1], rkl = rk[lane];
+      float* sc = reinterpret_cast<float*>(rec + kFragBlocks * kBlockElems * 2);
+      sc[kBfA * C + lane] = __builtin_amdgcn_exp2f(g2) * rkl;
+      sc[kBfD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
+      sc[kBfGam2 * C + lane] = g2;
+      sc[kBfRk * C + lane] = rkl;
+      // every beta' of the chunk in [0, 2] (each token's map then has spectral norm <= e^{g'}) and
+      // the chunk's decay sum <= 0: the chunk's map has spectral norm <= e^{sum g'} <= 1
+      const float bt = bet[lane];
+      const bool ok = __all(bt >= 0.f && bt <= 2.f) && g2C <= 0.f;
+      sc[kBfFlag * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
+    }
+    wave_lds_fence();   // the next head's gates and A are written after this head's last reads
+  }
+}
+
 // Workgroups of the persistent prep: kPrepPerCU per compute unit of the current device (what fits).
 static int prep_workgroups() {
   static int cache[64];
@@ -729,16 +939,18 @@ hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStre
     // (checked by the caller)
     const int64_t items = int64_t(p.B) * p.Hk * p.NC;
     const dim3 grid((unsigned)std::min<int64_t>(items, prep_workgroups()));
+    (void)grid;
+    const dim3 wgrid((unsigned)items), wblock(64 * kPrepWaves);
     if (p.chunk_list) {
       hipLaunchKernelGGL(gdr_chunk_list, dim3(1), dim3(256), 0, s, p.lengths, p.B, p.L, p.NC, p.chunk_list);
       if (beta_bf16)
-        hipLaunchKernelGGL((gdr_prep_keyhead<__bf16, true>), grid, dim3(256), 0, s, p, (int)items);
+        hipLaunchKernelGGL((gdr_prep_wave<__bf16, true>), wgrid, wblock, 0, s, p);
       else
-        hipLaunchKernelGGL((gdr_prep_keyhead<float, true>), grid, dim3(256), 0, s, p, (int)items);
+        hipLaunchKernelGGL((gdr_prep_wave<float, true>), wgrid, wblock, 0, s, p);
     } else if (beta_bf16) {
-      hipLaunchKernelGGL((gdr_prep_keyhead<__bf16, false>), grid, dim3(256), 0, s, p, (int)items);
+      hipLaunchKernelGGL((gdr_prep_wave<__bf16, false>), wgrid, wblock, 0, s, p);
     } else {
-      hipLaunchKernelGGL((gdr_prep_keyhead<float, false>), grid, dim3(256), 0, s, p, (int)items);
+      hipLaunchKernelGGL((gdr_prep_wave<float, false>), wgrid, wblock, 0, s, p);
     }
   } else {
     const dim3 grid(p.B * p.Hv * p.NC);
