@@ -10,22 +10,20 @@
 //   A[t][i] = beta'_t e^{gamma_t - gamma_i} rk_t rk_i (k_t . k_i)   (i < t)
 //   T = (I + A)^-1, Tb = T diag(beta'),  P[t][i] = rq_t rk_i e^{gamma_t - gamma_i} (q_t . k_i)  (i <= t)
 // and writes the chunk record: Tb (and for float32 P) as MFMA operand blocks (lower triangle
-// only), then the per-token scalars a = e^gamma rk, d = rk e^{gamma_63 - gamma}, e^{gamma_63},
-// gamma log2 e and rk (float32 also c = e^gamma rq and rq).
+// only), then the per-token scalars a = e^gamma rk, d = rk e^{gamma_63 - gamma}, gamma log2 e and
+// rk (float32 also c = e^gamma rq, rq and e^{gamma_63}; bf16 also the chunk's contraction flag).
 // Exponents are only taken of non-positive differences on the kept triangle ("direct" decay
 // from in-chunk differences), so nothing over- or underflows however strong the decay.
 //
-// bf16 (gdr_prep_keyhead): persistent workgroups, each walking work items (row b, key head kh,
-// chunk c) with the next item's K rows (HBM->LDS by DMA) and gates (into registers) in flight
-// while the current item computes. The Gram K K^T is formed once per item and shared by the
-// Hv / Hk value heads of the key head, each of which then gets its own A, inverse and record. q is
-// not read: the output pass forms the q norms from the Q tile it stages anyway. With lengths the
-// items are only the chunks that hold valid tokens (gdr_chunk_list).
+// bf16 (gdr_prep_wave): one workgroup of two waves per work item (row b, key head kh, chunk c),
+// each wave running the whole transform of one value head of the key head at a time on its own
+// (see there). q is not read: the output pass forms the q norms from the Q tile it stages anyway.
+// With lengths the items are only the chunks that hold valid tokens (gdr_chunk_list).
 //
 // float32 (gdr_prep): one workgroup (4 waves) per (row b, value head h, chunk c).
 //
-// Phases (one barrier each; the waves exchange data through LDS only, so the barriers do not
-// wait for the global stores of the record):
+// float32 phases (one barrier each; the waves exchange data through LDS only, so the barriers do
+// not wait for the global stores of the record; gdr_prep_wave runs the same steps in one wave):
 //   1. stage k (and q) rows in LDS, row norms, gates and gamma;
 //   2. Gram tiles on MFMA, balanced over the waves: wave w forms its diagonal K K^T tile (3 - w,
 //      3 - w) and 2, 2, 1, 1 of the tiles below the diagonal (GramTiles), and (float32) the K Q^T
@@ -37,7 +35,6 @@
 //   5. off-diagonal blocks by the 2x2 block rule T_BA = -T_BB A_BA T_AA, first within each
 //      32-row half (T_10, T_32), then across the halves, on fp32 MFMA, each written over A;
 //   6. Tb = T diag(beta') gathered into operand order.
-// The bf16 prep runs phases 3-6 for two value heads of a key head at once.
 #include <algorithm>
 
 #include "gdr_device.h"
@@ -452,14 +449,6 @@ __global__ __launch_bounds__(256, 2) void gdr_prep(PrepParams p) {
 // ====================================================================== bf16: per key head, persistent
 // LDS of the key-head prep: the K tile (swizzled 256-byte rows, written by DMA), and A, then T in
 // place, of two value heads.
-constexpr int kPrepPerCU = 3;   // resident workgroups per compute unit (measured: 4 is slower)
-struct PrepKhSmem {
-  unsigned char k[C * 256];
-  float m[2][kMatFloats];   // A, then T over it, of two value heads
-  float rk[C];
-  float gam[4][C], bet[4][C];   // gates of up to four value heads (one batch of the key head's)
-};
-
 // Gates of value head hr of an item's key head at this lane's token, in two steps so that the loads
 // of the next item stay in flight while the current one computes: gates_issue loads the raw words
 // (range-checked: tokens past L read zeros, and nothing waits on them), gates_finish applies the
@@ -530,24 +519,6 @@ __device__ __forceinline__ void store_gates(float* gam, float* bet, float gv, fl
   bet[lane] = bv;
 }
 
-// Gram tiles GramTiles<W> from the swizzled K tile: gk[t][e] = (K K^T)[16 I_t + 4G + e][16 J_t + n16].
-// Both operands are 16-byte row reads (key 32 kb + 8G + e in slot e of lane group G).
-template <int W>
-__device__ __forceinline__ void gram_kk(const unsigned char* kt, int n16, int G, f4 (&gk)[3]) {
-  using TL = GramTiles<W>;
-#pragma unroll
-  for (int t = 0; t < 3; ++t) gk[t] = f4_splat(0.f);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-    for (int t = 0; t < TL::n; ++t)
-      gk[t] = mfma(lds16(kt + swz(16 * TL::I[t] + n16, 4 * kb + G)), lds16(kt + swz(16 * TL::J[t] + n16, 4 * kb + G)), gk[t]);
-  }
-}
-
-// Work item it = ((b NC) + c) Hk + kh: items of one chunk and neighbouring key heads read
-// neighbouring 256-byte pieces of the same k rows. The next item's K tile is copied HBM -> LDS
-// (the waves' DMA, issued once the current Gram is formed) while the current item's inverses run.
 // The chunks of a right-padded batch that hold valid tokens, row-major: list[0] = their count U,
 // list[1 + u] = b NC + c. Rows whose length is out of range count all their chunks (they are
 // computed in full; the output pass turns them into NaN). One workgroup: rows in blocks of 256,
@@ -577,137 +548,6 @@ __global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, in
     __syncthreads();
   }
   if (tid == 0) list[0] = base;
-}
-
-template <typename TB, bool kList>
-__global__ __launch_bounds__(256, kPrepPerCU) void gdr_prep_keyhead(PrepParams p, int items) {
-  __shared__ __attribute__((aligned(16))) PrepKhSmem sm;
-  constexpr int kRecBytes = kFragBlocks * kBlockElems * 2 + kScalarBytes;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n16 = lane & 15, G = lane >> 4;
-  const int r = p.Hv / p.Hk;
-  const uint32_t row_bytes = (uint32_t)p.Hk * D * 2;
-
-  // Work items. With lengths (kList), the items are the chunks of the chunk list, key head fastest:
-  // it = kh + Hk u, so that every workgroup's items (it, it + grid, ...) are real work in equal
-  // number. Chunks wholly past their row's length are not in the list: they get no record, which
-  // the scan passes neither read nor need (there beta' = g' = 0, so the chunk leaves the state
-  // unchanged). Without lengths, the items are numbered key head fastest, then row, then chunk:
-  // it = kh + Hk (b + B c), so that a workgroup's items pass through every chunk position.
-  struct Item {
-    int b, c, kh;
-  };
-  auto item = [&](int it2) {
-    Item x;
-    x.kh = it2 % p.Hk;
-    if constexpr (kList) {
-      const int e = p.chunk_list[1 + it2 / p.Hk];
-      x.b = e / p.NC;
-      x.c = e - x.b * p.NC;
-    } else {
-      x.b = (it2 / p.Hk) % p.B;
-      x.c = it2 / (p.Hk * p.B);
-    }
-    return x;
-  };
-  if constexpr (kList) items = p.chunk_list[0] * p.Hk;
-
-  // This wave's quarter of item it's K tile: rows 16 wave .. 16 wave + 15, four DMA loads of four rows.
-  auto issue_k = [&](const Item& x) {
-    const int kh = x.kh, b = x.b, c = x.c;
-    const i32x4 rk = rsrc_words(reinterpret_cast<const __bf16*>(p.k) + (size_t)b * p.L * p.Hk * D,
-                                (uint32_t)p.L * row_bytes);   // rows past L read as zeros
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int row = 16 * wave + 4 * m + (lane >> 4), pos = lane & 15;
-      dma16(rk, (uint32_t)(c * C + row) * row_bytes + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(row)),
-            sm.k + (16 * wave + 4 * m) * 256);
-    }
-  };
-
-  // Wave 3 - j handles the gates of value head j of a batch of four: the waves with the fewest Gram
-  // tiles do the gate work.
-  const int jg = 3 - wave;
-  int it = blockIdx.x;
-  GateRaw graw{};   // raw gates of value head jg of item it (first batch of four), in flight
-  Item nxt{};       // item it, then the next one
-  if (it < items) {
-    nxt = item(it);
-    issue_k(nxt);
-    if (jg < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, jg, lane);
-  }
-  for (; it < items; it += gridDim.x) {
-    const int kh = nxt.kh, b = nxt.b, c = nxt.c;
-    // this wave's part of the K tile (and its gates) have landed; every wave is done with the
-    // previous item's A, T and gates
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as a builtin so that the compiler knows its own loads are done
-    lds_barrier();
-
-    // ---- 1-2. gates of the first (up to) four value heads; Gram tiles GramTiles<wave>; rk from
-    //           the Gram diagonal, rk_t = (|k_t|^2 + 1e-6)^-1/2 (model.py, _l2norm)
-    if (jg < r) {
-      float gv, bv;
-      gates_finish<TB>(p, graw, gv, bv);
-      store_gates(sm.gam[jg], sm.bet[jg], gv, bv, lane);
-    }
-    f4 gk[3];
-    switch (wave) {
-      case 0: gram_kk<0>(sm.k, n16, G, gk); break;
-      case 1: gram_kk<1>(sm.k, n16, G, gk); break;
-      case 2: gram_kk<2>(sm.k, n16, G, gk); break;
-      default: gram_kk<3>(sm.k, n16, G, gk); break;
-    }
-    {
-      const int Ik = 3 - wave, e = n16 & 3;   // diagonal element (16 Ik + n16, 16 Ik + n16): lane group n16 / 4
-      const f4 dg = gk[0];                    // the wave's diagonal tile
-      const float ss = e == 0 ? dg[0] : e == 1 ? dg[1] : e == 2 ? dg[2] : dg[3];
-      if ((n16 >> 2) == G) sm.rk[16 * Ik + n16] = 1.0f / sqrtf(ss + 1e-6f);
-    }
-    lds_barrier();   // the K tile is free, gates and rk are in LDS
-
-    // the next item's K tile and gates, while this item's inverses run
-    if (it + (int)gridDim.x < items) {
-      nxt = item(it + gridDim.x);
-      issue_k(nxt);
-      if (jg < r) graw = gates_issue<TB>(p, nxt.b, nxt.kh, nxt.c, jg, lane);
-    }
-
-    // ---- 3-6 for the value heads of the key head, two at a time
-    for (int hb = 0; 4 * hb < r; ++hb) {
-      if (hb > 0) {   // more than four value heads per key head: the next batch's gates, read now
-        float g2 = 0.f, b2 = 0.f;
-        if (4 * hb + jg < r) gates_finish<TB>(p, gates_issue<TB>(p, b, kh, c, 4 * hb + jg, lane), g2, b2);
-        lds_barrier();   // the previous batch's gates and matrices are no longer read
-        if (4 * hb + jg < r) store_gates(sm.gam[jg], sm.bet[jg], g2, b2, lane);
-        lds_barrier();
-      }
-      for (int j = 0; j < 4 && 4 * hb + j < r; j += 2) {
-        if (j > 0) lds_barrier();   // the previous pair's records are read out of M
-        const int nh = 4 * hb + j + 1 < r ? 2 : 1;
-        auto rec = [&](int i) {
-          return reinterpret_cast<unsigned char*>(p.ws) + (((size_t)b * p.Hv + kh * r + 4 * hb + j + i) * p.NC + c) * kRecBytes;
-        };
-        // the scalar rows of head j + i (rows c and rq are not used by bf16 records)
-        auto scalars = [&](int i) {
-          const float g2 = sm.gam[j + i][lane], g2C = sm.gam[j + i][C - 1], rkl = sm.rk[lane];
-          float* sc = reinterpret_cast<float*>(rec(i) + kFragBlocks * kBlockElems * 2);
-          sc[kBfA * C + lane] = __builtin_amdgcn_exp2f(g2) * rkl;
-          sc[kBfD * C + lane] = rkl * __builtin_amdgcn_exp2f(fminf(g2C - g2, 0.f));
-          sc[kBfGam2 * C + lane] = g2;
-          sc[kBfRk * C + lane] = rkl;
-          // every beta' of the chunk in [0, 2] (each token's map then has spectral norm <= e^{g'}) and
-          // the chunk's decay sum <= 0: the chunk's map has spectral norm <= e^{sum g'} <= 1
-          const float bt = sm.bet[j + i][lane];
-          const bool ok = __all(bt >= 0.f && bt <= 2.f) && g2C <= 0.f;
-          sc[kBfFlag * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
-        };
-        inverse_to_records<__bf16>(sm.m[0], sm.m[1], sm.gam[j], sm.gam[j + nh - 1], sm.rk, sm.bet[j],
-                                   sm.bet[j + nh - 1], gk, nh, wave, n16, G, lane, rec(0), rec(nh - 1), scalars);
-      }
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no DMA into LDS may be in flight at the end
 }
 
 // ---- bf16 prep, one wave per value head (gdr_prep_wave)
@@ -920,26 +760,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
   }
 }
 
-// Workgroups of the persistent prep: kPrepPerCU per compute unit of the current device (what fits).
-static int prep_workgroups() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  int* slot = dev < 64 ? &cache[dev] : nullptr;
-  if (slot && *slot > 0) return *slot;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  if (slot) *slot = kPrepPerCU * cus;
-  return kPrepPerCU * cus;
-}
-
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s) {
   if (qkv_bf16) {
     // items: an upper bound with a chunk list (the kernel reads the count); <= B Hv NC < 2^31
     // (checked by the caller)
     const int64_t items = int64_t(p.B) * p.Hk * p.NC;
-    const dim3 grid((unsigned)std::min<int64_t>(items, prep_workgroups()));
-    (void)grid;
     const dim3 wgrid((unsigned)items), wblock(64 * kPrepWaves);
     if (p.chunk_list) {
       hipLaunchKernelGGL(gdr_chunk_list, dim3(1), dim3(256), 0, s, p.lengths, p.B, p.L, p.NC, p.chunk_list);
