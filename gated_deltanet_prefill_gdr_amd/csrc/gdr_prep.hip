@@ -557,13 +557,21 @@ __global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, in
 // kh r + j with j = wave, wave + kPrepWaves, ... on its own, the steps of the keyhead kernel above in
 // sequence: gates and gamma, A, the blocked inverse in its own LDS matrix, and the record. A wave's
 // LDS accesses complete in order, so no other barrier is needed; the latency of one wave's steps is
-// hidden by the other workgroups on the compute unit (four fit) rather than split over four waves
-// with a barrier between every two steps.
+// hidden by the other workgroups on the compute unit rather than split over four waves with a
+// barrier between every two steps. With at most kPrepWaves value heads per key head (kOne), each wave
+// has at most one head: the waves meet once more after the Gram, the matrices are then written over
+// the K tile (22 KiB of LDS per workgroup instead of 38), and the forward substitution is kept from
+// loading all of its block ahead, so that three waves fit on a SIMD (six workgroups per CU) instead
+// of two.
 constexpr int kPrepWaves = 2;
-struct PrepWaveSmem {
-  unsigned char k[C * 256];             // K tile, rows swizzled (swz)
-  float m[kPrepWaves][kMatFloats];      // per wave: A, then T over it
+template <bool kOne> struct PrepWaveSmem {
+  static constexpr int kKBytes = C * 256, kMBytes = kPrepWaves * kMatFloats * 4;
+  // the K tile (rows swizzled, swz) and the waves' matrices (A, then T over it), the latter over the
+  // former with kOne
+  unsigned char buf[kOne ? (kKBytes > kMBytes ? kKBytes : kMBytes) : kKBytes + kMBytes];
   float rk[kPrepWaves][C], gam[kPrepWaves][C], bet[kPrepWaves][C];
+  __device__ unsigned char* k() { return buf; }
+  __device__ float* m(int w) { return reinterpret_cast<float*>(buf + (kOne ? 0 : kKBytes)) + w * kMatFloats; }
 };
 
 // The ten lower Gram tiles in order t = I (I + 1) / 2 + J (I >= J): tile_i(t), tile_j(t).
@@ -574,9 +582,9 @@ __device__ __forceinline__ constexpr int tile_j(int t) { return t - tile_i(t) * 
 // LDS accesses in order).
 __device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
 
-template <typename TB, bool kList>
-__global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
-  __shared__ __attribute__((aligned(16))) PrepWaveSmem sm;
+template <typename TB, bool kList, bool kOne>
+__global__ __launch_bounds__(64 * kPrepWaves, kOne ? 3 : 2) void gdr_prep_wave(PrepParams p) {
+  __shared__ __attribute__((aligned(16))) PrepWaveSmem<kOne> sm;
   constexpr int kRecBytes = kFragBlocks * kBlockElems * 2 + kScalarBytes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -605,7 +613,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
     for (int m = 0; m < kRowsPerWave / 4; ++m) {
       const int row = kRowsPerWave * wave + 4 * m + (lane >> 4), pos = lane & 15;
       dma16(rsk, (uint32_t)(c * C + row) * row_bytes + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(row)),
-            sm.k + (kRowsPerWave * wave + 4 * m) * 256);
+            sm.k() + (kRowsPerWave * wave + 4 * m) * 256);
     }
   }
   // the first head's gates, in flight with the tile
@@ -613,33 +621,41 @@ __global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
   if (wave < r) graw = gates_issue<TB>(p, b, kh, c, wave, lane);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), as a builtin so that the compiler knows its own loads are done
   lds_barrier();
-  if (wave >= r) return;   // uniform per wave; no barrier follows
 
   // ---- Gram: gk[t][e] = (K K^T)[16 I + 4G + e][16 J + n16] for the ten lower tiles; rk from the diagonal
-  f4 gk[10];
-#pragma unroll
-  for (int t = 0; t < 10; ++t) gk[t] = f4_splat(0.f);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    bf16x8 rows[4];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) rows[I] = lds16(sm.k + swz(16 * I + n16, 4 * kb + G));
-#pragma unroll
-    for (int t = 0; t < 10; ++t) gk[t] = mfma(rows[tile_i(t)], rows[tile_j(t)], gk[t]);
-  }
   float* rk = sm.rk[wave];
   float* gam = sm.gam[wave];
   float* bet = sm.bet[wave];
-  float* M = sm.m[wave];
+  float* M = sm.m(wave);
+  f4 gk[10];
+  auto gram = [&]() {
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {   // diagonal element (16 I + n16, 16 I + n16): lane group n16 / 4, slot n16 & 3
-    const f4 dg = gk[I * (I + 1) / 2 + I];
-    const int e = n16 & 3;
-    const float ss = e == 0 ? dg[0] : e == 1 ? dg[1] : e == 2 ? dg[2] : dg[3];
-    if ((n16 >> 2) == G) rk[16 * I + n16] = 1.0f / sqrtf(ss + 1e-6f);   // model.py, _l2norm
+    for (int t = 0; t < 10; ++t) gk[t] = f4_splat(0.f);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 rows[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) rows[I] = lds16(sm.k() + swz(16 * I + n16, 4 * kb + G));
+#pragma unroll
+      for (int t = 0; t < 10; ++t) gk[t] = mfma(rows[tile_i(t)], rows[tile_j(t)], gk[t]);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {   // diagonal element (16 I + n16, 16 I + n16): lane group n16 / 4, slot n16 & 3
+      const f4 dg = gk[I * (I + 1) / 2 + I];
+      const int e = n16 & 3;
+      const float ss = e == 0 ? dg[0] : e == 1 ? dg[1] : e == 2 ? dg[2] : dg[3];
+      if ((n16 >> 2) == G) rk[16 * I + n16] = 1.0f / sqrtf(ss + 1e-6f);   // model.py, _l2norm
+    }
+  };
+  if constexpr (kOne) {
+    if (wave < r) gram();
+    lds_barrier();   // every wave is done with the K tile, which the matrices overwrite
+  } else if (wave < r) {
+    gram();
   }
+  if (wave >= r) return;   // uniform per wave; no barrier follows
 
-  for (int j = wave; j < r; j += kPrepWaves) {
+  auto head = [&](int j) {
     // ---- gates of value head kh r + j and gamma (the next head's gates are loaded here too)
     float gv, bv;
     gates_finish<TB>(p, j == wave ? graw : gates_issue<TB>(p, b, kh, c, j, lane), gv, bv);
@@ -673,6 +689,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
       for (int i = 0; i < 16; ++i) x[i] = (i == n16) ? 1.f : 0.f;
 #pragma unroll
       for (int k = 0; k < 15; ++k) {
+        if (kOne && (k & 3) == 0) wave_lds_fence();   // loads at most four columns ahead
 #pragma unroll
         for (int i = k + 1; i < 16; ++i) x[i] -= ablk[moff(i, k)] * x[k];
       }
@@ -757,6 +774,11 @@ __global__ __launch_bounds__(64 * kPrepWaves) void gdr_prep_wave(PrepParams p) {
       sc[kBfFlag * C + lane] = (lane == 0 && ok) ? 1.f : 0.f;
     }
     wave_lds_fence();   // the next head's gates and A are written after this head's last reads
+  };
+  if constexpr (kOne) {
+    head(wave);
+  } else {
+    for (int j = wave; j < r; j += kPrepWaves) head(j);
   }
 }
 
@@ -766,17 +788,16 @@ hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStre
     // (checked by the caller)
     const int64_t items = int64_t(p.B) * p.Hk * p.NC;
     const dim3 wgrid((unsigned)items), wblock(64 * kPrepWaves);
-    if (p.chunk_list) {
-      hipLaunchKernelGGL(gdr_chunk_list, dim3(1), dim3(256), 0, s, p.lengths, p.B, p.L, p.NC, p.chunk_list);
-      if (beta_bf16)
-        hipLaunchKernelGGL((gdr_prep_wave<__bf16, true>), wgrid, wblock, 0, s, p);
-      else
-        hipLaunchKernelGGL((gdr_prep_wave<float, true>), wgrid, wblock, 0, s, p);
-    } else if (beta_bf16) {
-      hipLaunchKernelGGL((gdr_prep_wave<__bf16, false>), wgrid, wblock, 0, s, p);
-    } else {
-      hipLaunchKernelGGL((gdr_prep_wave<float, false>), wgrid, wblock, 0, s, p);
-    }
+    if (p.chunk_list) hipLaunchKernelGGL(gdr_chunk_list, dim3(1), dim3(256), 0, s, p.lengths, p.B, p.L, p.NC, p.chunk_list);
+    // one instantiation per (gate dtype, chunk list, at most one value head per wave)
+    using K = void (*)(PrepParams);
+    static const K kernels[2][2][2] = {
+        {{gdr_prep_wave<float, false, false>, gdr_prep_wave<float, false, true>},
+         {gdr_prep_wave<float, true, false>, gdr_prep_wave<float, true, true>}},
+        {{gdr_prep_wave<__bf16, false, false>, gdr_prep_wave<__bf16, false, true>},
+         {gdr_prep_wave<__bf16, true, false>, gdr_prep_wave<__bf16, true, true>}}};
+    const bool one = p.Hv / p.Hk <= kPrepWaves;
+    hipLaunchKernelGGL(kernels[beta_bf16 ? 1 : 0][p.chunk_list ? 1 : 0][one ? 1 : 0], wgrid, wblock, 0, s, p);
   } else {
     const dim3 grid(p.B * p.Hv * p.NC);
     hipLaunchKernelGGL((gdr_prep<float, float>), grid, dim3(256), 0, s, p);
