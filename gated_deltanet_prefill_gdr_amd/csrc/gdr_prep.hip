@@ -662,21 +662,23 @@ __global__ __launch_bounds__(64 * kPrepWaves, kOne ? 3 : 2) void gdr_prep_wave(P
     store_gates(gam, bet, gv, bv, lane);
     wave_lds_fence();
 
-    // ---- A (strictly lower, fp32) from the Gram tiles
+    // ---- A (strictly lower, fp32) from the Gram tiles: A[t][i] = (beta'_t rk_t) rk_i
+    //      2^{min(gamma2_t - gamma2_i, 0)} (K K^T)[t][i]; only the diagonal tiles need the mask
 #pragma unroll
-    for (int t = 0; t < 10; ++t) {
-      const int I = tile_i(t), J = tile_j(t);
+    for (int I = 0; I < 4; ++I) {
       const f4 gr = *reinterpret_cast<const f4*>(gam + 16 * I + 4 * G);
-      const f4 rr = *reinterpret_cast<const f4*>(rk + 16 * I + 4 * G);
-      const f4 br = *reinterpret_cast<const f4*>(bet + 16 * I + 4 * G);
-      const int col = 16 * J + n16;
-      const float gc = gam[col], rc = rk[col];
-      float* ab = blk(M, I, J);
+      const f4 u = *reinterpret_cast<const f4*>(bet + 16 * I + 4 * G) * *reinterpret_cast<const f4*>(rk + 16 * I + 4 * G);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * I + 4 * G + e;
-        const float x = br[e] * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * rr[e] * rc * gk[t][e];
-        ab[moff(4 * G + e, n16)] = row > col ? x : 0.f;
+      for (int J = 0; J <= I; ++J) {
+        const int col = 16 * J + n16;
+        const float gc = gam[col], rc = rk[col];
+        const f4 g = gk[I * (I + 1) / 2 + J];
+        float* ab = blk(M, I, J);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = u[e] * rc * __builtin_amdgcn_exp2f(fminf(gr[e] - gc, 0.f)) * g[e];
+          ab[moff(4 * G + e, n16)] = (J < I || 4 * G + e > n16) ? x : 0.f;
+        }
       }
     }
     wave_lds_fence();
@@ -745,19 +747,15 @@ __global__ __launch_bounds__(64 * kPrepWaves, kOne ? 3 : 2) void gdr_prep_wave(P
 #pragma unroll
     for (int bk = 0; bk < kFragBlocks; ++bk) {
       const int I = block_tile(bk), kb = block_kb(bk);
-      const int row = 16 * I + n16, c0 = 32 * kb + 4 * G;
+      const int c0 = 32 * kb + 4 * G;
       // columns c0.. lie in block (I, 2 kb), columns c0 + 16.. in block (I, 2 kb + 1), which is above
       // the diagonal (not stored, all zero in T) when 2 kb + 1 > I
       const f4 t_lo = tile_row(blk(M, I, 2 * kb), n16, G);
       const f4 t_hi = 2 * kb + 1 <= I ? tile_row(blk(M, I, 2 * kb + 1), n16, G) : f4_splat(0.f);
-      const f4 b_lo = *reinterpret_cast<const f4*>(&bet[c0]);
-      const f4 b_hi = *reinterpret_cast<const f4*>(&bet[c0 + 16]);
-      f4 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo[e] = (c0 + e <= row) ? t_lo[e] * b_lo[e] : 0.f;
-        hi[e] = (c0 + 16 + e <= row) ? t_hi[e] * b_hi[e] : 0.f;
-      }
+      // T is exactly zero above the diagonal of its stored diagonal blocks (the forward substitution
+      // leaves those entries at zero), so no mask is needed
+      const f4 lo = t_lo * *reinterpret_cast<const f4*>(&bet[c0]);
+      const f4 hi = t_hi * *reinterpret_cast<const f4*>(&bet[c0 + 16]);
       *reinterpret_cast<bf16x8*>(rec + (size_t)bk * kBlockElems * 2 + (size_t)lane * 16) = pack8(lo, hi);
     }
     {
