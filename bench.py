@@ -435,6 +435,16 @@ def main():
         step()
     torch.cuda.synchronize()
     ms, kern = run_timed(step, a.steps)
+    # (row, head) pairs the last call recomputed without truncation (the status word), then the same
+    # call with truncated segment starts switched off (the exact composition), for context
+    off = gdr.status_offset(desc)
+    reruns = int(ws[off:off + 4].view(torch.int32).item()) if off is not None else None
+    gdr.set_truncation(False)
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    ms_exact, _ = run_timed(step, max(10, a.steps // 2))
+    gdr.set_truncation(True)
 
     units, nbytes, flops = algorithmic(B, L, Hk, Hv, 2, 0, True)
     if a.fused:   # raw bf16 projections instead of fp32 g, beta; plus the gate z
@@ -487,7 +497,7 @@ def main():
                                          "interface_bytes": k_bytes,
                                          "interface_GBs": k_bytes / (k_ms * 1e-3) / 1e9}},
         "path": {"ms": ms, "kernel_ms": {n: t for n, (t, c) in per_kernel.items()}, "segments": P,
-                 "source_hash": source_hash()},
+                 "reruns": reruns, "exact_ms": ms_exact, "source_hash": source_hash()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -446,9 +446,7 @@ __global__ __launch_bounds__(256, 2) void gdr_prep(PrepParams p) {
                         [](int) {});
 }
 
-// ====================================================================== bf16: per key head, persistent
-// LDS of the key-head prep: the K tile (swizzled 256-byte rows, written by DMA), and A, then T in
-// place, of two value heads.
+// ====================================================================== bf16
 // Gates of value head hr of an item's key head at this lane's token, in two steps so that the loads
 // of the next item stay in flight while the current one computes: gates_issue loads the raw words
 // (range-checked: tokens past L read zeros, and nothing waits on them), gates_finish applies the
@@ -554,7 +552,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, in
 // One workgroup of kPrepWaves waves per work item (row b, key head kh, chunk c). The waves copy the
 // item's K tile HBM -> LDS by DMA (half of the rows each) and meet once; then each wave forms all ten
 // lower tiles of the Gram K K^T (bf16 MFMA; rk from their diagonal) and runs, for the value heads
-// kh r + j with j = wave, wave + kPrepWaves, ... on its own, the steps of the keyhead kernel above in
+// kh r + j with j = wave, wave + kPrepWaves, ... on its own, the steps of the float32 kernel above in
 // sequence: gates and gamma, A, the blocked inverse in its own LDS matrix, and the record. A wave's
 // LDS accesses complete in order, so no other barrier is needed; the latency of one wave's steps is
 // hidden by the other workgroups on the compute unit rather than split over four waves with a
