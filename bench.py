@@ -10,7 +10,8 @@ runs untimed for 0.3 s so that the GPU's clocks have settled. Prints one JSON li
   python bench.py --decode          # one fork decode step instead (gdr_decode, 64 rows x 1 token)
   python bench.py --layer           # the layer steps around it (gates, conv + SiLU, gated RMSNorm)
   python bench.py --fused           # the prefill with the gate prologue and gated RMSNorm fused in
-  python bench.py --all-configs     # every named workload: median call time, throughput, rooflines
+  python bench.py --all-configs     # every named workload: median call time, throughput, rooflines,
+                                    # per-kernel times (--config N for one of them)
   python bench.py --copy-probe      # a plain device copy of known size, for HBM counter scaling
 """
 from __future__ import annotations
@@ -323,13 +324,14 @@ def bench_all_configs(a):
     import torch
     import gated_deltanet_prefill_gdr_amd as gdr
     from workloads import CONFIGS
+    which = sorted(a.config) if a.config else sorted(CONFIGS)
     cpu = {}
     if not a.no_cpu_baseline:   # every config's oracle time first: its workers are forked
-        for i in sorted(CONFIGS):
+        for i in which:
             cpu[i] = cpu_baseline(CONFIGS[i].draw())
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    for i in sorted(CONFIGS):
+    for i in which:
         x = CONFIGS[i].draw()
         B, L, Hk, Hv, Dk, Dv = x.shape
         esz = 2 if x.q.dtype == torch.bfloat16 else 4
@@ -357,6 +359,13 @@ def bench_all_configs(a):
             e1.record()
         torch.cuda.synchronize()
         ms = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev)
+        gdr.timing_enable(True)   # per-kernel averages, in a loop of their own
+        gdr.timing_read()
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        kern = {n: t / c for n, (t, c) in gdr.timing_read().items() if c > 0}
+        gdr.timing_enable(False)
         units, nbytes, flops = algorithmic(B, L, Hk, Hv, esz, n_s0, True)
         nbytes += 4 * B if x.lengths is not None else 0
         valid_units = units if x.lengths is None else int(x.lengths.sum()) * Hv
@@ -366,7 +375,7 @@ def bench_all_configs(a):
                 "valid_tokens_heads_per_s": valid_units / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
                 "alg_GBs": nbytes / (ms * 1e-3) / 1e9, "mfma_frac": flops / (ms * 1e-3) / 1e12 / peak,
                 "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "alg_bytes": nbytes, "alg_flops": flops,
-                "cpu_baseline": cpu.get(i)}
+                "kernel_ms": kern, "cpu_baseline": cpu.get(i)}
         print(json.dumps(line), flush=True)
 
 
@@ -382,6 +391,8 @@ def main():
     ap.add_argument("--layer", action="store_true")
     ap.add_argument("--fused", action="store_true")
     ap.add_argument("--all-configs", action="store_true", help="time every named workload (a report)")
+    ap.add_argument("--config", type=int, action="append", choices=[1, 2, 3, 4, 5],
+                    help="with or instead of --all-configs: only these named workloads (repeatable)")
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up (0 for counter runs)")
     a = ap.parse_args()
@@ -400,7 +411,7 @@ def main():
     if a.layer:
         bench_layer(a)
         return
-    if a.all_configs:
+    if a.all_configs or a.config:
         bench_all_configs(a)
         return
     import gated_deltanet_prefill_gdr_amd as gdr
