@@ -15,7 +15,10 @@
 // its true entering state, writing outputs (and, for the last one, the final state). With
 // P = 1 only gdr_scan_bf16 runs. Chunks wholly past a row's length (right pads: beta' = g' = 0)
 // are the identity map: the transitions skip them and the output pass gives them a short loop of
-// their own (O = diag(rq) Q S).
+// their own (O = diag(rq) Q S). Under strong decay a (row, head) takes truncated segment starts
+// instead (the transition pass runs only a short window before each boundary from zero, the
+// combine returns at once, and gdr_finalize_bf16 checks the error bound afterwards, rerunning the
+// (row, head) exactly where it fails; see the truncation plan below).
 //
 // gdr_scan_f32: float32 inputs; one workgroup per (row, value head, 16-column slice), its four
 // waves splitting the slice's state by key blocks and walking all chunks together (fp32 MFMA, each
