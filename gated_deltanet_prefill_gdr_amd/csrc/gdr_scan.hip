@@ -168,9 +168,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // kWin (with kOut): a window, the chunks c_begin .. c_end - 1 run from zero on the value columns in
 // the output pass's layout but without its outputs; it leaves the end state and its norm.
-template <bool kOut, bool kWin = false>
+// kFuse (with kOut): the gated RMSNorm is fused into the outputs (p.z is set). A separate
+// instantiation, so that the plain output pass carries none of the norm's registers or branches.
+template <bool kOut, bool kWin = false, bool kFuse = false>
 __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds, int b, int h, const SegRun& run) {
   static_assert(kOut || !kWin, "a window runs in the output pass's layout");
+  static_assert(!kFuse || (kOut && !kWin), "the norm is fused into the outputs only");
   using Cfg = SegCfg<kOut>;
   constexpr int NSL = Cfg::NSL, NW = Cfg::NW;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -209,11 +212,11 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
                               (uint32_t)p.NC * kRecB);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + vo_base, vo_bytes);
   // fused gated RMSNorm (outputs only): gate z in o's layout, weights of this lane's columns
-  const i32x4 rz = rsrc_words(p.z ? reinterpret_cast<const __bf16*>(p.z) + vo_base : nullptr, p.z ? vo_bytes : 0u);
+  const i32x4 rz = rsrc_words(kFuse ? reinterpret_cast<const __bf16*>(p.z) + vo_base : nullptr, kFuse ? vo_bytes : 0u);
   f4 nw[NSL];
 #pragma unroll
   for (int sl = 0; sl < NSL; ++sl)
-    nw[sl] = (kOut && p.z) ? *reinterpret_cast<const f4*>(p.norm_w + seg_col<kOut>(w, sl) + 4 * G) : f4_splat(0.f);
+    nw[sl] = kFuse ? *reinterpret_cast<const f4*>(p.norm_w + seg_col<kOut>(w, sl) + 4 * G) : f4_splat(0.f);
 
   // This wave's share of chunk c: K (and Q, and the fused norm's gate rows) and V rows
   // R w .. R w + R - 1 (R = 64 / NW, loads of four rows each) and the 1 KiB record blocks w,
@@ -230,7 +233,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       if (parts & kStK) dma16(rk, kq, Bf + Cfg::kK + (R * w + 4 * m) * 256);
       if (kOut && (parts & kStQ)) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
       if (parts & kStV) dma16(rv, (t0 + r) * vo_row + 16 * (pos ^ (2 * (r & 7))), Bf + Cfg::kV + (R * w + 4 * m) * 256);
-      if (kOut && p.z && (parts & kStQ))
+      if (kFuse && (parts & kStQ))
         dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
     }
     if (parts & kStRec) {
@@ -251,7 +254,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
       const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
       if constexpr (kOut) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
-      if (kOut && p.z) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
+      if (kFuse) dma16(rz, (t0 + r) * vo_row + 16 * (pos ^ (r & 15)), Bf + Cfg::kZ + (R * w + 4 * m) * 256);
     }
   };
   // Q tiles of the pad chunks c0 .. c0 + kPadGroup - 1 (those before c_end) into the Q, K and V
@@ -438,7 +441,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     store_o(c);
   };
 
-  const bool fuse = kOut && p.z != nullptr;
+  constexpr bool fuse = kFuse;
   if (c_begin < c_mid)
     issue(c_begin, kStAll);
   else if (c_begin < c_end && fuse)
@@ -844,7 +847,8 @@ __device__ __forceinline__ int certificate_status(const ScanParams& p, size_t hb
 }
 
 
-// Outputs: one workgroup per (row, segment, value head), heads fastest.
+// Outputs: one workgroup per (row, segment, value head), heads fastest; kFuse when p.z is set.
+template <bool kFuse>
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
   const int lam = xcd_remap(blockIdx.x, gridDim.x);
@@ -863,7 +867,7 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
       run.cert = p.cert + (head_index(p, b, h) * p.P + j + 1) * kCertFloats;
     }
   }
-  seg_body<true>(p, lds, b, h, run);
+  seg_body<true, false, kFuse>(p, lds, b, h, run);
 }
 
 // Truncation plan of a (row, head), from the chunk records. Its loads are issued first, all of them
@@ -1020,7 +1024,10 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanP
   all.src = slot_ptr(p, b, h, 0);
   all.last = true;
   all.cert_chunk = -1;
-  seg_body<true>(p, lds, b, h, all);
+  if (p.z)
+    seg_body<true, false, true>(p, lds, b, h, all);
+  else
+    seg_body<true, false, false>(p, lds, b, h, all);
 }
 
 // Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero). One
@@ -1415,7 +1422,10 @@ hipError_t launch_finalize(const ScanParams& p, hipStream_t s) {
 
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s) {
   if (qkv_bf16) {
-    hipLaunchKernelGGL(gdr_scan_bf16, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
+    if (p.z)
+      hipLaunchKernelGGL(gdr_scan_bf16<true>, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
+    else
+      hipLaunchKernelGGL(gdr_scan_bf16<false>, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
   } else {
     hipLaunchKernelGGL(gdr_scan_f32, dim3(p.B * p.Hv * kSlices16), dim3(256), 0, s, p);
   }
