@@ -74,8 +74,9 @@ __device__ __forceinline__ int swz_z(int row, int chunk16) { return row * 256 + 
 // LDS accesses are done, then meet the other waves. Memory clobbers keep every LDS access on
 // its side of the wait and the barrier.
 template <int N> __device__ __forceinline__ void wait_and_barrier() {
-  static_assert(N == 0 || N == 4 || N == 8 || N == 12, "extend the list of encodings");   // stores
+  static_assert(N == 0 || N == 4 || N == 8 || N == 12 || N == 24, "extend the list of encodings");   // stores
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -870,6 +871,479 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
   seg_body<true, false, kFuse>(p, lds, b, h, run);
 }
 
+// ---- Output pass over a pair of value heads (bf16, Hv / Hk even, no fused norm; used without segments
+// when the pairs fill the GPU, see use_pair_pass)
+// Value heads 2 hp and 2 hp + 1 share one key head, so one workgroup runs both: the K and Q tiles are
+// staged once, and each wave holds two 16-column slices (32 columns of one head: waves 0-3 head 2 hp,
+// waves 4-7 head 2 hp + 1), so that every K, K^T and Q fragment it reads from LDS feeds two products.
+// Per head that halves the LDS reads of the single-head pass above, whose time they bound. Every column
+// runs the single-head pass's arithmetic in the same order (the same results, bit for bit).
+// A wave's V columns are staged by that wave alone, into an LDS area of its own with one buffer: the
+// next chunk's are loaded once this chunk's R has been formed, and no other wave waits for them.
+struct PairCfg {
+  static constexpr int NW = 8, NSL = 2;
+  static constexpr int kK = 0, kQ = kBufK, kRec = 2 * kBufK;   // head e's record at kRec + e kRecB
+  static constexpr int kBuf = kRec + 2 * kRecB;                  // one chunk: 48 KiB
+  static constexpr int kVWave = C * 64;                          // a wave's V: 64 tokens x 32 columns
+  static constexpr int kV = 2 * kBuf;                            // wave w's V at kV + w kVWave
+  static constexpr int kP = kV + NW * kVWave;                    // head e's P' at kP + e kFragBlocks KiB
+  static constexpr int kRq = kP + 2 * kFragBlocks * 1024;        // |q_t|^2 (kPadGroup chunks in the pads)
+  static constexpr int kLds = kRq + kPadGroup * C * 4;
+  static constexpr int kStores = 4 * NSL;                        // output stores per wave per chunk
+};
+static_assert(PairCfg::kLds <= 160 * 1024, "one workgroup's LDS");
+static_assert(2 * kRecB == kBufK, "the two records of a chunk hold one Q tile in the pads");
+
+// A wave's V tile in the pair pass: row t (64 bytes: the wave's two 16-column slices) at 64 t, its
+// halves swapped when bit 2 of t is set, so that the eight rows one transposing read touches fill
+// all 64 banks once.
+__device__ __forceinline__ int swz_pv(int row, int half) { return row * 64 + 32 * (half ^ ((row >> 2) & 1)); }
+
+struct PairRun {
+  int c_begin, c_end;
+  int src_kind;            // as SegRun::src_kind, for both heads
+  const float* src[2];     // head e's entering state (segment slot, pitch 2D)
+  bool last;               // the run ends the row: s_final is written
+  int cert_chunk[2];       // head e: chunk at whose top ||S||_F^2 goes to cert[e] (-1: none)
+  float* cert[2];
+};
+
+__device__ __forceinline__ void pair_body(const ScanParams& p, unsigned char* lds, int b, int hp, const PairRun& run) {
+  using Cfg = PairCfg;
+  constexpr int NSL = Cfg::NSL, NW = Cfg::NW;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, G = lane >> 4;
+  const int e = w >> 2, h = 2 * hp + e;           // this wave's head
+  const int kh = (2 * hp) / (p.Hv / p.Hk);        // the pair's key head
+  const int col0 = 32 * (w & 3);                  // the wave's first column of head h
+  const int c_begin = run.c_begin, c_end = run.c_end;
+  const __bf16* qg = reinterpret_cast<const __bf16*>(p.q);
+  const __bf16* kg = reinterpret_cast<const __bf16*>(p.k);
+  const __bf16* vg = reinterpret_cast<const __bf16*>(p.v);
+  __bf16* og = reinterpret_cast<__bf16*>(p.o);
+
+  int srow = 0;
+  if (row_is_bad(p, b, srow)) {   // NaN outputs for both heads
+    const float nan = __builtin_nanf("");
+    const int t_end = min(c_end * C, p.L);
+    for (int i = c_begin * C * 2 * D + tid; i < t_end * 2 * D; i += 64 * NW) {
+      const int t = i / (2 * D), r = i % (2 * D);
+      og[((size_t)b * p.L + t) * p.Hv * D + (size_t)(2 * hp + r / D) * D + r % D] = (__bf16)nan;
+    }
+    if (p.s_final && run.last)
+      for (int i = tid; i < 2 * D * D; i += 64 * NW) p.s_final[((size_t)b * p.Hv + 2 * hp) * D * D + i] = nan;
+    return;
+  }
+
+  int len_b = p.lengths ? p.lengths[b] : p.L;
+  len_b = len_b < 0 ? 0 : (len_b > p.L ? p.L : len_b);
+  const uint32_t kq_row = (uint32_t)p.Hk * D * 2, vo_row = (uint32_t)p.Hv * D * 2;
+  const size_t kq_base = (size_t)b * p.L * p.Hk * D, vo_base = ((size_t)b * p.L * p.Hv + h) * D;
+  const uint32_t vo_bytes = p.L > 0 ? (uint32_t)(p.L - 1) * vo_row + D * 2 : 0;
+  const i32x4 rk = rsrc_words(kg + kq_base, (uint32_t)p.L * kq_row);
+  const i32x4 rq = rsrc_words(qg + kq_base, (uint32_t)p.L * kq_row);
+  const i32x4 rv = rsrc_words(vg + vo_base, vo_bytes);   // this wave's head
+  // both heads' records: head 2 hp + 1's follow head 2 hp's
+  const i32x4 rr = rsrc_words(reinterpret_cast<const unsigned char*>(p.ws) + ((size_t)b * p.Hv + 2 * hp) * p.NC * kRecB,
+                              (uint32_t)(2 * p.NC) * kRecB);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(og + vo_base, vo_bytes);
+  unsigned char* Vw = lds + Cfg::kV + w * Cfg::kVWave;
+
+  // Chunk c's shared staging: K and Q rows 8 w .. 8 w + 7 (loads of four rows) and record blocks
+  // w, w + 8 of the fourteen (head 2 hp's seven, then head 2 hp + 1's).
+  constexpr int R = C / NW;
+  enum : int { kStK = 1, kStQ = 2, kStRec = 4, kStAll = 7 };
+  auto issue = [&](int c, int parts) {
+    unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
+    const uint32_t t0 = (uint32_t)c * C;
+#pragma unroll
+    for (int m = 0; m < R / 4; ++m) {
+      const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
+      const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
+      if (parts & kStK) dma16(rk, kq, Bf + Cfg::kK + (R * w + 4 * m) * 256);
+      if (parts & kStQ) dma16(rq, kq, Bf + Cfg::kQ + (R * w + 4 * m) * 256);
+    }
+    if (parts & kStRec) {
+#pragma unroll
+      for (int i0 = 0; i0 < 2 * kRecBlocks; i0 += NW) {
+        const int i = i0 + w;
+        if (i < 2 * kRecBlocks) {   // wave-uniform
+          const int he = i >= kRecBlocks ? 1 : 0, blk = i - he * kRecBlocks;
+          dma16(rr, ((uint32_t)he * p.NC + c) * kRecB + 1024 * blk + 16 * lane,
+                Bf + Cfg::kRec + he * kRecB + 1024 * blk);
+        }
+      }
+    }
+  };
+  // This wave's V columns of chunk c: four loads of 16 rows; lane l lands at byte 16 l of its load's
+  // kilobyte, which swz_pv assigns to row 16 m + l / 4 and the piece computed here.
+  auto issue_v = [&](int c) {
+    const uint32_t t0 = (uint32_t)c * C;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = 16 * m + (lane >> 2), qp = lane & 3;
+      const int pos = 2 * ((qp >> 1) ^ ((t >> 2) & 1)) + (qp & 1);
+      dma16(rv, (t0 + t) * vo_row + 2 * col0 + 16 * pos, Vw + 1024 * m);
+    }
+  };
+  // V[16 mt + 4G + i][col0 + 16 sl + n16], i = 0..3, from this wave's tile (as v_col4)
+  auto v_cols = [&](int mt, int sl) {
+    const int t = 16 * mt + 4 * G + (n16 >> 2);
+    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vw + swz_pv(t, sl) + 8 * (n16 & 3)));
+    const bf16x4 y = __builtin_bit_cast(bf16x4, x);
+    return f4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+  };
+  // Q tiles of the pad chunks c0 .. c0 + kPadGroup - 1 (those before c_end) into the Q, K and record
+  // regions of buffer bi
+  auto issue_qg = [&](int c0, int bi) {
+    unsigned char* Bf = lds + bi * Cfg::kBuf;
+#pragma unroll
+    for (int i = 0; i < kPadGroup; ++i) {
+      if (c0 + i >= c_end) break;   // uniform
+      const int region = i == 0 ? Cfg::kQ : (i == 1 ? Cfg::kK : Cfg::kRec);
+      const uint32_t t0 = (uint32_t)(c0 + i) * C;
+#pragma unroll
+      for (int m = 0; m < R / 4; ++m) {
+        const int r = R * w + 4 * m + (lane >> 4), pos = lane & 15;
+        const uint32_t kq = (t0 + r) * kq_row + (uint32_t)kh * D * 2 + 16 * (pos ^ swz_f(r));
+        dma16(rq, kq, Bf + region + (R * w + 4 * m) * 256);
+      }
+    }
+  };
+  const int c_mid = min(max((len_b + C - 1) / C, c_begin), c_end);
+
+  // ---- state entering the segment (this wave's columns of head h)
+  f4 S[NSL][4][2];
+  {
+    const float* src = nullptr;
+    size_t pitch = 0;
+    if (run.src_kind == 1) {
+      src = e ? run.src[1] : run.src[0];
+      pitch = 2 * D;
+    } else if (run.src_kind == 2 && p.s0) {
+      src = p.s0 + ((size_t)srow * p.Hv + h) * D * D;
+      pitch = D;
+    }
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[sl][kb][s2][i] = src ? src[(32 * kb + 8 * G + 4 * s2 + i) * pitch + col0 + 16 * sl + n16] : 0.f;
+  }
+
+  f4 Ot[4][NSL];
+  auto store_tile = [&](int c, int mt) {
+    const uint32_t orow = ((uint32_t)c * C + 16 * mt + n16) * vo_row;
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      const bf16x4 ob = {(__bf16)Ot[mt][sl][0], (__bf16)Ot[mt][sl][1], (__bf16)Ot[mt][sl][2], (__bf16)Ot[mt][sl][3]};
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, ob), ro, orow + 2 * (col0 + 16 * sl + 4 * G), 0, 0);
+    }
+  };
+
+  if (c_begin < c_mid) {
+    issue(c_begin, kStAll);
+    issue_v(c_begin);
+  } else if (c_begin < c_end) {
+    issue_qg(c_begin, c_begin & 1);
+  }
+  wait_and_barrier<0>();
+  __builtin_amdgcn_s_waitcnt(0);   // the entering-state loads are complete (no wait for them in the loop)
+
+  float* rqs = reinterpret_cast<float*>(lds + Cfg::kRq);   // |q_t|^2, t = 0..63
+  auto put_qnorms = [&](float* dst, int mt, const f4& qq) {   // lane (n16, G): rows 4G .. 4G + 3 of column n16
+    if ((n16 >> 2) == G) {
+      const int ee = n16 & 3;
+      dst[16 * mt + n16] = ee == 0 ? qq[0] : ee == 1 ? qq[1] : ee == 2 ? qq[2] : qq[3];
+    }
+  };
+  const int cert_chunk = e ? run.cert_chunk[1] : run.cert_chunk[0];
+  float* cert = e ? run.cert[1] : run.cert[0];
+
+  for (int c = c_begin; c < c_mid; ++c) {
+    // chunk c has landed for every wave (this wave's V too), every wave is done with chunk c - 1's
+    // buffer; after chunk c's loads each wave issued only chunk c - 1's output stores
+    wait_and_barrier<Cfg::kStores>();
+    if (c == cert_chunk) {   // ||S||_F^2 of the state entering chunk c: this wave's part, in slot w & 3
+      float ss = 0.f;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ss += S[sl][kb][s2][i] * S[sl][kb][s2][i];
+      ss = wave_sum(ss);
+      if (lane == 0) {
+        cert[w & 3] = ss;
+        cert[4 + (w & 3)] = 0.f;
+      }
+    }
+    if (c + 1 < c_mid)
+      issue(c + 1, kStK);
+    else if (c + 1 < c_end)
+      issue_qg(c + 1, (c + 1) & 1);
+    const bool stage_next = c + 1 < c_mid;
+
+    const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
+    const unsigned char* Kt = Bf + Cfg::kK;
+    const unsigned char* Qt = Bf + Cfg::kQ;
+    const unsigned char* Rc = Bf + Cfg::kRec + e * kRecB;   // this wave's head's record
+    const float* sc = reinterpret_cast<const float*>(Rc + kScOff);
+
+    // P' of this chunk for both heads: waves 0..5 form block w of K Q^T once (the key head's) and
+    // scale it by each head's gates; the waves of token tiles (kb2 = 0) also leave |q_t|^2 in LDS.
+    for (int blk = w; blk < w + 1 && blk < kFragBlocks; ++blk) {
+      const int mt = block_tile(blk), kb2 = block_kb(blk);
+      f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)}, qq = f4_splat(0.f);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
+        if (kb2 == 0) qq = mfma(qf, qf, qq);
+      }
+      if (kb2 == 0) put_qnorms(rqs, mt, qq);
+      const int t = 16 * mt + n16;
+#pragma unroll
+      for (int he = 0; he < 2; ++he) {
+        const float* sce = reinterpret_cast<const float*>(Bf + Cfg::kRec + he * kRecB + kScOff);
+        const float gt = sce[kBfGam2 * C + t];
+        f4 x2[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int i0 = 32 * kb2 + 16 * s2 + 4 * G;
+          const f4 gi = *reinterpret_cast<const f4*>(sce + kBfGam2 * C + i0);
+          const f4 ri = *reinterpret_cast<const f4*>(sce + kBfRk * C + i0);
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float x = ri[q4] * __builtin_amdgcn_exp2f(fminf(gt - gi[q4], 0.f)) * pt[s2][q4];
+            x2[s2][q4] = (i0 + q4 <= t) ? x : 0.f;
+          }
+        }
+        *reinterpret_cast<bf16x8*>(lds + Cfg::kP + he * kFragBlocks * 1024 + 1024 * blk + 16 * lane) = pack8(x2[0], x2[1]);
+      }
+    }
+
+    bf16x8 Sop[NSL][4];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
+
+    if (stage_next) issue(c + 1, kStQ);
+
+    // X = K S
+    f4 X[NSL][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = f4_splat(0.f);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kf = lds16(Kt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = mfma(kf, Sop[sl][kb], X[sl][mt]);
+      }
+    }
+    // R = V - diag(a) X
+    bf16x8 Rop[NSL][2];
+    {
+      f4 a4[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a4[mt] = *reinterpret_cast<const f4*>(sc + 16 * mt + 4 * G);
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        f4 Rv[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          Rv[mt] = -a4[mt] * X[sl][mt];
+          Rv[mt] += v_cols(mt, sl);
+        }
+        Rop[sl][0] = pack8(Rv[0], Rv[1]);
+        Rop[sl][1] = pack8(Rv[2], Rv[3]);
+      }
+    }
+    // Delta = Tb R (lower-triangular blocks only)
+    f4 Dl[NSL][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = f4_splat(0.f);
+#pragma unroll
+      for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
+        const bf16x8 tf = lds16(Rc + 1024 * frag_block(mt, kb2) + 16 * lane);
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Dl[sl][mt] = mfma(tf, Rop[sl][kb2], Dl[sl][mt]);
+      }
+    }
+    // the next chunk's V into this wave's area: its reads of this chunk's V are complete
+    if (stage_next) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue_v(c + 1);
+    }
+    bf16x8 Ddop[NSL][2];
+    {
+      f4 d4[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) d4[mt] = *reinterpret_cast<const f4*>(sc + kBfD * C + 16 * mt + 4 * G);
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        Ddop[sl][0] = pack8(Dl[sl][0] * d4[0], Dl[sl][1] * d4[1]);
+        Ddop[sl][1] = pack8(Dl[sl][2] * d4[2], Dl[sl][3] * d4[3]);
+      }
+    }
+    if (stage_next) issue(c + 1, kStRec);
+    lds_barrier();   // P' (both heads) and the q norms are complete
+    // O^T = diag(c) (S^T Q^T) + Delta^T P^T, then the q norm of each row
+    {
+      bf16x8 Dop[NSL][2];
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl) {
+        Dop[sl][0] = pack8(Dl[sl][0], Dl[sl][1]);
+        Dop[sl][1] = pack8(Dl[sl][2], Dl[sl][3]);
+      }
+      const unsigned char* Pe = lds + Cfg::kP + e * kFragBlocks * 1024;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
+        }
+        const float eg = __builtin_amdgcn_exp2f(sc[kBfGam2 * C + 16 * mt + n16]);   // e^gamma_t
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= eg;
+#pragma unroll
+        for (int kb2 = 0; kb2 <= (mt >> 1); ++kb2) {
+          const bf16x8 pf = lds16(Pe + 1024 * frag_block(mt, kb2) + 16 * lane);
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Dop[sl][kb2], pf, Ot[mt][sl]);
+        }
+        const float rqv = __builtin_amdgcn_rsqf(rqs[16 * mt + n16] + 1e-6f) * 0.08838834764831845f;   // * 128^-1/2
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rqv;
+        store_tile(c, mt);
+      }
+    }
+    // S <- e^{gamma_63} S + K^T diag(d) Delta
+    const float egc = __builtin_amdgcn_exp2f(sc[kBfGam2 * C + C - 1]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] *= egc;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const bf16x8 kt = kt_frag(Kt, kb, s2, kb2, G, n16);
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) S[sl][kb][s2] = mfma(kt, Ddop[sl][kb2], S[sl][kb][s2]);
+        }
+      }
+  }
+
+  // Right pads (beta' = g' = 0): the state stays as it is and O = diag(rq) Q S, groups of kPadGroup
+  // chunks, group g in buffer (c_mid + g) & 1; after a group's loads come the stores of the chunk or
+  // group before it (none when the segment starts in the pads: its first group was waited for above).
+  {
+    bf16x8 Sop[NSL][4];
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
+    for (int c0 = c_mid, g = 0; c0 < c_end; c0 += kPadGroup, ++g) {
+      const int bi = (c_mid + g) & 1, n = min(kPadGroup, c_end - c0);
+      if (g == 0)
+        wait_and_barrier<Cfg::kStores>();
+      else
+        wait_and_barrier<kPadGroup * Cfg::kStores>();
+      if (c0 + kPadGroup < c_end) issue_qg(c0 + kPadGroup, bi ^ 1);
+      const unsigned char* Bq = lds + bi * Cfg::kBuf;
+      for (int pr = w; pr < 4 * n; pr += NW) {   // q norms of (chunk pr / 4, token tile pr % 4)
+        const int i = pr >> 2, mt = pr & 3;
+        const unsigned char* Qt = Bq + (i == 0 ? Cfg::kQ : (i == 1 ? Cfg::kK : Cfg::kRec));
+        f4 qq = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+          qq = mfma(qf, qf, qq);
+        }
+        put_qnorms(rqs + 64 * i, mt, qq);
+      }
+      lds_barrier();
+      for (int i = 0; i < n; ++i) {
+        const unsigned char* Qt = Bq + (i == 0 ? Cfg::kQ : (i == 1 ? Cfg::kK : Cfg::kRec));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = f4_splat(0.f);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] = mfma(Sop[sl][kb], qf, Ot[mt][sl]);
+          }
+          const float rqv = __builtin_amdgcn_rsqf(rqs[64 * i + 16 * mt + n16] + 1e-6f) * 0.08838834764831845f;
+#pragma unroll
+          for (int sl = 0; sl < NSL; ++sl) Ot[mt][sl] *= rqv;
+          store_tile(c0 + i, mt);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no load into LDS may still be in flight when the workgroup ends
+
+  // ---- end state
+  if (!(p.s_final && run.last)) return;
+  float* dst = p.s_final + ((size_t)b * p.Hv + h) * D * D;
+#pragma unroll
+  for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(32 * kb + 8 * G + 4 * s2 + i) * D + col0 + 16 * sl + n16] = S[sl][kb][s2][i];
+}
+
+// Outputs over value-head pairs: one workgroup per (row, segment, head pair), pairs fastest.
+__global__ __launch_bounds__(64 * PairCfg::NW) void gdr_scan_bf16_pair(ScanParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[PairCfg::kLds];
+  const int np = p.Hv / 2;
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);
+  const int hp = lam % np, j = (lam / np) % p.P, b = lam / (np * p.P);
+  PairRun run{};
+  run.c_begin = j * p.Ls;
+  run.c_end = min(run.c_begin + p.Ls, p.NC);
+  run.src_kind = p.P > 1 ? 1 : 2;   // with segments, the combine has put every entering state in its slot
+  run.last = j == p.P - 1;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int h = 2 * hp + e;
+    run.src[e] = p.P > 1 ? slot_ptr(p, b, h, j) : nullptr;
+    run.cert_chunk[e] = -1;
+    run.cert[e] = nullptr;
+    if (p.P > 1 && p.trunc && j + 1 < p.P) {
+      const PlanEntry pe = p.plan[head_index(p, b, h) * p.P + j + 1];
+      if (pe.trunc) {   // the window of boundary j + 1 starts inside this segment
+        run.cert_chunk[e] = (j + 1) * p.Ls - pe.W;
+        run.cert[e] = p.cert + (head_index(p, b, h) * p.P + j + 1) * kCertFloats;
+      }
+    }
+  }
+  pair_body(p, lds, b, hp, run);
+}
+
 // Truncation plan of a (row, head), from the chunk records. Its loads are issued first, all of them
 // together (one memory round trip), and decided on after: PlanLoads holds what thread t of the
 // workgroup reads, decide_window / chunks_contract decide from it.
@@ -1420,10 +1894,21 @@ hipError_t launch_finalize(const ScanParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The pair pass needs Hv / Hk even and no fused norm. It is taken when the rows need no segments and
+// the pairs alone fill the GPU (B Hv / 2 workgroups, at least one per CU). With segments it would need
+// twice as many of them to fill the GPU, so twice the window transitions (two rounds of workgroups)
+// and twice the entering-state loads, which cost more than its faster chunks save at the long prefill.
+static bool use_pair_pass(const ScanParams& p) {
+  return p.z == nullptr && p.Hk > 0 && p.Hv % p.Hk == 0 && (p.Hv / p.Hk) % 2 == 0 && p.P == 1 &&
+         int64_t(p.B) * (p.Hv / 2) >= kSegTargetWorkgroups;
+}
+
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s) {
   if (qkv_bf16) {
     if (p.z)
       hipLaunchKernelGGL(gdr_scan_bf16<true>, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
+    else if (use_pair_pass(p))
+      hipLaunchKernelGGL(gdr_scan_bf16_pair, dim3(p.B * (p.Hv / 2) * p.P), dim3(64 * PairCfg::NW), 0, s, p);
     else
       hipLaunchKernelGGL(gdr_scan_bf16<false>, dim3(p.B * p.Hv * p.P), dim3(64 * SegCfg<true>::NW), 0, s, p);
   } else {

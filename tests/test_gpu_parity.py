@@ -224,6 +224,53 @@ def test_head_pairs_identical():
     assert torch.equal(o[:, :, 0::2], o[:, :, 1::2]) and torch.equal(s[:, 0::2], s[:, 1::2])
 
 
+# ------------------------------------------------------------------ value-head pairs
+# Without segments and with B Hv / 2 >= 256, the bf16 output pass runs the two value heads of a key head
+# in one workgroup (each column with the single-head pass's arithmetic, in the same order). A batch that
+# takes it must equal, bit for bit, the same rows run in halves, which are too few for the pair pass.
+PAIR_KW = dict(lengths=[200, 0, 64, 65, 1, 130, 199, 128] * 4, s0_rows=3, s0_row=[0, 1, 2] * 10 + [1, 0])
+
+
+def _rows(x, lo, hi):
+    """Rows lo .. hi - 1 of x (the same initial-state rows)."""
+    from dataclasses import replace
+    return replace(x, **{n: getattr(x, n)[lo:hi].contiguous()
+                         for n in ("q", "k", "v", "g", "beta", "lengths", "s0_row")})
+
+
+def test_pair_pass_equals_single_head_pass_bitwise():
+    x = draw(32, 200, 4, 16, 128, "R1", 520, torch.bfloat16, **PAIR_KW)   # 32 x 8 pairs: the pair pass
+    o, s = run_gpu(x)
+    for lo in (0, 16):   # 16 x 16 heads: 128 pairs, the single-head pass, still without segments
+        oh, sh = run_gpu(_rows(x, lo, lo + 16))
+        assert torch.equal(oh, o[lo:lo + 16]) and torch.equal(sh, s[lo:lo + 16]), lo
+
+
+def test_pair_pass_against_oracle():
+    x = draw(32, 200, 4, 16, 128, "R1", 521, torch.bfloat16, **PAIR_KW)
+    o, s = run_gpu(x)
+    rows = [0, 1, 2, 3, 4, 7, 29, 31]   # full, empty, one chunk, ragged, one token, ...
+    check(x, o, s, rows=rows, label=f"pair pass rows={rows}")
+
+
+def test_pair_pass_nan_rows():
+    import gated_deltanet_prefill_gdr_amd as gdr
+    x = draw(32, 200, 4, 16, 128, "R1", 522, torch.bfloat16, **PAIR_KW)
+    dev = "cuda"
+    lengths = x.lengths.clone()
+    lengths[5] = 201                   # past L: a bad row
+    s0_row = x.s0_row.clone()
+    s0_row[9] = 3                      # past the state rows: a bad row
+    o, s = gdr.prefill(x.q.to(dev), x.k.to(dev), x.v.to(dev), x.g.to(dev), x.beta.to(dev),
+                       valid=lengths.to(dev), s0=x.s0.to(dev), s0_row=s0_row.to(dev))
+    ref_o, ref_s = run_gpu(x)
+    torch.cuda.synchronize()
+    for b in (5, 9):
+        assert torch.isnan(o[b].float()).all() and torch.isnan(s[b]).all(), b
+    good = [b for b in range(32) if b not in (5, 9)]
+    assert torch.equal(o[good], ref_o[good]) and torch.equal(s[good], ref_s[good])
+
+
 def test_split_continuation():
     x = draw(1, 320, 2, 4, 128, "R2", 511, torch.float32, s0_rows=1)
     o, s = run_gpu(x)
