@@ -1447,14 +1447,7 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   __syncthreads();   // read before the staging area is written
   const size_t hb = head_index(p, b, h) * p.P;
   if (jb_t == j + 1) p.plan[hb + jb_t] = PlanEntry{W, l2, trunc ? 1 : 0, 0};
-  if (trunc) {
-    if (j == 0) {   // segment 0 enters with s0 (or zero); kept in slot 0, where a rerun starts from
-      int srow = 0;
-      const bool bad = row_is_bad(p, b, srow);   // bad rows are never truncated; kept for clarity
-      const float* s0 = (p.s0 && !bad) ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
-      float* s = slot_ptr(p, b, h, 0);
-      for (int i = t; i < D * D; i += 64 * SegCfg<false>::NW) s[(i / D) * 2 * D + i % D] = s0 ? s0[i] : 0.f;
-    }
+  if (trunc) {   // (segment 0's entering state, s0 or zero, is copied into slot 0 by the combine)
     SegRun win{};   // chunks (j + 1) Ls - W .. (j + 1) Ls - 1
     win.c_end = (j + 1) * p.Ls;
     win.c_begin = win.c_end - w_own;
@@ -1479,7 +1472,7 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
 // Finalize (bf16 with P > 1): one workgroup per (row, value head). For a (row, head) that took the
 // truncated path it checks the certificate and, where it fails, counts the (row, head) in the status
 // word and runs it again in one piece from its entering state in slot 0 (s0 or zero, put there by the
-// transition pass), overwriting o and s_final. (Checking in the output pass's last workgroup per head
+// combine), overwriting o and s_final. (Checking in the output pass's last workgroup per head
 // instead would need device-scope fences around a per-head counter, which write back and invalidate
 // the compute die's L2 once per workgroup and cost far more than this launch.)
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanParams p) {
@@ -1504,7 +1497,8 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanP
     seg_body<true, false, false>(p, lds, b, h, all);
 }
 
-// Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero). One
+// Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero), which every
+// (row, head) gets in slot 0, the truncated ones too (then the kernel stops there). One
 // workgroup per (row, value head, 16-column slice); wave w computes key rows 32w .. 32w + 31
 // (tiles 2w, 2w + 1, plain row order) and the waves exchange the state each step as bf16
 // hi + lo operand pairs, so that with M = Mh + Ml the products Mh Sh + Mh Sl + Ml Sh keep
@@ -1543,9 +1537,7 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   const int slice = lam % kSlices16, h = (lam / kSlices16) % p.Hv, b = lam / (kSlices16 * p.Hv);
   int srow = 0;
   if (row_is_bad(p, b, srow)) return;   // the output pass writes NaN for this row
-  // A truncated (row, head): the transition pass has left the entering state of every segment in its
-  // slot (slot 0: s0 or zero).
-  if (p.trunc && p.plan[((size_t)b * p.Hv + h) * p.P + 1].trunc) return;
+  const bool truncated = p.trunc && p.plan[((size_t)b * p.Hv + h) * p.P + 1].trunc;
   const int col = 16 * slice + n16;
   float* slots = p.seg + ((size_t)b * p.Hv + h) * p.P * kSlotFloats;
   i32x4 rs = rsrc_words(slots, (uint32_t)(p.P * kSlotFloats * sizeof(float)));
@@ -1562,6 +1554,10 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
     for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+  // Slot 0 now holds s0 (or zero), where the output pass and a rerun start from (a copy: s_final may
+  // be s0 itself). A truncated (row, head) is done: the transition pass has left the entering state
+  // of every later segment in its slot.
+  if (truncated) return;
   // With no initial state S_1 = B_0, which is already in its slot: the chain starts at step 1.
   const int steps = p.P - 1, first = p.s0 ? 0 : 1;
   if (!p.s0 && steps > 0) {
