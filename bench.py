@@ -393,6 +393,8 @@ def main():
     ap.add_argument("--all-configs", action="store_true", help="time every named workload (a report)")
     ap.add_argument("--config", type=int, action="append", choices=[1, 2, 3, 4, 5],
                     help="with or instead of --all-configs: only these named workloads (repeatable)")
+    ap.add_argument("--no-exact", action="store_true",
+                    help="skip timing the call with truncated segment starts switched off (profiler runs)")
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed steps before the warm-up (0 for counter runs)")
     a = ap.parse_args()
@@ -450,12 +452,14 @@ def main():
     # call with truncated segment starts switched off (the exact composition), for context
     off = gdr.status_offset(desc)
     reruns = int(ws[off:off + 4].view(torch.int32).item()) if off is not None else None
-    gdr.set_truncation(False)
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    ms_exact, _ = run_timed(step, max(10, a.steps // 2))
-    gdr.set_truncation(True)
+    ms_exact = None
+    if not a.no_exact:
+        gdr.set_truncation(False)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        ms_exact, _ = run_timed(step, max(10, a.steps // 2))
+        gdr.set_truncation(True)
 
     units, nbytes, flops = algorithmic(B, L, Hk, Hv, 2, 0, True)
     if a.fused:   # raw bf16 projections instead of fp32 g, beta; plus the gate z
