@@ -147,11 +147,16 @@ __device__ __forceinline__ int block_kb(int blk) { return blk < 2 ? 0 : (blk - 2
 __device__ __forceinline__ int slot_col(int kb, int G, int j) { return 32 * kb + (j < 4 ? 4 * G + j : 12 + 4 * G + j); }
 
 // ---- 64 x 128 bf16 tiles staged in LDS by DMA (256-byte rows, no padding)
-// The 16-byte chunk q of row r sits at position q ^ f(r), f swapping the two 2-bit fields of
-// r mod 16. Sixteen consecutive rows of one chunk (the row operands) and four consecutive rows of
-// four consecutive chunks (the transposing reads) then both land on 16 distinct positions, i.e.
-// on all 64 banks once.
-__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// The 16-byte chunk q of row r sits at position q ^ f(r mod 16), f the table below (nibble r of the
+// constant; as bits: bit 3 of f = bit 0 of r, bit 2 = bit 1, bit 1 = bit 2 xor bit 3, bit 0 = bit 2).
+// Measured with the LDS bank-conflict counter over every tile read of the segment kernels, it leaves
+// the 16-byte row reads (sixteen consecutive rows of one chunk per lane group: the K, Q operands and
+// the Gram) free of bank conflicts, and the transposing 8-byte reads of K^T (four rows by four chunks
+// per 16 lanes) at two ways: every lane reads the same half of its chunk, so half of the bank slots
+// go unused, and no swizzle tried did better. (The earlier swap of the two 2-bit fields of r gave the
+// row reads two ways as well.) A table, because the compiler keeps the operand addresses in fewer
+// registers than for the bit form.
+__device__ __forceinline__ int swz_f(int row) { return (int)((0xd591e6a2f7b3c480ull >> (4 * (row & 15))) & 15); }
 __device__ __forceinline__ int swz(int row, int chunk16) { return row * 256 + 16 * (chunk16 ^ swz_f(row)); }
 
 // 16 bytes per lane from a range-checked buffer straight into LDS at lds + 16 * lane (out of
