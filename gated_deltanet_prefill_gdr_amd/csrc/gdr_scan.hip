@@ -540,22 +540,20 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // products. The q norm of token t,
     // rq_t = (|q_t|^2 + 1e-6)^-1/2 128^-1/2 (model page model.py, _l2norm), is a factor of both
     // output terms of row t (O = diag(rq) (diag(e^gamma) Q S + P' Delta)), so it is applied to the
-    // finished row. Its sum of squares comes from the same Q reads: the waves with kb2 = 0 (one per
-    // token tile) also form the tile's Q Q^T on MFMA and leave its diagonal in LDS.
+    // finished row. Its sum of squares is the diagonal of the token tile's Q Q^T, which waves 6 and 7
+    // (no P' block) form on MFMA, two tiles each, and leave in LDS.
     if constexpr (kOut) {
       const unsigned char* Qt = Bf + Cfg::kQ;
       // one block each for waves 0..5
       for (int blk = w; blk < w + 1 && blk < kFragBlocks; ++blk) {
         const int mt = block_tile(blk), kb2 = block_kb(blk);
-        f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)}, qq = f4_splat(0.f);
+        f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
-          if (kb2 == 0) qq = mfma(qf, qf, qq);   // Q Q^T of the token tile: its diagonal is |q_t|^2
         }
-        if (kb2 == 0) put_qnorms(mt, qq);
         const int t = 16 * mt + n16;
         const float gt = sc[kBfGam2 * C + t];
 #pragma unroll
@@ -570,6 +568,21 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
           }
         }
         *reinterpret_cast<bf16x8*>(lds + Cfg::kP + 1024 * blk + 16 * lane) = pack8(pt[0], pt[1]);
+      }
+      // waves 6 and 7, which form no P' block, form the Q Q^T of two token tiles each: its diagonal
+      // is |q_t|^2
+      if (w >= kFragBlocks) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int mt = 2 * (w - kFragBlocks) + h2;
+          f4 qq = f4_splat(0.f);
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+            qq = mfma(qf, qf, qq);
+          }
+          put_qnorms(mt, qq);
+        }
       }
     }
 
@@ -1098,18 +1111,16 @@ __device__ __forceinline__ void pair_body(const ScanParams& p, unsigned char* ld
     const float* sc = reinterpret_cast<const float*>(Rc + kScOff);
 
     // P' of this chunk for both heads: waves 0..5 form block w of K Q^T once (the key head's) and
-    // scale it by each head's gates; the waves of token tiles (kb2 = 0) also leave |q_t|^2 in LDS.
+    // scale it by each head's gates; waves 6 and 7 leave |q_t|^2 in LDS (two token tiles each).
     for (int blk = w; blk < w + 1 && blk < kFragBlocks; ++blk) {
       const int mt = block_tile(blk), kb2 = block_kb(blk);
-      f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)}, qq = f4_splat(0.f);
+      f4 pt[2] = {f4_splat(0.f), f4_splat(0.f)};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) pt[s2] = mfma(lds16(Kt + swz(32 * kb2 + 16 * s2 + n16, 4 * kb + G)), qf, pt[s2]);
-        if (kb2 == 0) qq = mfma(qf, qf, qq);
       }
-      if (kb2 == 0) put_qnorms(rqs, mt, qq);
       const int t = 16 * mt + n16;
 #pragma unroll
       for (int he = 0; he < 2; ++he) {
@@ -1128,6 +1139,19 @@ __device__ __forceinline__ void pair_body(const ScanParams& p, unsigned char* ld
           }
         }
         *reinterpret_cast<bf16x8*>(lds + Cfg::kP + he * kFragBlocks * 1024 + 1024 * blk + 16 * lane) = pack8(x2[0], x2[1]);
+      }
+    }
+    if (w >= kFragBlocks) {   // waves 6 and 7: the Q Q^T of two token tiles each, whose diagonal is |q_t|^2
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int mt = 2 * (w - kFragBlocks) + h2;
+        f4 qq = f4_splat(0.f);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 qf = lds16(Qt + swz(16 * mt + n16, 4 * kb + G));
+          qq = mfma(qf, qf, qq);
+        }
+        put_qnorms(rqs, mt, qq);
       }
     }
 
