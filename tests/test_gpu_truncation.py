@@ -35,12 +35,13 @@ def seg_plan(B, Hv, NC):
 
 
 def run(x, in_place=False):
-    """Prefill through the binding with a workspace of our own; returns o, s_final, the status word and
-    the per-(row, head) truncation flags (None without segments)."""
+    """Prefill through the binding with a workspace of our own, filled with NaN bytes first (so that
+    reading a slot no kernel of the call wrote spoils the results); returns o, s_final, the status word
+    and the per-(row, head) truncation flags (None without segments)."""
     d = to_dev(x)
     B, L, Hk, Hv, Dk, Dv = x.shape
     desc = gdr.make_desc(B, L, Hk, Hv, 0 if x.s0 is None else x.s0.shape[0], True, False)
-    ws = torch.zeros(gdr.workspace_size(desc), device="cuda", dtype=torch.uint8)
+    ws = torch.full((gdr.workspace_size(desc),), 0xFF, device="cuda", dtype=torch.uint8)
     kw = {}
     if in_place:
         kw["s_final"] = d["s0"]
@@ -75,7 +76,8 @@ def test_long_prefill_truncated_all_heads():
 
 
 def test_long_prefill_exact_all_heads():
-    """The same workload with truncation switched off: the exact segment transitions and combine."""
+    """The same workload with truncation switched off: the exact segment transitions, chained by the
+    output pass."""
     x = CONFIGS[5].draw()
     gdr.set_truncation(False)
     o, s, status, trunc = run(x)
@@ -89,6 +91,24 @@ def test_weak_decay_takes_exact_path():
     o, s, status, trunc = run(x)
     assert not trunc.any()
     check(x, o, s, "weak decay bf16 L=4096")
+
+
+def test_exact_path_from_shared_s0_rows():
+    """Weak decay (the exact path) with initial states: three rows start from two s0 rows, so the output
+    pass chains the segment maps from s0 itself."""
+    x = draw(3, 2048, 2, 4, 128, "R2", 817, torch.bfloat16, s0_rows=2, s0_row=[1, 0, 1])
+    o, s, status, trunc = run(x)
+    assert not trunc.any() and status == 0
+    check(x, o, s, "exact path from shared s0 rows")
+
+
+def test_exact_path_in_place():
+    """Weak decay with s_final written over s0: the transition pass copies s0 into slot 0 and the output
+    pass chains the segment maps from that copy."""
+    x = draw(2, 2048, 2, 4, 128, "R2", 818, torch.bfloat16, s0_rows=2)
+    o, s, status, trunc = run(x, in_place=True)
+    assert not trunc.any() and status == 0
+    check(x, o, s, "exact path in place")
 
 
 def test_mixed_heads():
@@ -124,7 +144,7 @@ def test_certificate_failure_reruns():
 
 
 def test_in_place_with_truncation_and_rerun():
-    """s_final written over s0: the rerun starts from the copy of s0 the combine keeps in slot 0."""
+    """s_final written over s0: the rerun starts from the copy of s0 the transition pass keeps in slot 0."""
     B, L, Hk, Hv = 2, 1024, 1, 2
     x = draw(B, L, Hk, Hv, 128, "LONG", 814, torch.bfloat16, s0_rows=B)
     gen = torch.Generator().manual_seed(8)
@@ -165,4 +185,25 @@ def test_fused_norm_with_truncation():
     err = np.abs(got - n_ref).max() / np.abs(n_ref).max()
     es = np.abs(s.double().cpu().numpy()[:, heads] - s_ref).max() / np.abs(s_ref).max()
     print(f"[parity] fused norm truncated: o {err:.3e} S {es:.3e}", flush=True)
+    assert err <= 2e-2 and es <= 2e-2
+
+
+def test_fused_norm_exact_path():
+    """The fused gated RMSNorm of the output pass on the exact path (segment maps chained), with s0."""
+    import oracle
+    from workloads import draw_layer
+    x = draw(1, 2048, 2, 8, 128, "R2", 819, torch.bfloat16, s0_rows=1)
+    y = draw_layer(1, x.q.shape[1], 1, 8, 1, 820, torch.bfloat16)
+    d = to_dev(x)
+    z, nw = y.x.cuda(), y.norm_w.cuda()
+    gdr.set_truncation(False)
+    o, s = gdr.prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], s0=d["s0"], norm=(z, nw, 1e-6))
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.gated_delta_rule(x.q.double().numpy(), x.k.double().numpy(), x.v.double().numpy(),
+                                           x.g.double().numpy(), x.beta.double().numpy(),
+                                           s0=x.s0.double().numpy())
+    n_ref = oracle.gated_rmsnorm(o_ref, y.x.double().numpy(), y.norm_w.double().numpy(), 1e-6)
+    err = np.abs(o.double().cpu().numpy() - n_ref).max() / np.abs(n_ref).max()
+    es = np.abs(s.double().cpu().numpy() - s_ref).max() / np.abs(s_ref).max()
+    print(f"[parity] fused norm exact: o {err:.3e} S {es:.3e}", flush=True)
     assert err <= 2e-2 and es <= 2e-2
