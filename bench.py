@@ -1,7 +1,7 @@
 """Benchmark of the chunked gated delta rule prefill on one MI355X.
 
-One step = one gdr_prefill call (all its kernels: the per-chunk prep, the segment transitions, the
-output scan, the truncation check) over the long-prefill workload: B = 1, 16 key / 32 value heads, Dk = Dv = 128, L = 16384,
+One step = one gdr_prefill call (all its kernels: the per-chunk prep, the segment transitions and
+their combine, the output scan) over the long-prefill workload: B = 1, 16 key / 32 value heads, Dk = Dv = 128, L = 16384,
 bf16 q/k/v, fp32 g/beta/state, zero initial state, final state returned. Inputs, outputs and
 the workspace are resident in HBM before the timed region. Before the W warm-up steps the step
 runs untimed for 0.3 s so that the GPU's clocks have settled. Prints one JSON line.
@@ -71,9 +71,10 @@ def kernel_bytes(name, B, L, Hk, Hv, esz, P, fused=False):
         return 2 * qk + gb + recs
     if name == "gdr_transition":
         return frac * (qk + vo + B * Hv * NC * rec_tb) + B * Hv * (P - 1) * slot
+    if name == "gdr_combine":
+        return B * Hv * (P - 1) * (slot * 3 // 2) + B * Hv * P * slot // 2
     if name == "gdr_scan":
-        # segments 1 .. P - 1 read their entering state from a slot (the truncated path)
-        return (2 * qk + 2 * vo + recs + B * Hv * D * D * 4 + (B * Hv * (P - 1) * slot // 2 if P > 1 else 0)
+        return (2 * qk + 2 * vo + recs + B * Hv * D * D * 4 + (B * Hv * P * slot // 2 if P > 1 else 0)
                 + (vo if fused else 0))
     if name == "gdr_gated_rmsnorm":   # o and z read, o written
         return 3 * vo

@@ -277,7 +277,6 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
     sp.plan = reinterpret_cast<gdr::PlanEntry*>(tr + gdr::kTruncHeader);
     sp.cert = reinterpret_cast<float*>(tr + gdr::kTruncHeader + n * sizeof(gdr::PlanEntry));
     sp.trunc = g_truncation ? 1 : 0;
-    sp.s0_in_slot = s0 && s_final == s0 ? 1 : 0;   // the output pass writes s_final over s0
   }
   if (fused_norm && bf16) {   // applied in the output pass's registers
     sp.z = fu->z;
@@ -287,6 +286,8 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
   if (plan.P > 1) {
     hipError_t e = timed(GDR_KERNEL_TRANSITION, s, [&] { return gdr::launch_transition(sp, s); });
     if (e != hipSuccess) return fail(GDR_EHIP, "transition launch: %s", hipGetErrorString(e));
+    e = timed(GDR_KERNEL_COMBINE, s, [&] { return gdr::launch_combine(sp, s); });
+    if (e != hipSuccess) return fail(GDR_EHIP, "combine launch: %s", hipGetErrorString(e));
   }
   hipError_t e = timed(GDR_KERNEL_SCAN, s, [&] { return gdr::launch_scan(sp, bf16, s); });
   if (e != hipSuccess) return fail(GDR_EHIP, "scan launch: %s", hipGetErrorString(e));

@@ -57,11 +57,10 @@ inline SegPlan seg_plan(int B, int Hv, int NC, bool bf16) {
 }
 
 // Segment states (bf16 with P > 1), after the records: per (row b, value head h) P slots of
-// 128 x 256 floats, slot (b*Hv + h)*P + j. Columns 0..127 of slot j >= 1: the local state
-// B_{j-1} that segment j-1 reaches from a zero state (exact path; the output pass chains them), or
-// the state entering segment j that the window before it reaches (truncated path); of slot 0: a
-// copy of s0 when s_final is s0 itself. Columns 128..255 of slot j: the transition M_j of segment j
-// (column k is the state segment j reaches from e_k with zero values), key index as row.
+// 128 x 256 floats, slot (b*Hv + h)*P + j. Columns 0..127 of slot j: first the local state
+// B_{j-1} that segment j-1 reaches from a zero state, then (after the combine) the true state
+// entering segment j. Columns 128..255 of slot j: the transition M_j of segment j (column k
+// is the state segment j reaches from e_k with zero values), key index as row.
 constexpr size_t kSlotFloats = size_t(kHeadDim) * 2 * kHeadDim;
 
 inline size_t records_bytes(int B, int Hv, int NC, size_t elem) {
@@ -81,8 +80,8 @@ inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 
 // S_j = Phi S(c_j - W) + S~_j, where S~_j is the state that the last W chunks before c_j reach from
 // zero and Phi is the product of those chunks' maps, ||Phi||_2 <= 2^{l2} with l2 the sum of g' log2 e
 // over the window (when every beta' there lies in [0, 2]). When a window with l2 <= -kTruncLog2 exists
-// for every boundary of a (row, head), the transition pass computes S~_j over that window alone and no
-// segment maps are chained; the output pass records ||S(c_j - W)||_F, and the finalize pass checks the bound
+// for every boundary of a (row, head), the transition pass computes S~_j over that window alone and the
+// combine is skipped; the output pass records ||S(c_j - W)||_F, and the finalize pass checks the bound
 // eps_j = 2^{l2_j} (||S(c_j - W_j)||_F + eps_{j-1}) <= 2^-24 ||S~_j||_F at every boundary, rerunning the
 // (row, head) without truncation where it fails.
 constexpr float kTruncLog2 = 40.f;     // a-priori window decay: 2^-40
@@ -153,7 +152,6 @@ struct ScanParams {
   float* cert;
   int32_t* status;
   int trunc;
-  int s0_in_slot;    // bf16 with P > 1 and s_final == s0: segment 0 and a rerun start from a copy in slot 0
   // fused gated RMSNorm of o (bf16 output pass; null z = plain o): o <- w o / rms(o) silu(z)
   const void* z;     // [B, L, Hv, 128], o's dtype
   const float* norm_w;   // [128]
@@ -224,9 +222,10 @@ hipError_t launch_gated_rmsnorm(const NormParams& p, int bf16, hipStream_t s);
 
 hipError_t launch_prep(const PrepParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int qkv_bf16, int beta_bf16, hipStream_t s);
-// bf16 with P > 1: segment transitions (all segments but the last), which the output pass of
-// launch_scan chains into the state entering every segment; launch_scan always runs last.
+// bf16 with P > 1: segment transitions (all segments but the last), then the combine that
+// turns them into the state entering every segment; launch_scan always runs last.
 hipError_t launch_transition(const ScanParams& p, hipStream_t s);
+hipError_t launch_combine(const ScanParams& p, hipStream_t s);
 hipError_t launch_scan(const ScanParams& p, int qkv_bf16, hipStream_t s);
 // bf16 with P > 1, after launch_scan: checks the truncation certificates of every (row, head) that
 // took the truncated path and reruns those whose bound fails from their entering state.

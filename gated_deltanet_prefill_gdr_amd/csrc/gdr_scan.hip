@@ -10,15 +10,15 @@
 // bf16: segment-parallel. The map from the state entering a run of chunks to the state leaving
 // it is affine, S -> M S + B, with M independent of the values. The chunks of each (row, head)
 // are cut into P segments; gdr_transition_bf16 runs every segment but the last from the
-// augmented start [0 | identity] (giving B_j and M_j), and gdr_scan_bf16 runs every segment
-// again from its true entering state, writing outputs (and, for the last one, the final state):
-// segment j's workgroup first chains S_{i+1} = M_i S_i + B_i for i < j from the state entering
-// segment 0. With P = 1 only gdr_scan_bf16 runs. Chunks wholly past a row's length (right pads:
-// beta' = g' = 0) are the identity map: the transitions skip them and the output pass gives them a
-// short loop of their own (O = diag(rq) Q S). Under strong decay a (row, head) takes truncated
-// segment starts instead (the transition pass runs only a short window before each boundary from
-// zero, leaving the entering state of the next segment, and gdr_finalize_bf16 checks the error bound
-// afterwards, rerunning the (row, head) exactly where it fails; see the truncation plan below).
+// augmented start [0 | identity] (giving B_j and M_j), gdr_combine chains
+// S_{j+1} = M_j S_j + B_j over the segments, and gdr_scan_bf16 runs every segment again from
+// its true entering state, writing outputs (and, for the last one, the final state). With
+// P = 1 only gdr_scan_bf16 runs. Chunks wholly past a row's length (right pads: beta' = g' = 0)
+// are the identity map: the transitions skip them and the output pass gives them a short loop of
+// their own (O = diag(rq) Q S). Under strong decay a (row, head) takes truncated segment starts
+// instead (the transition pass runs only a short window before each boundary from zero, the
+// combine returns at once, and gdr_finalize_bf16 checks the error bound afterwards, rerunning the
+// (row, head) exactly where it fails; see the truncation plan below).
 //
 // gdr_scan_f32: float32 inputs; one workgroup per (row, value head, 16-column slice), its four
 // waves splitting the slice's state by key blocks and walking all chunks together (fp32 MFMA, each
@@ -152,8 +152,6 @@ struct SegRun {
   int c_begin, c_end;
   int src_kind;         // 0: zero (identity for the transitions' M columns), 1: src (pitch 2D), 2: s0 row
   const float* src;     // the entering state in a segment slot, columns 0 .. 127
-  int chain;            // outputs, exact (row, head): segment maps 0 .. chain - 1 applied to it first,
-  const float* maps;    //   from the (row, head)'s slots (slot 0 here)
   bool last;            // outputs: the run ends the row, so it writes s_final
   int cert_chunk;       // outputs: at the top of this chunk (-1: none) each wave writes the sum of
   float* cert;          //   squares of its part of the state into cert[wave]
@@ -167,83 +165,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
   return x;
-}
-
-// The state entering segment `steps` of an exact (row, head), from the state entering segment 0 in
-// S: S <- M_i S + B_i for i = 0 .. steps - 1, with M_i in columns 128..255 of slot i and B_i in
-// columns 0..127 of slot i + 1 (left by the transition pass). Each wave of the output pass applies the
-// maps to its own 16 columns (the state layout of seg_body). Per step M_i (64 KiB; the 16-byte
-// chunk q of row r at position q ^ swz_m(r), so that the sixteen rows one operand read touches fall
-// on distinct banks) and the waves' columns of B_i (8 KiB each) are copied HBM->LDS by DMA. Both
-// factors are split into bf16 hi + lo, and Mh Sh + Mh Sl + Ml Sh keeps about 16 significant bits
-// more than bf16 alone.
-__device__ __forceinline__ int swz_m(int row) { return 4 * ((row >> 3) & 3) + (row & 3); }
-constexpr int kChainM = D * D * 4;   // LDS bytes of M_i; the waves' columns of B_i follow
-static_assert(2 * kChainM <= SegCfg<true>::kLds, "the chain's staging fits the output pass's LDS");
-__device__ __forceinline__ void chain_entry(const float* slots, int n_slots, unsigned char* lds, int steps,
-                                            f4 (&S)[4][2]) {
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n16 = lane & 15, G = lane >> 4;
-  const i32x4 rs = rsrc_words(slots, (uint32_t)(n_slots * kSlotFloats * sizeof(float)));
-  unsigned char* Ml = lds;
-  unsigned char* Bl = lds + kChainM + w * (D * 16 * 4);   // row r of this wave's 16 columns at 64 r
-  for (int i = 0; i < steps; ++i) {
-    const uint32_t mb = (uint32_t)i * kSlotFloats * 4, bb = (uint32_t)(i + 1) * kSlotFloats * 4;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {   // rows 16 w + 2 m, + 1 of M_i
-      const int r = 16 * w + 2 * m + (lane >> 5), qs = lane & 31;
-      dma16(rs, mb + ((uint32_t)r * 2 * D + D) * 4 + 16 * (qs ^ swz_m(r)), Ml + (16 * w + 2 * m) * 512);
-    }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {   // rows 16 m .. 16 m + 15 of this wave's columns of B_i
-      const int r = 16 * m + (lane >> 2);
-      dma16(rs, bb + ((uint32_t)r * 2 * D + 16 * w + 4 * (lane & 3)) * 4, Bl + 16 * m * 64);
-    }
-    wait_and_barrier<0>();
-    bf16x8 sh[4], sl[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sh[kb] = pack8(S[kb][0], S[kb][1]);
-      f4 r0, r1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r0[e] = S[kb][0][e] - (float)sh[kb][e];
-        r1[e] = S[kb][1][e] - (float)sh[kb][4 + e];
-      }
-      sl[kb] = pack8(r0, r1);
-    }
-    // output tile (kb, s2): its row m stands for key 32 kb + 8 (m >> 2) + 4 s2 + (m & 3), the state
-    // layout, so operand row n16 is that row of M_i
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int row = 32 * kb + 8 * (n16 >> 2) + 4 * s2 + (n16 & 3);
-        const unsigned char* mrow = Ml + row * 512;
-        f4 acc = f4_splat(0.f);
-#pragma unroll
-        for (int kb2 = 0; kb2 < 4; ++kb2) {
-          const int q = 8 * kb2 + 2 * G;   // keys 32 kb2 + 8 G .. + 7: chunks q, q + 1 of the row
-          const f4 m0 = *reinterpret_cast<const f4*>(mrow + 16 * (q ^ swz_m(row)));
-          const f4 m1 = *reinterpret_cast<const f4*>(mrow + 16 * ((q + 1) ^ swz_m(row)));
-          const bf16x8 mh = pack8(m0, m1);
-          f4 r0, r1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            r0[e] = m0[e] - (float)mh[e];
-            r1[e] = m1[e] - (float)mh[4 + e];
-          }
-          const bf16x8 ml = pack8(r0, r1);
-          acc = mfma(mh, sh[kb2], acc);
-          acc = mfma(mh, sl[kb2], acc);
-          acc = mfma(ml, sh[kb2], acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          S[kb][s2][e] = acc[e] + *reinterpret_cast<const float*>(Bl + (32 * kb + 8 * G + 4 * s2 + e) * 64 + 4 * n16);
-      }
-    lds_barrier();   // every wave is done with this step's LDS before the next step's copies
-  }
 }
 
 // kWin (with kOut): a window, the chunks c_begin .. c_end - 1 run from zero on the value columns in
@@ -389,10 +310,6 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 #pragma unroll
             for (int i = 0; i < 4; ++i)   // zero, or e_k for the identity columns
               S[sl][kb][s2][i] = (seg_col<kOut>(w, sl) + n16 - D == 32 * kb + 8 * G + 4 * s2 + i) ? 1.f : 0.f;
-    }
-    if constexpr (kOut && !kWin) {
-      static_assert(!kOut || NSL == 1, "one 16-column slice per wave");
-      if (run.chain > 0) chain_entry(run.maps, p.P, lds, run.chain, S[0]);
     }
   }
 
@@ -953,16 +870,8 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
   SegRun run{};
   run.c_begin = j * p.Ls;
   run.c_end = min(run.c_begin + p.Ls, p.NC);
-  const bool exact = p.P > 1 && j > 0 && !(p.trunc && p.plan[head_index(p, b, h) * p.P + j].trunc);
-  if (p.P > 1 && j > 0 && !exact) {   // truncated: the window's end state in slot j
-    run.src_kind = 1;
-    run.src = slot_ptr(p, b, h, j);
-  } else {   // the state entering segment 0 (s0 or zero, or its copy in slot 0), then the maps before j
-    run.src_kind = p.s0_in_slot ? 1 : 2;
-    run.src = p.s0_in_slot ? slot_ptr(p, b, h, 0) : nullptr;
-    run.chain = exact ? j : 0;
-    run.maps = exact ? slot_ptr(p, b, h, 0) : nullptr;
-  }
+  run.src_kind = p.P > 1 ? 1 : 2;   // with segments, the combine has put every entering state in its slot
+  run.src = p.P > 1 ? slot_ptr(p, b, h, j) : nullptr;
   run.last = j == p.P - 1;
   run.cert_chunk = -1;
   if (p.P > 1 && p.trunc && j + 1 < p.P) {
@@ -1440,12 +1349,12 @@ __global__ __launch_bounds__(64 * PairCfg::NW) void gdr_scan_bf16_pair(ScanParam
   PairRun run{};
   run.c_begin = j * p.Ls;
   run.c_end = min(run.c_begin + p.Ls, p.NC);
-  run.src_kind = 2;   // rows without segments only (P = 1): the entering state is s0 or zero
+  run.src_kind = p.P > 1 ? 1 : 2;   // with segments, the combine has put every entering state in its slot
   run.last = j == p.P - 1;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int h = 2 * hp + e;
-    run.src[e] = nullptr;
+    run.src[e] = p.P > 1 ? slot_ptr(p, b, h, j) : nullptr;
     run.cert_chunk[e] = -1;
     run.cert[e] = nullptr;
     if (p.P > 1 && p.trunc && j + 1 < p.P) {
@@ -1532,10 +1441,8 @@ __device__ __forceinline__ bool chunks_contract(const ScanParams& p, const PlanL
 // segment j's workgroup either runs the window before boundary j + 1 from zero on the value columns
 // alone (the output pass's layout, without outputs), leaving the entering state of segment j + 1 in its
 // slot and its norm in the certificate (truncated), or runs the whole segment on the augmented start
-// [0 | I], leaving B_j and M_j, which the output pass chains (exact). When s_final is s0 itself,
-// segment 0's workgroup also copies s0 into slot 0, where the output pass and a rerun then start
-// from. The grid is below 256 + B Hv workgroups, so the output pass's larger LDS (one workgroup per
-// CU) costs no parallelism.
+// [0 | I], leaving B_j and M_j for the combine (exact). The grid is below 256 + B Hv workgroups, so
+// the output pass's larger LDS (one workgroup per CU) costs no parallelism.
 static_assert(SegCfg<true>::kLds >= SegCfg<false>::kLds && SegCfg<true>::NW == SegCfg<false>::NW, "shared LDS");
 __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
@@ -1543,18 +1450,6 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   const int h = lam % p.Hv, j = (lam / p.Hv) % (p.P - 1), b = lam / (p.Hv * (p.P - 1));
   if (blockIdx.x == 0 && threadIdx.x == 0) *p.status = 0;   // read by the caller only
   const int t = threadIdx.x, jb_t = t + 1;
-  if (p.s0_in_slot && j == 0 && b < p.n_s0) {   // (s0_row is null when s_final is s0)
-    const f4* src = reinterpret_cast<const f4*>(p.s0 + ((size_t)b * p.Hv + h) * D * D);
-    f4* dst = reinterpret_cast<f4*>(slot_ptr(p, b, h, 0));
-    f4 x[D * D / 4 / (64 * SegCfg<false>::NW)];
-#pragma unroll
-    for (int i = 0; i < D * D / 4 / (64 * SegCfg<false>::NW); ++i) x[i] = src[t + 64 * SegCfg<false>::NW * i];
-#pragma unroll
-    for (int i = 0; i < D * D / 4 / (64 * SegCfg<false>::NW); ++i) {
-      const int e = t + 64 * SegCfg<false>::NW * i;   // f4 e: row e / 32, columns 4 (e % 32) ..
-      dst[(e / 32) * (2 * D / 4) + e % 32] = x[i];
-    }
-  }
   int W = 0;
   float l2 = 0.f;
   bool contract = true;
@@ -1576,7 +1471,7 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   __syncthreads();   // read before the staging area is written
   const size_t hb = head_index(p, b, h) * p.P;
   if (jb_t == j + 1) p.plan[hb + jb_t] = PlanEntry{W, l2, trunc ? 1 : 0, 0};
-  if (trunc) {
+  if (trunc) {   // (segment 0's entering state, s0 or zero, is copied into slot 0 by the combine)
     SegRun win{};   // chunks (j + 1) Ls - W .. (j + 1) Ls - 1
     win.c_end = (j + 1) * p.Ls;
     win.c_begin = win.c_end - w_own;
@@ -1600,8 +1495,8 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
 
 // Finalize (bf16 with P > 1): one workgroup per (row, value head). For a (row, head) that took the
 // truncated path it checks the certificate and, where it fails, counts the (row, head) in the status
-// word and runs it again in one piece from its entering state (s0 or zero, or the copy of s0 in slot 0
-// when s_final is s0 itself), overwriting o and s_final. (Checking in the output pass's last workgroup per head
+// word and runs it again in one piece from its entering state in slot 0 (s0 or zero, put there by the
+// combine), overwriting o and s_final. (Checking in the output pass's last workgroup per head
 // instead would need device-scope fences around a per-head counter, which write back and invalidate
 // the compute die's L2 once per workgroup and cost far more than this launch.)
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanParams p) {
@@ -1616,14 +1511,175 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanP
   SegRun all{};
   all.c_begin = 0;
   all.c_end = p.NC;
-  all.src_kind = p.s0_in_slot ? 1 : 2;
-  all.src = p.s0_in_slot ? slot_ptr(p, b, h, 0) : nullptr;
+  all.src_kind = 1;
+  all.src = slot_ptr(p, b, h, 0);
   all.last = true;
   all.cert_chunk = -1;
   if (p.z)
     seg_body<true, false, true>(p, lds, b, h, all);
   else
     seg_body<true, false, false>(p, lds, b, h, all);
+}
+
+// Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero), which every
+// (row, head) gets in slot 0, the truncated ones too (then the kernel stops there). One
+// workgroup per (row, value head, 16-column slice); wave w computes key rows 32w .. 32w + 31
+// (tiles 2w, 2w + 1, plain row order) and the waves exchange the state each step as bf16
+// hi + lo operand pairs, so that with M = Mh + Ml the products Mh Sh + Mh Sl + Ml Sh keep
+// about 16 significant bits more than bf16 alone.
+//
+// Step jj reads this wave's 32 rows of M_jj (all 128 keys) and of the slice of B_jj; neither
+// depends on the chained state, so each wave copies them HBM->LDS by DMA two steps ahead into a
+// ring of two slots of its own (no other wave reads them, so no barrier guards them). In a slot the
+// 16-byte chunk q of M row r sits at position q ^ (r & 15): the sixteen rows that one operand read
+// touches then fall on distinct banks.
+struct CombineSmem {
+  unsigned char m[2][4][32 * 512];   // [slot][wave]: 32 rows of M_jj, 512 bytes each
+  unsigned char bs[2][4][32 * 64];   // [slot][wave]: 32 rows of the B_jj slice, 64 bytes each
+  bf16x8 sx[2][2][4][64];            // [step parity][hi, lo][wave][lane]: the state exchange
+};
+// Vector-memory operations this wave issues after the loads of step jj's slot, when that slot is
+// waited for: the loads of step jj + 1 (kCombineLoads, if any) and the state stores of the steps
+// in between (kCombineStores each).
+constexpr int kCombineLoads = 16 + 2, kCombineStores = 8;
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N == 0 || N == 8 || N == 16 || N == 18 || N == 26 || N == 34, "extend the list of encodings");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if constexpr (N == 26) asm volatile("s_waitcnt vmcnt(26)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(34)" ::: "memory");
+}
+
+__global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
+  __shared__ __attribute__((aligned(16))) CombineSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15, G = lane >> 4;
+  const int lam = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = lam % kSlices16, h = (lam / kSlices16) % p.Hv, b = lam / (kSlices16 * p.Hv);
+  int srow = 0;
+  if (row_is_bad(p, b, srow)) return;   // the output pass writes NaN for this row
+  const bool truncated = p.trunc && p.plan[((size_t)b * p.Hv + h) * p.P + 1].trunc;
+  const int col = 16 * slice + n16;
+  float* slots = p.seg + ((size_t)b * p.Hv + h) * p.P * kSlotFloats;
+  i32x4 rs = rsrc_words(slots, (uint32_t)(p.P * kSlotFloats * sizeof(float)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rs[i]);   // uniform: keep it in SGPRs
+
+  f4 S[2];
+  const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)   // all loads first: the stores below may alias s0 as far as the
+#pragma unroll                      // compiler knows, which would otherwise serialise them
+    for (int i = 0; i < 4; ++i) S[s2][i] = s0 ? s0[(32 * w + 16 * s2 + 4 * G + i) * D + col] : 0.f;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+  // Slot 0 now holds s0 (or zero), where the output pass and a rerun start from (a copy: s_final may
+  // be s0 itself). A truncated (row, head) is done: the transition pass has left the entering state
+  // of every later segment in its slot.
+  if (truncated) return;
+  // With no initial state S_1 = B_0, which is already in its slot: the chain starts at step 1.
+  const int steps = p.P - 1, first = p.s0 ? 0 : 1;
+  if (!p.s0 && steps > 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[s2][i] = slots[kSlotFloats + (32 * w + 16 * s2 + 4 * G + i) * 2 * D + col];
+  }
+  // This wave's rows of M_jj (slot jj, columns 128..255; two rows per load) and of the B_jj slice
+  // (slot jj + 1, columns 16 slice ..; sixteen rows per load) into ring slot u.
+  auto issue = [&](int jj, int u) {
+    const uint32_t mbase = (uint32_t)jj * kSlotFloats * 4, bbase = (uint32_t)(jj + 1) * kSlotFloats * 4;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 2 * i + (lane >> 5), pos = lane & 31;
+      dma16(rs, mbase + ((uint32_t)(32 * w + r) * 2 * D + D) * 4 + 16 * (pos ^ (r & 15)), sm.m[u][w] + 2 * i * 512);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      dma16(rs, bbase + ((uint32_t)(32 * w + r) * 2 * D + 16 * slice + 4 * (lane & 3)) * 4, sm.bs[u][w] + 16 * i * 64);
+    }
+  };
+  // A wait the compiler sees: the state loads above are then known complete, so it places no wait
+  // for them inside the loop (where it would also stall on the slot loads in flight).
+  __builtin_amdgcn_s_waitcnt(0);
+  if (first < steps) issue(first, 0);
+  if (first + 1 < steps) issue(first + 1, 1);
+  for (int jj = first; jj < steps; ++jj) {
+    const int rel = jj - first, u = rel & 1;
+    const bool next = jj + 1 < steps;   // step jj + 1's loads were issued after this step's
+    if (rel == 0) {
+      if (next) wait_vm<kCombineLoads>(); else wait_vm<0>();
+    } else if (rel == 1) {
+      if (next) wait_vm<kCombineLoads + kCombineStores>(); else wait_vm<kCombineStores>();
+    } else {
+      if (next) wait_vm<kCombineLoads + 2 * kCombineStores>(); else wait_vm<2 * kCombineStores>();
+    }
+    bf16x8 mh[2][4], ml[2][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const unsigned char* mrow = sm.m[u][w] + (16 * s2 + n16) * 512;
+        const f4 m0 = *reinterpret_cast<const f4*>(mrow + 16 * ((8 * kb + G) ^ n16));
+        const f4 m1 = *reinterpret_cast<const f4*>(mrow + 16 * ((8 * kb + 4 + G) ^ n16));
+        mh[s2][kb] = pack8(m0, m1);
+        f4 r0, r1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r0[i] = m0[i] - (float)mh[s2][kb][i];
+          r1[i] = m1[i] - (float)mh[s2][kb][4 + i];
+        }
+        ml[s2][kb] = pack8(r0, r1);
+      }
+    f4 Bv[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Bv[s2][i] = *reinterpret_cast<const float*>(sm.bs[u][w] + (16 * s2 + 4 * G + i) * 64 + 4 * n16);
+    if (jj + 2 < steps) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave is done reading slot u
+      issue(jj + 2, u);
+    }
+    {
+      const bf16x8 hi = pack8(S[0], S[1]);
+      f4 r0, r1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r0[i] = S[0][i] - (float)hi[i];
+        r1[i] = S[1][i] - (float)hi[4 + i];
+      }
+      sm.sx[jj & 1][0][w][lane] = hi;
+      sm.sx[jj & 1][1][w][lane] = pack8(r0, r1);
+    }
+    lds_barrier();   // the state exchange is in LDS; the loads of later steps stay in flight
+    f4 acc[2] = {f4_splat(0.f), f4_splat(0.f)};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16x8 sh = sm.sx[jj & 1][0][kb][lane], sl = sm.sx[jj & 1][1][kb][lane];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        acc[s2] = mfma(mh[s2][kb], sh, acc[s2]);
+        acc[s2] = mfma(mh[s2][kb], sl, acc[s2]);
+        acc[s2] = mfma(ml[s2][kb], sh, acc[s2]);
+      }
+    }
+    // the state entering segment jj + 1, over B_jj in slot jj + 1: exactly kCombineStores stores
+    float* Bn = slots + (size_t)(jj + 1) * kSlotFloats;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      S[s2] = acc[s2] + Bv[s2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bn[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load into LDS may be in flight at the end
 }
 
 // ====================================================================== fp32 scan
@@ -1845,6 +1901,11 @@ __global__ __launch_bounds__(256) void gdr_scan_f32(ScanParams p) {
 
 hipError_t launch_transition(const ScanParams& p, hipStream_t s) {
   hipLaunchKernelGGL(gdr_transition_bf16, dim3(p.B * p.Hv * (p.P - 1)), dim3(64 * SegCfg<false>::NW), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const ScanParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(gdr_combine, dim3(p.B * p.Hv * kSlices16), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

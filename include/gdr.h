@@ -231,7 +231,7 @@ enum {
   GDR_KERNEL_PREP = 0,        /* per-chunk transform: norms, decays, T diag(beta), scores */
   GDR_KERNEL_SCAN = 1,        /* state scan writing o (and s_final) */
   GDR_KERNEL_TRANSITION = 2,  /* bf16 long sequences: per-segment state maps */
-  GDR_KERNEL_COMBINE = 3,     /* no longer launched (the output pass chains the segment maps): reads 0 */
+  GDR_KERNEL_COMBINE = 3,     /* bf16 long sequences: chains the segment maps */
   GDR_KERNEL_DECODE = 4,      /* gdr_decode */
   GDR_KERNEL_GATES = 5,       /* gdr_gates */
   GDR_KERNEL_CONV = 6,        /* gdr_conv_silu */

@@ -20,7 +20,6 @@
 // ------------------------------------------------------------------ stubs
 static std::vector<std::string> g_launches;
 static uintptr_t g_ws_lo = 0, g_ws_hi = 0;   // the workspace of the call under test
-static int g_s0_in_slot = -1;                 // what the last scan launch was told about s0
 
 static void fail_here(const char* what) {
   std::fprintf(stderr, "host_check FAILED: %s\n", what);
@@ -45,11 +44,9 @@ static void check_scan(const ScanParams& p) {
     in_ws(p.plan, size_t(p.B) * p.Hv * p.P * sizeof(PlanEntry), "plan entries");
     in_ws(p.cert, size_t(p.B) * p.Hv * p.P * kCertFloats * 4, "certificate parts");
   }
-  // segment 0 and a rerun start from a copy of s0 exactly when s_final overwrites s0
-  if (p.s0_in_slot != ((p.P > 1 && p.s0 && p.s_final == p.s0) ? 1 : 0)) fail_here("s0_in_slot");
-  g_s0_in_slot = p.s0_in_slot;
 }
 hipError_t launch_transition(const ScanParams& p, hipStream_t) { g_launches.push_back("transition"); check_scan(p); return hipSuccess; }
+hipError_t launch_combine(const ScanParams& p, hipStream_t) { g_launches.push_back("combine"); check_scan(p); return hipSuccess; }
 hipError_t launch_scan(const ScanParams& p, int, hipStream_t) { g_launches.push_back("scan"); check_scan(p); return hipSuccess; }
 hipError_t launch_finalize(const ScanParams& p, hipStream_t) { g_launches.push_back("finalize"); check_scan(p); return hipSuccess; }
 hipError_t launch_decode(const DecodeParams&, int, int, hipStream_t) { g_launches.push_back("decode"); return hipSuccess; }
@@ -138,8 +135,7 @@ int main() {
   {
     Call c(1, 16384, 16, 32, true, false, false);   // the long prefill: 8 segments
     expect(c.check() == GDR_OK, "long prefill valid");
-    expect(c.run() == GDR_OK && order() == "prep,transition,scan,finalize" && g_s0_in_slot == 0,
-           "long prefill launch order");
+    expect(c.run() == GDR_OK && order() == "prep,transition,combine,scan,finalize", "long prefill launch order");
     expect(gdr_prefill_status_offset(&c.d) != size_t(-1) && gdr_prefill_status_offset(&c.d) < c.ws_bytes, "status offset");
   }
   {
@@ -154,8 +150,7 @@ int main() {
   {
     Call c(1, 200, 1, 2, true, true, true);   // short bf16 with segments, in-place state
     c.sf = c.s0;
-    expect(c.run() == GDR_OK && order() == "prep,transition,scan,finalize" && g_s0_in_slot == 1,
-           "in place with segments");
+    expect(c.run() == GDR_OK && order() == "prep,transition,combine,scan,finalize", "in place with segments");
   }
   // timing: events recorded around each launch and read back
   {
@@ -200,7 +195,7 @@ int main() {
     g_ws_hi = g_ws_lo + (size_t(128) << 20);
     expect(gdr_prefill_noalloc(&s.d, s.q, s.k, s.v, static_cast<float*>(s.g), s.beta, nullptr, nullptr, nullptr, s.o,
                                static_cast<float*>(s.sf), nullptr) == GDR_OK &&
-               order() == "prep,transition,scan,finalize",
+               order() == "prep,transition,combine,scan,finalize",
            "noalloc small");
   }
   // decode and the layer steps: valid and invalid

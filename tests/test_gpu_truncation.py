@@ -76,8 +76,7 @@ def test_long_prefill_truncated_all_heads():
 
 
 def test_long_prefill_exact_all_heads():
-    """The same workload with truncation switched off: the exact segment transitions, chained by the
-    output pass."""
+    """The same workload with truncation switched off: the exact segment transitions and combine."""
     x = CONFIGS[5].draw()
     gdr.set_truncation(False)
     o, s, status, trunc = run(x)
@@ -94,8 +93,8 @@ def test_weak_decay_takes_exact_path():
 
 
 def test_exact_path_from_shared_s0_rows():
-    """Weak decay (the exact path) with initial states: three rows start from two s0 rows, so the output
-    pass chains the segment maps from s0 itself."""
+    """Weak decay (the exact path) with initial states: three rows start from two s0 rows, so the combine
+    chains the segment maps from s0 rows shared between batch rows."""
     x = draw(3, 2048, 2, 4, 128, "R2", 817, torch.bfloat16, s0_rows=2, s0_row=[1, 0, 1])
     o, s, status, trunc = run(x)
     assert not trunc.any() and status == 0
@@ -103,8 +102,8 @@ def test_exact_path_from_shared_s0_rows():
 
 
 def test_exact_path_in_place():
-    """Weak decay with s_final written over s0: the transition pass copies s0 into slot 0 and the output
-    pass chains the segment maps from that copy."""
+    """Weak decay with s_final written over s0: the combine chains the segment maps from the copy of s0
+    it keeps in slot 0, and the last segment overwrites s0 with the final state."""
     x = draw(2, 2048, 2, 4, 128, "R2", 818, torch.bfloat16, s0_rows=2)
     o, s, status, trunc = run(x, in_place=True)
     assert not trunc.any() and status == 0
@@ -144,7 +143,7 @@ def test_certificate_failure_reruns():
 
 
 def test_in_place_with_truncation_and_rerun():
-    """s_final written over s0: the rerun starts from the copy of s0 the transition pass keeps in slot 0."""
+    """s_final written over s0: the rerun starts from the copy of s0 the combine keeps in slot 0."""
     B, L, Hk, Hv = 2, 1024, 1, 2
     x = draw(B, L, Hk, Hv, 128, "LONG", 814, torch.bfloat16, s0_rows=B)
     gen = torch.Generator().manual_seed(8)
@@ -189,7 +188,7 @@ def test_fused_norm_with_truncation():
 
 
 def test_fused_norm_exact_path():
-    """The fused gated RMSNorm of the output pass on the exact path (segment maps chained), with s0."""
+    """The fused gated RMSNorm of the output pass on the exact path (segment maps combined), with s0."""
     import oracle
     from workloads import draw_layer
     x = draw(1, 2048, 2, 8, 128, "R2", 819, torch.bfloat16, s0_rows=1)
