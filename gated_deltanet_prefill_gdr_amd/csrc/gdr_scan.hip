@@ -870,8 +870,9 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParam
   SegRun run{};
   run.c_begin = j * p.Ls;
   run.c_end = min(run.c_begin + p.Ls, p.NC);
-  run.src_kind = p.P > 1 ? 1 : 2;   // with segments, the combine has put every entering state in its slot
-  run.src = p.P > 1 ? slot_ptr(p, b, h, j) : nullptr;
+  // with segments, the combine has put every entering state in its slot (the first one only with s0)
+  run.src_kind = p.P > 1 && (j > 0 || p.s0) ? 1 : 2;
+  run.src = run.src_kind == 1 ? slot_ptr(p, b, h, j) : nullptr;
   run.last = j == p.P - 1;
   run.cert_chunk = -1;
   if (p.P > 1 && p.trunc && j + 1 < p.P) {
@@ -1495,8 +1496,8 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
 
 // Finalize (bf16 with P > 1): one workgroup per (row, value head). For a (row, head) that took the
 // truncated path it checks the certificate and, where it fails, counts the (row, head) in the status
-// word and runs it again in one piece from its entering state in slot 0 (s0 or zero, put there by the
-// combine), overwriting o and s_final. (Checking in the output pass's last workgroup per head
+// word and runs it again in one piece from its entering state (the copy of s0 the combine put in
+// slot 0, or zero), overwriting o and s_final. (Checking in the output pass's last workgroup per head
 // instead would need device-scope fences around a per-head counter, which write back and invalidate
 // the compute die's L2 once per workgroup and cost far more than this launch.)
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanParams p) {
@@ -1511,8 +1512,8 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanP
   SegRun all{};
   all.c_begin = 0;
   all.c_end = p.NC;
-  all.src_kind = 1;
-  all.src = slot_ptr(p, b, h, 0);
+  all.src_kind = p.s0 ? 1 : 2;   // the copy of s0 in slot 0, or zero
+  all.src = p.s0 ? slot_ptr(p, b, h, 0) : nullptr;
   all.last = true;
   all.cert_chunk = -1;
   if (p.z)
@@ -1521,8 +1522,8 @@ __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_finalize_bf16(ScanP
     seg_body<true, false, false>(p, lds, b, h, all);
 }
 
-// Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero), which every
-// (row, head) gets in slot 0, the truncated ones too (then the kernel stops there). One
+// Combine: the state entering segment j + 1 is M_j S_j + B_j, S_0 = s0 (or zero). With s0, every
+// (row, head) gets a copy of it in slot 0, the truncated ones too (then the kernel stops there). One
 // workgroup per (row, value head, 16-column slice); wave w computes key rows 32w .. 32w + 31
 // (tiles 2w, 2w + 1, plain row order) and the waves exchange the state each step as bf16
 // hi + lo operand pairs, so that with M = Mh + Ml the products Mh Sh + Mh Sl + Ml Sh keep
@@ -1568,19 +1569,21 @@ __global__ __launch_bounds__(256) void gdr_combine(ScanParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) rs[i] = __builtin_amdgcn_readfirstlane(rs[i]);   // uniform: keep it in SGPRs
 
-  f4 S[2];
-  const float* s0 = p.s0 ? p.s0 + ((size_t)srow * p.Hv + h) * D * D : nullptr;
+  f4 S[2] = {f4_splat(0.f), f4_splat(0.f)};
+  if (p.s0) {
+    const float* s0 = p.s0 + ((size_t)srow * p.Hv + h) * D * D;
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)   // all loads first: the stores below may alias s0 as far as the
+    for (int s2 = 0; s2 < 2; ++s2)   // all loads first: the stores below may alias s0 as far as the
 #pragma unroll                      // compiler knows, which would otherwise serialise them
-    for (int i = 0; i < 4; ++i) S[s2][i] = s0 ? s0[(32 * w + 16 * s2 + 4 * G + i) * D + col] : 0.f;
+      for (int i = 0; i < 4; ++i) S[s2][i] = s0[(32 * w + 16 * s2 + 4 * G + i) * D + col];
 #pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
-  // Slot 0 now holds s0 (or zero), where the output pass and a rerun start from (a copy: s_final may
-  // be s0 itself). A truncated (row, head) is done: the transition pass has left the entering state
-  // of every later segment in its slot.
+      for (int i = 0; i < 4; ++i) slots[(32 * w + 16 * s2 + 4 * G + i) * 2 * D + col] = S[s2][i];
+  }
+  // Slot 0 now holds s0, where the output pass and a rerun start from (a copy: s_final may be s0
+  // itself); without s0 they start from zero and slot 0 is not read. A truncated (row, head) is done:
+  // the transition pass has left the entering state of every later segment in its slot.
   if (truncated) return;
   // With no initial state S_1 = B_0, which is already in its slot: the chain starts at step 1.
   const int steps = p.P - 1, first = p.s0 ? 0 : 1;
