@@ -323,23 +323,28 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       const unsigned char* Bf = lds + (c & 1) * Cfg::kBuf;
       const unsigned char* Kt = Bf + Cfg::kK;
       const float* sc = reinterpret_cast<const float*>(Bf + Cfg::kRec + kScOff);
-      bf16x8 Sop[NSL][4];
-#pragma unroll
-      for (int sl = 0; sl < NSL; ++sl)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
-      // X = K S, R = V - diag(a) X, Delta = Tb R (lower-triangular blocks only)
+      // X = K S, R = V - diag(a) X, Delta = Tb R (lower-triangular blocks only); the window starts
+      // from zero, so its first chunk has X = 0 (uniform branch)
+      const bool first = c == c_begin;
       f4 X[NSL][4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = f4_splat(0.f);
+      if (!first) {
+        bf16x8 Sop[NSL][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 kf = lds16(Kt + swz(16 * mt + n16, 4 * kb + G));
+        for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-          for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = mfma(kf, Sop[sl][kb], X[sl][mt]);
-        }
+          for (int kb = 0; kb < 4; ++kb) Sop[sl][kb] = pack8(S[sl][kb][0], S[sl][kb][1]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const bf16x8 kf = lds16(Kt + swz(16 * mt + n16, 4 * kb + G));
+#pragma unroll
+            for (int sl = 0; sl < NSL; ++sl) X[sl][mt] = mfma(kf, Sop[sl][kb], X[sl][mt]);
+          }
       }
       bf16x8 Rop[NSL][2];
 #pragma unroll
@@ -373,8 +378,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
         Ddop[sl][0] = pack8(Dl[sl][0], Dl[sl][1]);
         Ddop[sl][1] = pack8(Dl[sl][2], Dl[sl][3]);
       }
-      // S <- e^{gamma_63} S + K^T diag(d) Delta
-      const float egc = __builtin_amdgcn_exp2f(sc[kBfGam2 * C + C - 1]);   // e^{gamma_63}
+      // S <- e^{gamma_63} S + K^T diag(d) Delta (S = 0 before the first chunk)
+      const float egc = first ? 0.f : __builtin_amdgcn_exp2f(sc[kBfGam2 * C + C - 1]);   // e^{gamma_63}
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
