@@ -142,7 +142,9 @@ __global__ __launch_bounds__(256) void gdr_conv_silu_kernel(ConvParams p) {
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(dst + (size_t)b * p.L * dpitch, (uint32_t)p.L * drow);
   const uint32_t dcoff = (uint32_t)dc * sizeof(T);
 
-  constexpr int U = 4;   // tokens loaded together
+  // tokens loaded together: eight keep 64 bytes per thread in flight (110 -> 104 us at L = 16384,
+  // Cm = 8192, also when the gate and norm kernels run around it; sixteen gain nothing more)
+  constexpr int U = 8;
 #pragma unroll 1
   for (int tt = 0; tt < kConvTile; tt += U) {
     Vec4<T> raw[U];
