@@ -143,6 +143,25 @@ def test_desc_errors(field, value, status, msg):
     assert st == status and msg in err
 
 
+def test_size_limits():
+    """Shapes past the launch-grid limits or the 32-bit buffer offsets of one batch row are refused on the
+    host with GDR_EUNSUPPORTED (and the workspace query raises), before any launch; the longest row
+    that fits is accepted."""
+    cases = [({"B": 70000}, "grid limits"),                              # B > 65535
+             ({"B": 40000, "L": 64 * 60000, "Hv": 2}, "grid limits"),    # B Hv ceil(L/64) >= 2^31
+             ({"B": 1, "L": 1 << 18, "Hv": 32}, "4 GiB")]                # (L + 128) Hv 512 bytes >= 4 GiB
+    for fields, msg in cases:
+        c = Call(B=1, L=130, Hk=1, Hv=2, s0=False)
+        for k, v in fields.items():
+            setattr(c.desc, k, v)
+        assert c.check() == EUNSUP and msg in gdr.last_error(), (fields, gdr.last_error())
+        assert c.prefill() == EUNSUP
+        with pytest.raises(gdr.GdrError, match=msg):
+            gdr.workspace_size(c.desc)
+    c = Call(B=1, L=(1 << 18) - 256, Hk=1, Hv=32, s0=False)   # (L + 128) Hv 512 bytes just below 4 GiB
+    assert c.check() == OK, gdr.last_error()
+
+
 def test_beta_dtype_mismatch():
     def m(c):
         c.desc.qkv_dtype = gdr.GDR_F32

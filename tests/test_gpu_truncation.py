@@ -92,6 +92,19 @@ def test_weak_decay_takes_exact_path():
     check(x, o, s, "weak decay bf16 L=4096")
 
 
+@pytest.mark.parametrize("regime,seed", [("LONG", 821), ("R2", 822)])
+def test_long_sequence_many_segments(regime, seed):
+    """L = 65536 on two value heads: 128 segments of 8 chunks, far past the benchmark shapes in sequence
+    length and segment count. LONG: every boundary takes a window; R2 (weak decay): the exact path, whose
+    combine chains 127 segment maps. Every output and the final states against the oracle."""
+    x = draw(1, 65536, 1, 2, 128, regime, seed, torch.bfloat16)
+    assert seg_plan(1, 2, 1024) == (128, 8)
+    o, s, status, trunc = run(x)
+    assert status == 0
+    assert trunc.all() if regime == "LONG" else not trunc.any(), trunc
+    check(x, o, s, f"L=65536, 128 segments, {regime}")
+
+
 def test_exact_path_from_shared_s0_rows():
     """Weak decay (the exact path) with initial states: three rows start from two s0 rows, so the combine
     chains the segment maps from s0 rows shared between batch rows."""
