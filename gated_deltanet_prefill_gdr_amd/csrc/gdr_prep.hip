@@ -96,6 +96,31 @@ __device__ __forceinline__ void store_acc(float* tile, int n16, int G, const f4&
 __device__ __forceinline__ const float* blk(const float* m, int I, int J) { return m + kBlk * (I * (I + 1) / 2 + J); }
 __device__ __forceinline__ float* blk(float* m, int I, int J) { return m + kBlk * (I * (I + 1) / 2 + J); }
 
+// The same products on bf16 MFMA (bf16 sequences): a 16x16x16 bf16 product takes, per lane, the four
+// k values 4G .. 4G + 3 that mma_acc's four fp32 steps take one at a time, so the operands keep their
+// layouts. Each fp32 factor is split into bf16 hi + lo, and Ah Bh + Ah Bl + Al Bh drops only Al Bl
+// (about 2^-16 of the product), far below the bf16 rounding the record applies to T afterwards; the
+// fp32 products run at 1/16 of the bf16 rate.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+struct Split4 {
+  s16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(const f4& x) {
+  Split4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 h = (__bf16)x[e];
+    r.hi[e] = __builtin_bit_cast(short, h);
+    r.lo[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)h));
+  }
+  return r;
+}
+__device__ __forceinline__ void mma_split(f4& acc, const Split4& a, const Split4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+}
+
 // The lower 16x16 tiles (I, J) of K K^T that wave W forms and scales into A: its diagonal tile
 // (3 - W, 3 - W) first (the row norms come from its diagonal), then 2, 2, 1, 1 of the six tiles
 // below the diagonal, so that the Gram and A work is spread evenly over the four waves.
@@ -698,40 +723,44 @@ __global__ __launch_bounds__(64 * kPrepWaves, kOne ? 3 : 2) void gdr_prep_wave(P
     }
     wave_lds_fence();
 
-    // ---- off-diagonal blocks. A_20, A_21, A_30, A_31 are read before they are overwritten.
-    const f4 a21 = tile_row(blk(M, 2, 1), n16, G), a31 = tile_row(blk(M, 3, 1), n16, G);
+    // ---- off-diagonal blocks (split bf16 products). A_20, A_21, A_30, A_31 are read before they are
+    //      overwritten.
+    const Split4 a21 = split4(tile_row(blk(M, 2, 1), n16, G)), a31 = split4(tile_row(blk(M, 3, 1), n16, G));
     f4 pre0 = f4_splat(0.f), pre1 = f4_splat(0.f);
     {
-      const f4 t00 = tile_acc(blk(M, 0, 0), n16, G);
-      mma_lds_acc(pre0, blk(M, 2, 0), n16, G, t00);   // A_20 T_00
-      mma_lds_acc(pre1, blk(M, 3, 0), n16, G, t00);   // A_30 T_00
+      const Split4 t00 = split4(tile_acc(blk(M, 0, 0), n16, G));
+      mma_split(pre0, split4(tile_row(blk(M, 2, 0), n16, G)), t00);   // A_20 T_00
+      mma_split(pre1, split4(tile_row(blk(M, 3, 0), n16, G)), t00);   // A_30 T_00
     }
     // within each 32-row half: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int I = 2 * hf + 1, J = 2 * hf;
       f4 x = f4_splat(0.f), y = f4_splat(0.f);
-      mma_lds_acc(x, blk(M, I, J), n16, G, tile_acc(blk(M, J, J), n16, G));
-      mma_lds_acc(y, blk(M, I, I), n16, G, x);
+      mma_split(x, split4(tile_row(blk(M, I, J), n16, G)), split4(tile_acc(blk(M, J, J), n16, G)));
+      mma_split(y, split4(tile_row(blk(M, I, I), n16, G)), split4(x));
       store_acc(blk(M, I, J), n16, G, -y);
     }
     wave_lds_fence();
     // across the halves: Z_IJ = A_I0 T_0J + A_I1 T_1J (T_01 = 0), T_2J = -T_22 Z_2J,
     // T_3J = -(T_32 Z_2J + T_33 Z_3J), J = 0, 1
     {
-      const f4 t10 = tile_acc(blk(M, 1, 0), n16, G), t11 = tile_acc(blk(M, 1, 1), n16, G);
+      const Split4 t10 = split4(tile_acc(blk(M, 1, 0), n16, G)), t11 = split4(tile_acc(blk(M, 1, 1), n16, G));
       f4 z20 = pre0, z30 = pre1, z21 = f4_splat(0.f), z31 = f4_splat(0.f);
-      mma_acc(z20, a21, t10);
-      mma_acc(z30, a31, t10);
-      mma_acc(z21, a21, t11);
-      mma_acc(z31, a31, t11);
+      mma_split(z20, a21, t10);
+      mma_split(z30, a31, t10);
+      mma_split(z21, a21, t11);
+      mma_split(z31, a31, t11);
+      const Split4 r22 = split4(tile_row(blk(M, 2, 2), n16, G)), r32 = split4(tile_row(blk(M, 3, 2), n16, G)),
+                   r33 = split4(tile_row(blk(M, 3, 3), n16, G));
+      const Split4 s20 = split4(z20), s21 = split4(z21), s30 = split4(z30), s31 = split4(z31);
       f4 o20 = f4_splat(0.f), o21 = f4_splat(0.f), o30 = f4_splat(0.f), o31 = f4_splat(0.f);
-      mma_lds_acc(o20, blk(M, 2, 2), n16, G, z20);
-      mma_lds_acc(o21, blk(M, 2, 2), n16, G, z21);
-      mma_lds_acc(o30, blk(M, 3, 2), n16, G, z20);
-      mma_lds_acc(o30, blk(M, 3, 3), n16, G, z30);
-      mma_lds_acc(o31, blk(M, 3, 2), n16, G, z21);
-      mma_lds_acc(o31, blk(M, 3, 3), n16, G, z31);
+      mma_split(o20, r22, s20);
+      mma_split(o21, r22, s21);
+      mma_split(o30, r32, s20);
+      mma_split(o30, r33, s30);
+      mma_split(o31, r32, s21);
+      mma_split(o31, r33, s31);
       store_acc(blk(M, 2, 0), n16, G, -o20);
       store_acc(blk(M, 2, 1), n16, G, -o21);
       store_acc(blk(M, 3, 0), n16, G, -o30);
