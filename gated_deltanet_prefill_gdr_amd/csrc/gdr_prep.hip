@@ -98,21 +98,33 @@ __device__ __forceinline__ float* blk(float* m, int I, int J) { return m + kBlk 
 
 // The same products on bf16 MFMA (bf16 sequences): a 16x16x16 bf16 product takes, per lane, the four
 // k values 4G .. 4G + 3 that mma_acc's four fp32 steps take one at a time, so the operands keep their
-// layouts. Each fp32 factor is split into bf16 hi + lo, and Ah Bh + Ah Bl + Al Bh drops only Al Bl
-// (about 2^-16 of the product), far below the bf16 rounding the record applies to T afterwards; the
-// fp32 products run at 1/16 of the bf16 rate.
+// layouts. Each fp32 factor is split into bf16 hi + lo: hi is x with its low 16 bits cleared (exact as
+// a float, and its bf16 pattern is the upper half of x), lo = x - hi (exact) rounded to bf16. Then
+// Ah Bh + Ah Bl + Al Bh drops only Al Bl and lo's rounding (about 2^-15 of the product), far below the
+// bf16 rounding the record applies to T afterwards; the fp32 products run at 1/16 of the bf16 rate.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 struct Split4 {
   s16x4 hi, lo;
 };
 __device__ __forceinline__ Split4 split4(const f4& x) {
-  Split4 r;
+  uint32_t u[4];
+  float l[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const __bf16 h = (__bf16)x[e];
-    r.hi[e] = __builtin_bit_cast(short, h);
-    r.lo[e] = __builtin_bit_cast(short, (__bf16)(x[e] - (float)h));
+    const float xe = x[e];   // a scalar copy: bit_cast of the vector element x[e] itself compiled to element 0
+    u[e] = __builtin_bit_cast(uint32_t, xe);
+    l[e] = x[e] - __builtin_bit_cast(float, u[e] & 0xFFFF0000u);
   }
+  Split4 r;
+  // upper halves of u[0], u[1] (and u[2], u[3]) as one word each: bytes 2, 3 of the low operand, then
+  // bytes 2, 3 of the high one
+  r.hi = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                                         __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)});
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 l01 = __builtin_convertvector(f2{l[0], l[1]}, bf16x2), l23 = __builtin_convertvector(f2{l[2], l[3]}, bf16x2);
+  r.lo = __builtin_bit_cast(s16x4, u32x2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)});
   return r;
 }
 __device__ __forceinline__ void mma_split(f4& acc, const Split4& a, const Split4& b) {
