@@ -1355,12 +1355,13 @@ __global__ __launch_bounds__(64 * PairCfg::NW) void gdr_scan_bf16_pair(ScanParam
   PairRun run{};
   run.c_begin = j * p.Ls;
   run.c_end = min(run.c_begin + p.Ls, p.NC);
-  run.src_kind = p.P > 1 ? 1 : 2;   // with segments, the combine has put every entering state in its slot
+  // with segments, the combine has put every entering state in its slot (the first one only with s0)
+  run.src_kind = p.P > 1 && (j > 0 || p.s0) ? 1 : 2;
   run.last = j == p.P - 1;
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int h = 2 * hp + e;
-    run.src[e] = p.P > 1 ? slot_ptr(p, b, h, j) : nullptr;
+    run.src[e] = run.src_kind == 1 ? slot_ptr(p, b, h, j) : nullptr;
     run.cert_chunk[e] = -1;
     run.cert[e] = nullptr;
     if (p.P > 1 && p.trunc && j + 1 < p.P) {
