@@ -33,7 +33,8 @@
 //   4. T of the four 16x16 diagonal blocks by forward substitution, one lane per column, all in
 //      registers (one wave per value head), written over A;
 //   5. off-diagonal blocks by the 2x2 block rule T_BA = -T_BB A_BA T_AA, first within each
-//      32-row half (T_10, T_32), then across the halves, on fp32 MFMA, each written over A;
+//      32-row half (T_10, T_32), then across the halves, on fp32 MFMA (gdr_prep_wave: on bf16 MFMA
+//      with split factors, mma_split), each written over A;
 //   6. Tb = T diag(beta') gathered into operand order.
 #include <algorithm>
 

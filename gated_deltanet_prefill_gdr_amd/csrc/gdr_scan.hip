@@ -1,7 +1,9 @@
 // Inter-chunk state scan of the chunked gated delta rule (gfx950).
 //
-// Per chunk (S = state entering the chunk, [Dk, Dv], fp32; a, c, d, e^{gamma_63}, Tb and P from
-// the chunk record written by the prep kernel; K, Q the raw chunk rows):
+// Per chunk (S = state entering the chunk, [Dk, Dv], fp32; a, c, d, e^{gamma_63} and Tb from the
+// chunk record written by the prep kernel; P, the decayed and masked scores, from the record too
+// (fp32) or formed by the output pass from the staged Q and K tiles as P' (bf16); K, Q the raw
+// chunk rows):
 //   X = K S,  R = V - diag(a) X,  Delta = Tb R,  O = diag(c) Q S + P Delta,
 //   S <- e^{gamma_63} S + K^T diag(d) Delta
 // which is the per-token recurrence of the kernel-test page (r15_kernel_test.py, function
@@ -521,9 +523,9 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
       if (lane == 0) run.cert[w] = ss;
     }
     // The next chunk's staging. The output pass spreads it over the iteration: K here, Q after the
-    // P formation, V after X, the record before the P barrier. Issued all at once, these loads
+    // P' formation, V after X, the record before the P' barrier. Issued all at once, these loads
     // hold up this chunk's first LDS reads and products (about a tenth of the pass at the long
-    // prefill). The transitions, which form no P, issue it all here.
+    // prefill). The transitions, which form no P', issue it all here.
     if (c + 1 < c_mid)
       issue(c + 1, kOut ? kStK : kStAll);
     else if (kOut && c + 1 < c_end && fuse)
@@ -660,7 +662,7 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // consecutive columns 4G .. 4G + 3 of one token, stored as one 8-byte write.
     if constexpr (kOut) {
       if (stage_next) issue(c + 1, kStRec);
-      lds_barrier();   // P is complete
+      lds_barrier();   // P' is complete
       const unsigned char* Qt = Bf + Cfg::kQ;
       bf16x8 Dop[NSL][2];
 #pragma unroll
