@@ -278,6 +278,11 @@ gdr_status gdr_prefill_ex(const gdr_desc* d, const void* q, const void* k, const
     sp.cert = reinterpret_cast<float*>(tr + gdr::kTruncHeader + n * sizeof(gdr::PlanEntry));
     sp.trunc = g_truncation ? 1 : 0;
   }
+  if (bf16 && lengths && plan.P == 1 && NC > 0)   // rows longest first (written with the chunk list)
+    sp.row_order = reinterpret_cast<const int32_t*>(static_cast<char*>(ws) +
+                                                    gdr::records_bytes(d->B, d->Hv, NC, dtype_size(d->qkv_dtype)) +
+                                                    gdr::seg_bytes(d->B, d->Hv, NC, dtype_size(d->qkv_dtype))) +
+                   1 + size_t(d->B) * NC;
   if (fused_norm && bf16) {   // applied in the output pass's registers
     sp.z = fu->z;
     sp.norm_w = fu->norm_w;

@@ -73,8 +73,9 @@ inline size_t seg_bytes(int B, int Hv, int NC, size_t elem) {
 }
 
 // Chunk list (bf16, after the segment states): the chunks that hold valid tokens when lengths are
-// given, row-major: int32 count U, then U entries b NC + c.
-inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 4 * (1 + size_t(B) * NC) : 0; }
+// given, row-major: int32 count U, then U entries b NC + c (room for B NC); then the B rows ordered
+// by their number of such chunks, longest first (ties in any order).
+inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 4 * (1 + size_t(B) * NC + B) : 0; }
 
 // Truncated segment starts (bf16 with P > 1). The state entering segment j >= 1 is
 // S_j = Phi S(c_j - W) + S~_j, where S~_j is the state that the last W chunks before c_j reach from
@@ -130,7 +131,7 @@ struct PrepParams {
   const void* a_raw;
   const float* A_log;     // [Hv]
   const float* dt_bias;   // [Hv]
-  int32_t* chunk_list;     // bf16 with lengths: the chunk list (written by the prep launch), else null
+  int32_t* chunk_list;     // bf16 with lengths: the chunk list and row order (written by the prep launch), else null
 };
 
 struct ScanParams {
@@ -152,6 +153,9 @@ struct ScanParams {
   float* cert;
   int32_t* status;
   int trunc;
+  // bf16 without segments, with lengths: the rows by number of chunks, longest first (the chunk
+  // list's row order); the output pass takes its rows in this order (null: row index order)
+  const int32_t* row_order;
   // fused gated RMSNorm of o (bf16 output pass; null z = plain o): o <- w o / rms(o) silu(z)
   const void* z;     // [B, L, Hv, 128], o's dtype
   const float* norm_w;   // [128]

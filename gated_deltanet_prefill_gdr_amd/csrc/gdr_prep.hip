@@ -559,17 +559,18 @@ __device__ __forceinline__ void store_gates(float* gam, float* bet, float gv, fl
 // list[1 + u] = b NC + c. Rows whose length is out of range count all their chunks (they are
 // computed in full; the output pass turns them into NaN). One workgroup: rows in blocks of 256,
 // each with a workgroup-wide inclusive prefix sum of the rows' chunk counts.
+__device__ __forceinline__ int row_chunks(const int32_t* lengths, int b, int L, int NC) {
+  const int len = lengths[b];
+  return (len < 0 || len > L) ? NC : (len + C - 1) / C;
+}
 __global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, int B, int L, int NC, int32_t* list) {
   __shared__ int sc[256];
   const int tid = threadIdx.x;
-  int base = 0;
+  int base = 0, nc_first = 0;   // this thread's row of the first block (all rows when B <= 256)
   for (int b0 = 0; b0 < B; b0 += 256) {
     const int b = b0 + tid;
-    int nc = 0;
-    if (b < B) {
-      const int len = lengths[b];
-      nc = (len < 0 || len > L) ? NC : (len + C - 1) / C;
-    }
+    const int nc = b < B ? row_chunks(lengths, b, L, NC) : 0;
+    if (b0 == 0) nc_first = nc;
     sc[tid] = nc;
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
@@ -584,6 +585,27 @@ __global__ __launch_bounds__(256) void gdr_chunk_list(const int32_t* lengths, in
     __syncthreads();
   }
   if (tid == 0) list[0] = base;
+
+  // The rows by number of chunks, longest first, after the list's B NC entries: a counting sort on
+  // key 255 - min(chunks, 255) (so that longer rows come first). Equal keys land in the order of the
+  // LDS atomics, which decides only which workgroup of the output pass takes a row.
+  int32_t* order = list + 1 + (size_t)B * NC;
+  auto key = [&](int b) { return 255 - min(b < 256 ? nc_first : row_chunks(lengths, b, L, NC), 255); };
+  sc[tid] = 0;
+  __syncthreads();
+  for (int b = tid; b < B; b += 256) atomicAdd(&sc[key(b)], 1);
+  __syncthreads();
+  const int cnt = sc[tid];
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {   // inclusive prefix sum of the counts
+    const int y = tid >= d ? sc[tid - d] : 0;
+    __syncthreads();
+    sc[tid] += y;
+    __syncthreads();
+  }
+  sc[tid] -= cnt;   // exclusive: the first position of key tid
+  __syncthreads();
+  for (int b = tid; b < B; b += 256) order[atomicAdd(&sc[key(b)], 1)] = b;
 }
 
 // ---- bf16 prep, one wave per value head (gdr_prep_wave)

@@ -872,8 +872,12 @@ __device__ __forceinline__ int certificate_status(const ScanParams& p, size_t hb
 template <bool kFuse>
 __global__ __launch_bounds__(64 * SegCfg<true>::NW) void gdr_scan_bf16(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[SegCfg<true>::kLds];
-  const int lam = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = lam % p.Hv, j = (lam / p.Hv) % p.P, b = lam / (p.Hv * p.P);
+  // With a row order (rows of unequal lengths, no segments) the workgroups take the rows longest
+  // first, in dispatch order, so that the long rows start early on every XCD; otherwise the
+  // workgroups of a (row, head) run side by side on one XCD.
+  const int lam = p.row_order ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
+  const int h = lam % p.Hv, j = (lam / p.Hv) % p.P;
+  const int b = p.row_order ? p.row_order[lam / (p.Hv * p.P)] : lam / (p.Hv * p.P);
   SegRun run{};
   run.c_begin = j * p.Ls;
   run.c_end = min(run.c_begin + p.Ls, p.NC);
@@ -1352,8 +1356,9 @@ __device__ __forceinline__ void pair_body(const ScanParams& p, unsigned char* ld
 __global__ __launch_bounds__(64 * PairCfg::NW) void gdr_scan_bf16_pair(ScanParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[PairCfg::kLds];
   const int np = p.Hv / 2;
-  const int lam = xcd_remap(blockIdx.x, gridDim.x);
-  const int hp = lam % np, j = (lam / np) % p.P, b = lam / (np * p.P);
+  const int lam = p.row_order ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);   // as gdr_scan_bf16
+  const int hp = lam % np, j = (lam / np) % p.P;
+  const int b = p.row_order ? p.row_order[lam / (np * p.P)] : lam / (np * p.P);
   PairRun run{};
   run.c_begin = j * p.Ls;
   run.c_end = min(run.c_begin + p.Ls, p.NC);

@@ -38,6 +38,10 @@ hipError_t launch_prep(const PrepParams& p, int, int, hipStream_t) {
   return hipSuccess;
 }
 static void check_scan(const ScanParams& p) {
+  if (p.row_order) {   // the rows longest first: only without segments, after the chunk list
+    if (p.P != 1) fail_here("row order with segments");
+    in_ws(p.row_order, size_t(p.B) * 4, "row order");
+  }
   if (p.P > 1) {
     in_ws(p.seg, size_t(p.B) * p.Hv * p.P * kSlotFloats * 4, "segment slots");
     in_ws(p.status, 4, "status word");

@@ -93,7 +93,7 @@ def test_workspace_size():
     slot = 128 * 256 * 4
     # bf16 also keeps a list of the chunks that hold valid tokens (used when lengths are given):
     # an int32 count and one int32 per (row, chunk)
-    lst = lambda B, NC: 4 * (1 + B * NC)
+    lst = lambda B, NC: 4 * (1 + B * NC + B)   # chunk list, then the row order
     # with segments, a 256-byte-aligned tail: a 256-byte status header, then per (row, head, segment)
     # a 16-byte truncation plan entry and 16 floats of certificate parts
     up = lambda x: (x + 255) // 256 * 256
