@@ -205,6 +205,26 @@ def test_batch_invariance_bitwise():
         assert torch.equal(ob[0], o[b]) and torch.equal(sb[0], s[b])
 
 
+@pytest.mark.parametrize("B", [64, 128])
+def test_row_order_invariance_bitwise(B):
+    """Without segments (B Hv >= 256) ragged rows are taken longest first, ties in any order, by the
+    single-head pass (B = 64) or the pair pass (B = 128): a row's results do not depend on the run nor
+    on where the row sits in the batch."""
+    gen = torch.Generator().manual_seed(3)
+    lens = [int(v) for v in torch.randint(1, 1025, (B,), generator=gen)]
+    lens[:8] = [1024, 1024, 64, 64, 1, 1, 700, 700]   # ties
+    x = draw(B, 1024, 2, 4, 128, "R1", 510, torch.bfloat16, lengths=lens, s0_rows=B)
+    o1, s1 = run_gpu(x)
+    o2, s2 = run_gpu(x)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    perm = torch.randperm(B, generator=gen)
+    xp = draw(B, 1024, 2, 4, 128, "R1", 510, torch.bfloat16, lengths=lens, s0_rows=B)
+    for n in ("q", "k", "v", "g", "beta", "lengths", "s0"):
+        setattr(xp, n, getattr(xp, n)[perm].contiguous())
+    op, sp = run_gpu(xp)
+    assert torch.equal(op, o1[perm]) and torch.equal(sp, s1[perm])
+
+
 def test_pad_garbage_is_ignored():
     kw = dict(lengths=[200, 90], s0_rows=2)
     x = draw(2, 200, 2, 4, 128, "R1", 509, torch.bfloat16, **kw)
