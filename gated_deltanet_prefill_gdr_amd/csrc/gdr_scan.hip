@@ -1384,10 +1384,13 @@ __global__ __launch_bounds__(64 * PairCfg::NW) void gdr_scan_bf16_pair(ScanParam
 
 // Truncation plan of a (row, head), from the chunk records. Its loads are issued first, all of them
 // together (one memory round trip), and decided on after: PlanLoads holds what thread t of the
-// workgroup reads, decide_window / chunks_contract decide from it.
+// workgroup reads, decide_window / chunks_contract decide from it. The window candidates come in
+// batches of kPlanBatch chunks; a boundary that the first batch does not decide loads the next one.
+constexpr int kPlanBatch = 8;
+static_assert(kTruncMaxW % kPlanBatch == 0, "whole batches");
 struct PlanLoads {
   int len, srow;                                // the row's length and s0 row, as stored
-  float flag[kTruncMaxW], dec[kTruncMaxW];      // boundary t + 1's window candidates cb - 1, cb - 2, ...
+  float flag[kPlanBatch], dec[kPlanBatch];      // boundary t + 1's window candidates cb - 1, cb - 2, ...
   float cflag;                                  // contraction flag of chunk t (1 past the last boundary)
 };
 __device__ __forceinline__ const float* rec_scalars(const ScanParams& p, int b, int h, int c) {
@@ -1402,7 +1405,7 @@ __device__ __forceinline__ PlanLoads plan_loads(const ScanParams& p, int b, int 
   // min(Ls, kTruncMaxW) or before chunk 0, and chunks past the last boundary, are ignored later.
   const int cb = min(t + 1, p.P - 1) * p.Ls;   // <= (P - 1) Ls < NC
 #pragma unroll
-  for (int w = 1; w <= kTruncMaxW; ++w) {
+  for (int w = 1; w <= kPlanBatch; ++w) {
     const float* sc = rec_scalars(p, b, h, max(cb - w, 0));
     pl.flag[w - 1] = sc[kBfFlag * C];
     pl.dec[w - 1] = sc[kBfGam2 * C + C - 1];   // the chunk's whole decay, in log2
@@ -1415,7 +1418,8 @@ __device__ __forceinline__ PlanLoads plan_loads(const ScanParams& p, int b, int 
 // c = jb Ls whose chunks all hold valid tokens, all carry the contraction flag (every beta' in [0, 2],
 // decay sum <= 0) and whose decay sums to l2 = sum g' log2 e <= -kTruncLog2. W = 0 when there is none
 // (or the row's length or s0 row is out of range).
-__device__ __forceinline__ void decide_window(const ScanParams& p, const PlanLoads& pl, int jb, int& W, float& l2) {
+__device__ __forceinline__ void decide_window(const ScanParams& p, const PlanLoads& pl, int b, int h, int jb,
+                                              int& W, float& l2) {
   W = 0;
   l2 = 0.f;
   if (jb >= p.P) return;
@@ -1423,15 +1427,32 @@ __device__ __forceinline__ void decide_window(const ScanParams& p, const PlanLoa
   const int cb = jb * p.Ls;
   if (cb > (pl.len + C - 1) / C) return;   // the window would reach into the row's pads
   const int wmax = min(min(p.Ls, kTruncMaxW), cb);
-  float acc = 0.f;
+  float acc = 0.f, flag[kPlanBatch], dec[kPlanBatch];
 #pragma unroll
-  for (int w = 1; w <= kTruncMaxW; ++w) {
-    if (w > wmax || !(pl.flag[w - 1] == 1.f)) return;
-    acc += pl.dec[w - 1];
-    if (acc <= -kTruncLog2) {
-      W = w;
-      l2 = acc;
-      return;
+  for (int i = 0; i < kPlanBatch; ++i) {
+    flag[i] = pl.flag[i];
+    dec[i] = pl.dec[i];
+  }
+#pragma unroll
+  for (int w0 = 0; w0 < kTruncMaxW; w0 += kPlanBatch) {
+    if (w0 > 0) {   // the next batch: candidates cb - w0 - 1, ... (clamped to chunk 0; past wmax unused)
+#pragma unroll
+      for (int i = 0; i < kPlanBatch; ++i) {
+        const float* sc = rec_scalars(p, b, h, max(cb - w0 - 1 - i, 0));
+        flag[i] = sc[kBfFlag * C];
+        dec[i] = sc[kBfGam2 * C + C - 1];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kPlanBatch; ++i) {
+      const int w = w0 + i + 1;
+      if (w > wmax || !(flag[i] == 1.f)) return;
+      acc += dec[i];
+      if (acc <= -kTruncLog2) {
+        W = w;
+        l2 = acc;
+        return;
+      }
     }
   }
 }
@@ -1469,7 +1490,7 @@ __global__ __launch_bounds__(64 * SegCfg<false>::NW) void gdr_transition_bf16(Sc
   bool contract = true;
   if (p.trunc) {
     const PlanLoads pl = plan_loads(p, b, h, t);
-    decide_window(p, pl, jb_t, W, l2);
+    decide_window(p, pl, b, h, jb_t, W, l2);
     contract = chunks_contract(p, pl, b, h, t, blockDim.x);
   }
   // every boundary has a window: an AND over the workgroup in the first word of the (not yet used)

@@ -85,7 +85,7 @@ def test_long_prefill_exact_all_heads():
 
 
 def test_weak_decay_takes_exact_path():
-    """g ~ -0.02 U(0, 1): no window of at most 8 chunks decays by 2^-40, so no head is truncated."""
+    """g ~ -0.02 U(0, 1): no window of at most 16 chunks decays by 2^-40, so no head is truncated."""
     x = draw(1, 4096, 4, 8, 128, "R2", 811, torch.bfloat16)
     o, s, status, trunc = run(x)
     assert not trunc.any()
@@ -121,6 +121,18 @@ def test_exact_path_in_place():
     o, s, status, trunc = run(x, in_place=True)
     assert not trunc.any() and status == 0
     check(x, o, s, "exact path in place")
+
+
+def test_medium_decay_long_windows():
+    """g ~ -U(0.03, 0.05) (about 3.7 in log2 per chunk): a boundary needs a window of about 11 chunks to
+    decay by 2^-40, longer than 8 and within the 16-chunk segments here (B Hv = 32: 8 segments)."""
+    x = draw(4, 8192, 4, 8, 128, "LONG", 823, torch.bfloat16)
+    gen = torch.Generator().manual_seed(9)
+    x.g = (-(0.03 + 0.02 * torch.rand(x.g.shape, generator=gen))).contiguous()
+    assert seg_plan(4, 8, 128) == (8, 16)
+    o, s, status, trunc = run(x)
+    assert trunc.all() and status == 0, (trunc, status)
+    check(x, o, s, "medium decay, long windows", rows=[0, 3], heads=[0, 7])
 
 
 def test_mixed_heads():
