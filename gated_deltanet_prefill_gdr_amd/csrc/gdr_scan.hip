@@ -417,8 +417,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
 
   // Output tiles of a chunk and, with the fused gated RMSNorm, its gate values. The norm needs each
   // token's sum of squares over all 128 columns, i.e. over all waves: every wave leaves its partial
-  // sums in LDS (two buffers, by chunk parity) and normalises and stores chunk c - 1 right after
-  // the barrier that opens chunk c, so the fusion adds no barrier.
+  // sums in LDS (two buffers, by chunk parity) and normalises and stores chunk c - 1 during chunk c,
+  // after chunk c + 1's loads are issued and before the P' barrier, so the fusion adds no barrier.
   // Ot: the chunk's outputs; sz: w silu(z) of the same lanes' elements, formed from the gate rows
   // staged with the chunk while the chunk computes.
   f4 Ot[4][NSL], sz[4][NSL];
@@ -502,13 +502,12 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
   for (int c = c_begin; c < c_mid; ++c) {
     // chunk c has landed for every wave, every wave is done with chunk c - 1's buffer, and (fused
     // norm) chunk c - 1's gate rows and partial sums are in LDS. Vector-memory operations issued
-    // after chunk c's loads: chunk c - 1's output stores; none with the fused norm (its stores
-    // come first in the iteration).
-    if (fuse)
+    // after chunk c's loads: the output stores of chunk c - 1 (with the fused norm: of chunk c - 2,
+    // none in the first iteration).
+    if (fuse && c <= c_begin + 1)
       wait_and_barrier<0>();
     else
       wait_and_barrier<Cfg::kStores>();
-    if (fuse && c > c_begin) finish_norm(c - 1);
     if (kOut && c == run.cert_chunk) {   // ||S||_F^2 of the state entering chunk c, this wave's part
       float ss = 0.f;
 #pragma unroll
@@ -662,6 +661,10 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     // consecutive columns 4G .. 4G + 3 of one token, stored as one 8-byte write.
     if constexpr (kOut) {
       if (stage_next) issue(c + 1, kStRec);
+      // the norm of chunk c - 1 and its stores: after all of the next chunk's loads (so that the
+      // wait that opens the next chunk leaves only these stores in flight), before this chunk's
+      // output products take over Ot
+      if (fuse && c > c_begin) finish_norm(c - 1);
       lds_barrier();   // P' is complete
       const unsigned char* Qt = Bf + Cfg::kQ;
       bf16x8 Dop[NSL][2];
@@ -766,8 +769,8 @@ __device__ __forceinline__ void seg_body(const ScanParams& p, unsigned char* lds
     }
     for (int c = c_mid; fuse && c < c_end; ++c) {
       wait_and_barrier<0>();
-      if (c > c_begin) finish_norm(c - 1);
       if (c + 1 < c_end) issue_q(c + 1);
+      if (c > c_begin) finish_norm(c - 1);
       const unsigned char* Qt = lds + (c & 1) * Cfg::kBuf + Cfg::kQ;
       if (w < 4) {   // q norms of token tile w
         f4 qq = f4_splat(0.f);
