@@ -135,6 +135,21 @@ def test_medium_decay_long_windows():
     check(x, o, s, "medium decay, long windows", rows=[0, 3], heads=[0, 7])
 
 
+@pytest.mark.parametrize("lo,width,truncated", [(0.027, 0.002, True), (0.020, 0.004, False)])
+def test_window_limit(lo, width, truncated):
+    """The long prefill's shape (8 segments of 32 chunks) with g ~ -U(lo, lo + width): windows of exactly
+    16 chunks (the longest allowed: every head truncated) and of 20 chunks (past the limit: every head
+    takes the exact path), the window lengths worked out from the drawn gates beforehand."""
+    x = draw(1, 16384, 16, 32, 128, "LONG", 824, torch.bfloat16)
+    gen = torch.Generator().manual_seed(10)
+    x.g = (-(lo + width * torch.rand(x.g.shape, generator=gen))).contiguous()
+    assert seg_plan(1, 32, 256) == (8, 32)
+    o, s, status, trunc = run(x)
+    assert status == 0
+    assert trunc.all() if truncated else not trunc.any(), trunc
+    check(x, o, s, f"window limit, g ~ -U({lo:.3f}, {lo + width:.3f})", heads=[0, 31])
+
+
 def test_mixed_heads():
     """Heads with strong decay are truncated, heads without decay are not, in one call."""
     x = draw(1, 2048, 2, 4, 128, "LONG", 812, torch.bfloat16)
