@@ -87,7 +87,7 @@ inline size_t chunk_list_bytes(int B, int NC, size_t elem) { return elem == 2 ? 
 // (row, head) without truncation where it fails.
 constexpr float kTruncLog2 = 40.f;     // a-priori window decay: 2^-40
 constexpr float kCertRel = 5.9604645e-8f;   // 2^-24
-constexpr int kTruncMaxW = 16;          // longest window, in chunks (at most the segment length)
+constexpr int kTruncMaxW = 32;          // longest window, in chunks (at most the segment length)
 struct PlanEntry {                      // per (row, head, boundary j), written by the transition pass
   int32_t W;                            // window length in chunks (0: no window, boundary not truncated)
   float l2;                             // sum of g' log2(e) over the window

@@ -205,7 +205,7 @@ gdr_status gdr_decode_ex(const gdr_desc* desc, const void* q, const void* k, con
  * S -> Phi S + B with ||Phi||_2 <= exp(sum of g' over the run) whenever every beta' of the run lies in
  * [0, 2] (each token multiplies S by exp(g') (I - beta' k_hat k_hat^T), whose spectral norm is then at
  * most exp(g'), since |k_hat| < 1). When, for every segment boundary of a (row, head), the last few
- * chunks (at most 16) before the boundary decay by at least 2^-40 in that sense, the library takes the
+ * chunks (at most 32) before the boundary decay by at least 2^-40 in that sense, the library takes the
  * state entering the segment from those chunks alone, run from zero, instead of composing the maps of
  * all earlier segments. The dropped term is at most 2^-40 times the norm of the state where the window
  * starts; the kernels measure that norm and, in a last pass, check at every boundary that the error

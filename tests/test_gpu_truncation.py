@@ -85,7 +85,8 @@ def test_long_prefill_exact_all_heads():
 
 
 def test_weak_decay_takes_exact_path():
-    """g ~ -0.02 U(0, 1): no window of at most 16 chunks decays by 2^-40, so no head is truncated."""
+    """g ~ -0.02 U(0, 1): no window within the 2-chunk segments here decays by 2^-40, so no head is
+    truncated."""
     x = draw(1, 4096, 4, 8, 128, "R2", 811, torch.bfloat16)
     o, s, status, trunc = run(x)
     assert not trunc.any()
@@ -125,7 +126,8 @@ def test_exact_path_in_place():
 
 def test_medium_decay_long_windows():
     """g ~ -U(0.03, 0.05) (about 3.7 in log2 per chunk): a boundary needs a window of about 11 chunks to
-    decay by 2^-40, longer than 8 and within the 16-chunk segments here (B Hv = 32: 8 segments)."""
+    decay by 2^-40, longer than one batch of plan loads (8) and within the 16-chunk segments here
+    (B Hv = 32: 8 segments)."""
     x = draw(4, 8192, 4, 8, 128, "LONG", 823, torch.bfloat16)
     gen = torch.Generator().manual_seed(9)
     x.g = (-(0.03 + 0.02 * torch.rand(x.g.shape, generator=gen))).contiguous()
@@ -135,11 +137,12 @@ def test_medium_decay_long_windows():
     check(x, o, s, "medium decay, long windows", rows=[0, 3], heads=[0, 7])
 
 
-@pytest.mark.parametrize("lo,width,truncated", [(0.027, 0.002, True), (0.020, 0.004, False)])
+@pytest.mark.parametrize("lo,width,truncated", [(0.027, 0.002, True), (0.0136, 0.0002, True), (0.012, 0.0005, False)])
 def test_window_limit(lo, width, truncated):
-    """The long prefill's shape (8 segments of 32 chunks) with g ~ -U(lo, lo + width): windows of exactly
-    16 chunks (the longest allowed: every head truncated) and of 20 chunks (past the limit: every head
-    takes the exact path), the window lengths worked out from the drawn gates beforehand."""
+    """The long prefill's shape (8 segments of 32 chunks) with g ~ -U(lo, lo + width): windows of 16
+    chunks (two batches of plan loads), of 32 (four batches; the whole segment before the boundary, the
+    longest allowed: every head truncated) and of 36 (past it: every head takes the exact path), the
+    window lengths worked out from the drawn gates beforehand."""
     x = draw(1, 16384, 16, 32, 128, "LONG", 824, torch.bfloat16)
     gen = torch.Generator().manual_seed(10)
     x.g = (-(lo + width * torch.rand(x.g.shape, generator=gen))).contiguous()
