@@ -1430,33 +1430,49 @@ __device__ __forceinline__ void decide_window(const ScanParams& p, const PlanLoa
   const int cb = jb * p.Ls;
   if (cb > (pl.len + C - 1) / C) return;   // the window would reach into the row's pads
   const int wmax = min(min(p.Ls, kTruncMaxW), cb);
-  float acc = 0.f, flag[kPlanBatch], dec[kPlanBatch];
+  float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < kPlanBatch; ++i) {
-    flag[i] = pl.flag[i];
-    dec[i] = pl.dec[i];
+  for (int i = 0; i < kPlanBatch; ++i) {   // the first batch, loaded with the plan's other loads
+    const int w = i + 1;
+    if (w > wmax || !(pl.flag[i] == 1.f)) return;
+    acc += pl.dec[i];
+    if (acc <= -kTruncLog2) {
+      W = w;
+      l2 = acc;
+      return;
+    }
   }
 #pragma unroll
-  for (int w0 = 0; w0 < kTruncMaxW; w0 += kPlanBatch) {
-    if (w0 > 0) {   // the next batch: candidates cb - w0 - 1, ... (clamped to chunk 0; past wmax unused)
+  for (int w0 = kPlanBatch; w0 < kTruncMaxW; w0 += kPlanBatch) {
+    // the next batch: candidates cb - w0 - 1, ... (clamped to chunk 0; past wmax unused), decided
+    // without branches (selects only), so that every load of the batch is used in straight-line code
+    // and all of them are in flight together: decided one candidate at a time behind early exits,
+    // the loads were sunk to their uses and waited for one by one
+    float flag[kPlanBatch], dec[kPlanBatch];
 #pragma unroll
-      for (int i = 0; i < kPlanBatch; ++i) {
-        const float* sc = rec_scalars(p, b, h, max(cb - w0 - 1 - i, 0));
-        flag[i] = sc[kBfFlag * C];
-        dec[i] = sc[kBfGam2 * C + C - 1];
-      }
+    for (int i = 0; i < kPlanBatch; ++i) {
+      const float* sc = rec_scalars(p, b, h, max(cb - w0 - 1 - i, 0));
+      flag[i] = sc[kBfFlag * C];
+      dec[i] = sc[kBfGam2 * C + C - 1];
     }
+    bool stop = false;   // a candidate past wmax or without the contraction flag ends the search
+    int hit = 0;         // window length found in this batch (0: none yet)
+    float hit_l2 = 0.f;
 #pragma unroll
     for (int i = 0; i < kPlanBatch; ++i) {
       const int w = w0 + i + 1;
-      if (w > wmax || !(flag[i] == 1.f)) return;
+      stop = stop || w > wmax || !(flag[i] == 1.f);
       acc += dec[i];
-      if (acc <= -kTruncLog2) {
-        W = w;
-        l2 = acc;
-        return;
-      }
+      const bool take = !stop && hit == 0 && acc <= -kTruncLog2;
+      hit = take ? w : hit;
+      hit_l2 = take ? acc : hit_l2;
     }
+    if (hit > 0) {
+      W = hit;
+      l2 = hit_l2;
+      return;
+    }
+    if (stop) return;
   }
 }
 
